@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Throughput of the product-VQ encode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+A step is one call of the whole hot path (``vq_encode`` through the C ABI)
+over one batch of synthetic input.  The default workload is the Falcon3-7B
+key-cache shape of the VeloxQuant-MLX post "I Wrote a Metal Kernel to Stop My
+Mac From OOMing" (section "What quantize_vq Was Doing Wrong": 4096 tokens x 4
+KV heads x head_dim 256, sub_dim 4 -> 1,048,576 sub-vectors, 256 centroids),
+with seeded per-channel-scaled Gaussian keys and outlier channels.  Inputs are
+resident in HBM before the timed region starts.
+
+Printed: one JSON line with sub-vectors/s over the timed region, the
+roofline position of the encode kernel (algorithmic fp32 flops,
+3*sub_dim*n_centroids per sub-vector, per launch divided by the launch's
+average duration measured with HIP events on the launch stream, against the
+MI355X fp32 vector peak) and the CPU oracle's rate on a bounded sample on the
+host (``cpu_baseline``).  Other workloads (``--config``) are for exploration.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X published fp32 vector peak
+HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
+# Pages' own figure for the same workload, on an Apple-Silicon GPU (context):
+# 1,048,576 sub-vectors in 7.98 ms (post's "The Numbers" throughput table).
+PAGES_FALCON_SUBVEC_PER_S = 1048576 / 7.98e-3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_falcon3_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "product_vq_kv_amd", "csrc", "vq_encode.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_bytes_per_launch():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, sample_rows: int):
+    import numpy as np
+    import oracle
+    rows = min(sample_rows, wl.n)
+    xs = np.ascontiguousarray(wl.x[:rows])
+    t0 = time.perf_counter()
+    idx = oracle.encode(xs, wl.codebook, wl.sub_dim, wl.n_centroids, wl.dtype, threads=1)
+    dt = time.perf_counter() - t0
+    return idx, dict(value=rows / dt, unit="sub-vectors/s", cores=1, kind="oracle",
+                     sample=f"first {rows} of {wl.n} sub-vectors of the same workload, "
+                            f"one thread, {dt:.1f} s")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-sample", type=int, default=1 << 19,
+                    help="rows the CPU oracle encodes for cpu_baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the encode step needs no exchange between "
+              "GPUs, and this build runs on a single MI355X (see the sharding note in the "
+              "design document).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (there is no CPU path)", file=sys.stderr)
+        return 2
+    import product_vq_kv_amd as vq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.config(args.config)
+    log(f"workload: {wl.name} (n={wl.n})")
+    tdt = torch.float16 if wl.dtype == W.F16 else torch.bfloat16
+    x = torch.from_numpy(wl.x.view(np.int16)).view(tdt).to(dev)
+    cb = torch.from_numpy(wl.codebook.view(np.int16)).view(tdt).to(dev)
+    out = torch.empty(wl.n, dtype=torch.uint32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    call = (x.data_ptr(), cb.data_ptr(), wl.n, wl.sub_dim, wl.n_centroids, wl.dtype,
+            wl.codebook_stride, wl.n_codebooks, wl.group_len, None, out.data_ptr(), sptr)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        vq.encode_raw(*call)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        vq.encode_raw(*call)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+
+    if args.copy_calibration:
+        # plain copy of 256 MiB, five times: the counter scale reference
+        src = torch.empty(1 << 26, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 5 x 268435456-byte device copies")
+
+    ms_per_step = wall * 1e3 / args.steps
+    launch_s = gpu_ms / 1e3 / args.steps
+    flops = 3.0 * wl.sub_dim * wl.n_centroids * wl.n
+    algo_bytes = wl.n * (2 * wl.sub_dim + 4) + wl.n_codebooks * wl.n_centroids * wl.sub_dim * 2
+    achieved = flops / launch_s / 1e12
+    value = wl.n / (ms_per_step / 1e3)
+
+    gpu_idx = out.cpu().numpy().view(np.uint32)
+    cpu = None
+    parity_sample = None
+    if args.cpu_sample > 0:
+        log(f"cpu baseline: oracle on {min(args.cpu_sample, wl.n)} rows, one thread")
+        ref, cpu = cpu_baseline(wl, args.cpu_sample)
+        parity_sample = dict(rows=int(ref.size), equal=int(np.sum(ref == gpu_idx[:ref.size])))
+
+    cfg = dict(workload=wl.name, n_subvectors=wl.n, sub_dim=wl.sub_dim,
+               n_centroids=wl.n_centroids, element="fp16" if wl.dtype == W.F16 else "bf16",
+               n_codebooks=wl.n_codebooks, **{k: v for k, v in wl.meta.items()
+                                               if isinstance(v, (int, float, str))})
+    line = {
+        "metric": "sub-vectors encoded/sec and % fp32 VALU peak (Falcon3-7B shape, 1 GPU)",
+        "value": value,
+        "unit": "sub-vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (value / PAGES_FALCON_SUBVEC_PER_S) if args.config == 3 else None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; per-channel LogNormal-scaled Gaussian keys, outlier channels)",
+        "config": cfg,
+        "roofline": {
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
+            "traffic": traffic_bytes_per_launch() if args.config == 3 else None,
+        },
+        "cpu_baseline": cpu,
+        "kernel_ms_per_launch": launch_s * 1e3,
+        "algorithmic_gb_per_s": algo_bytes / launch_s / 1e9,
+        "hbm_frac": algo_bytes / launch_s / 1e9 / HBM_PEAK_GBS,
+        "parity_sample": parity_sample,
+        "vs_baseline_note": "pages' Apple-Silicon Metal kernel on the same shape (context only)",
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

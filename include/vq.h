@@ -1,0 +1,124 @@
+/*
+ * vq.h -- C ABI of the MI355X (gfx950) product-VQ encode library, libvq.so.
+ *
+ * The operation is the encode step of VecInfer product vector quantization
+ * as described in the VeloxQuant-MLX blog post "I Wrote a Metal Kernel to
+ * Stop My Mac From OOMing":
+ *   - section "What Even Is a KV Cache And Why Should You Care" (steps 1-3):
+ *     a key is cut into sub-vectors of length sub_dim and each sub-vector is
+ *     replaced by the index of its nearest codebook centroid;
+ *   - section "What quantize_vq Was Doing Wrong": nearest = argmin over the
+ *     centroids of the summed squared component differences;
+ *   - section "The Kernel: 18 Lines of MSL": fp32 promotion of every
+ *     component, squared distance accumulated in one fp32 value, strict-<
+ *     running argmin from (+infinity, index 0), one uint32 per sub-vector.
+ * Fixed arithmetic (identical to the CPU oracle the library is tested
+ * against): per component d = fp32(x_i) - fp32(c_i) rounded once, then
+ * dist = fma(d, d, dist), components in order i = 0 .. sub_dim-1 from +0.
+ * Ties go to the lowest index; NaN distances never win; a sub-vector whose
+ * distances are all +inf or NaN gets index 0.
+ *
+ * Batched caches: sub-vector n belongs to group g = n / group_len and is
+ * encoded against codebook slot k = group_map ? group_map[g] : g, which
+ * starts at element k * codebook_stride of the codebook buffer.  One launch
+ * covers every group (e.g. one codebook per (layer, kv head) with
+ * group_len = tokens * head_dim / sub_dim).  Batching all heads into one call
+ * follows the residual-VQ benchmark post's section "The Throughput Problem
+ * (and How We Solved It)", change 1.
+ *
+ * Memory: every pointer is device memory owned by the caller.  The library
+ * allocates nothing, keeps no state between calls and is re-entrant.  Calls
+ * are asynchronous on `stream` (a hipStream_t; NULL = the default stream):
+ * results are valid once the stream has been synchronised.
+ *
+ * Errors: every argument check happens on the host before any HIP call; a
+ * rejected call launches nothing and writes nothing.  Launch failures return
+ * VQ_ERR_DEVICE and the HIP error code is kept (per host thread) for
+ * vq_last_hip_error().  Device memory the kernels read is never read out of
+ * bounds for arguments that pass the checks, given buffers of the documented
+ * sizes.
+ */
+#ifndef PRODUCT_VQ_KV_AMD_VQ_H
+#define PRODUCT_VQ_KV_AMD_VQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VQ_F16 = 0,  /* IEEE binary16 elements */
+    VQ_BF16 = 1  /* bfloat16 elements */
+} vq_dtype;
+
+typedef enum {
+    VQ_OK = 0,
+    VQ_ERR_INVALID_ARG = -1, /* null pointer with n > 0, bad count, stride or group layout */
+    VQ_ERR_UNSUPPORTED = -2, /* sub_dim not 4 or 8, unknown dtype, n_centroids > 65536 */
+    VQ_ERR_MISALIGNED = -3,  /* x not aligned to 2*sub_dim bytes, codebook to 2, idx/out to 4 */
+    VQ_ERR_DEVICE = -4       /* the HIP launch failed; see vq_last_hip_error() */
+} vq_status;
+
+/* Index written for every sub-vector of a group whose group_map entry is not
+ * a valid slot (outside [0, n_codebooks)). */
+#define VQ_BAD_SLOT 0xFFFFFFFFu
+#define VQ_MAX_CENTROIDS 65536
+#define VQ_ABI_VERSION 1
+
+/*
+ * vq_encode -- nearest-centroid index of every sub-vector.
+ *
+ *   x            device, [n][sub_dim] elements of `dtype`, row-major, aligned
+ *                to 2*sub_dim bytes.
+ *   codebook     device, n_codebooks slots; slot k holds [n_centroids][sub_dim]
+ *                elements of `dtype` at element offset k*codebook_stride.
+ *   n            number of sub-vectors (>= 0; 0 returns VQ_OK, no launch).
+ *   sub_dim      4 or 8.
+ *   n_centroids  1 .. 65536.
+ *   codebook_stride  elements between slots; >= n_centroids*sub_dim when
+ *                n_codebooks > 1 (ignored when n_codebooks == 1).
+ *   n_codebooks  >= 1.
+ *   group_len    sub-vectors per group, >= 1 (group_len >= n: one group).
+ *   group_map    device int32 [ceil(n/group_len)] group -> slot, or NULL for
+ *                slot = group (then ceil(n/group_len) <= n_codebooks is
+ *                checked on the host).  Entries outside [0, n_codebooks)
+ *                make that group's indices VQ_BAD_SLOT.
+ *   out_idx      device, [n] uint32, aligned to 4 bytes.
+ *   stream       hipStream_t or NULL.
+ */
+vq_status vq_encode(const void *x, const void *codebook, int64_t n, int32_t sub_dim,
+                    int32_t n_centroids, vq_dtype dtype, int64_t codebook_stride,
+                    int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
+                    uint32_t *out_idx, void *stream);
+
+/*
+ * vq_decode -- gather used to check encode: row n of out_x is centroid idx[n]
+ * of the slot of n's group, copied bit for bit (the reconstruction the post
+ * measures MSE on, section "Correctness: Bit-Exact on fp32, MSE-Identical on
+ * fp16"; the gather of section "Mistake 1: I Wrote the Dequant Kernel First").
+ * An index >= n_centroids or a bad slot gives a row of zero bits.
+ *
+ *   idx    device, [n] uint32, aligned to 4 bytes.
+ *   out_x  device, [n][sub_dim] elements of `dtype`, aligned to 2 bytes.
+ *   other arguments as for vq_encode.
+ */
+vq_status vq_decode(const uint32_t *idx, const void *codebook, int64_t n, int32_t sub_dim,
+                    int32_t n_centroids, vq_dtype dtype, int64_t codebook_stride,
+                    int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
+                    void *out_x, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *vq_status_str(int32_t status);
+
+/* hipError_t of the last VQ_ERR_DEVICE returned on this host thread (0 if none). */
+int32_t vq_last_hip_error(void);
+
+/* VQ_ABI_VERSION of the loaded library. */
+int32_t vq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRODUCT_VQ_KV_AMD_VQ_H */

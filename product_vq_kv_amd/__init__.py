@@ -1,0 +1,187 @@
+"""MI355X-native product-VQ KV-cache encode (VecInfer ``quantize_vq``).
+
+Thin Python binding over the C ABI of ``libvq.so`` (declared in
+``include/vq.h``): every step of the computation runs in the library's HIP
+kernels; this module only checks tensor shapes and passes device pointers,
+sizes and the current HIP stream.  There is no CPU fallback: if the library
+is missing or cannot be loaded, importing this package raises.
+
+    import torch, product_vq_kv_amd as vq
+    idx = vq.encode(keys_subvectors, codebook)          # uint32 [N]
+    rec = vq.decode(idx, codebook)                      # gather, for checking
+
+``encode`` follows the encode step of VecInfer product vector quantization as
+the VeloxQuant-MLX blog post "I Wrote a Metal Kernel to Stop My Mac From
+OOMing" describes it (sections "What quantize_vq Was Doing Wrong" and "The
+Kernel: 18 Lines of MSL"): the index of the nearest centroid by squared L2
+distance, evaluated in fp32, ties to the lowest index.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loads the HIP runtime that libvq.so binds to (same soname)
+
+__all__ = ["encode", "decode", "encode_raw", "decode_raw", "VQError", "lib", "LIB_PATH",
+           "F16", "BF16", "BAD_SLOT", "MAX_CENTROIDS", "STATUS"]
+
+F16 = 0
+BF16 = 1
+BAD_SLOT = 0xFFFFFFFF
+MAX_CENTROIDS = 65536
+STATUS = {0: "VQ_OK", -1: "VQ_ERR_INVALID_ARG", -2: "VQ_ERR_UNSUPPORTED",
+          -3: "VQ_ERR_MISALIGNED", -4: "VQ_ERR_DEVICE"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m product_vq_kv_amd.build` "
+                      "(there is no CPU fallback)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+lib.vq_encode.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _p, _p]
+lib.vq_encode.restype = _i32
+lib.vq_decode.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _p, _p]
+lib.vq_decode.restype = _i32
+lib.vq_status_str.argtypes = [_i32]
+lib.vq_status_str.restype = ctypes.c_char_p
+lib.vq_last_hip_error.argtypes = []
+lib.vq_last_hip_error.restype = _i32
+lib.vq_abi_version.argtypes = []
+lib.vq_abi_version.restype = _i32
+
+
+class VQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.vq_status_str(status).decode()
+        extra = ""
+        if status == -4:
+            extra = f" (hipError {lib.vq_last_hip_error()})"
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}{extra}")
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise VQError(rc, where)
+
+
+def encode_raw(x_ptr: int, codebook_ptr: int, n: int, sub_dim: int, n_centroids: int,
+               dtype: int, codebook_stride: int, n_codebooks: int, group_len: int,
+               group_map_ptr: Optional[int], out_ptr: int, stream: Optional[int]) -> None:
+    """Direct call of ``vq_encode`` with integer pointers (raises on error)."""
+    _check(lib.vq_encode(x_ptr, codebook_ptr, n, sub_dim, n_centroids, dtype, codebook_stride,
+                         n_codebooks, group_len, group_map_ptr, out_ptr, stream), "vq_encode")
+
+
+def decode_raw(idx_ptr: int, codebook_ptr: int, n: int, sub_dim: int, n_centroids: int,
+               dtype: int, codebook_stride: int, n_codebooks: int, group_len: int,
+               group_map_ptr: Optional[int], out_ptr: int, stream: Optional[int]) -> None:
+    """Direct call of ``vq_decode`` with integer pointers (raises on error)."""
+    _check(lib.vq_decode(idx_ptr, codebook_ptr, n, sub_dim, n_centroids, dtype, codebook_stride,
+                         n_codebooks, group_len, group_map_ptr, out_ptr, stream), "vq_decode")
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float16:
+        return F16
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"elements must be float16 or bfloat16, got {t}")
+
+
+def _codebook_layout(codebook: torch.Tensor):
+    """(n_codebooks, n_centroids, sub_dim, stride) of a [.., n_c, sd] tensor."""
+    if codebook.dim() == 2:
+        n_c, sd = codebook.shape
+        if not codebook.is_contiguous():
+            raise ValueError("codebook must be contiguous")
+        return 1, n_c, sd, n_c * sd
+    if codebook.dim() == 3:
+        k, n_c, sd = codebook.shape
+        if codebook.stride(2) != 1 or codebook.stride(1) != sd:
+            raise ValueError("each codebook slot must be a contiguous [n_centroids, sub_dim] block")
+        return k, n_c, sd, codebook.stride(0)
+    raise ValueError("codebook must be [n_centroids, sub_dim] or [slots, n_centroids, sub_dim]")
+
+
+def _stream_of(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def encode(x: torch.Tensor, codebook: torch.Tensor, *, group_len: Optional[int] = None,
+           group_map: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Nearest-centroid index of every sub-vector, as a uint32 tensor [N].
+
+    x         fp16/bf16 CUDA tensor whose last dimension is a multiple of
+              sub_dim (e.g. keys [..., head_dim] or sub-vectors [N, sub_dim]);
+              it is viewed as [N, sub_dim] and must be contiguous.
+    codebook  [n_centroids, sub_dim] or [slots, n_centroids, sub_dim], same dtype.
+    group_len sub-vectors per group when several codebook slots are used:
+              sub-vector n uses slot group_map[n // group_len] (or n // group_len).
+    """
+    if not (x.is_cuda and codebook.is_cuda):
+        raise ValueError("x and codebook must be device tensors (no CPU path exists)")
+    dt = _dtype_code(x.dtype)
+    if codebook.dtype != x.dtype:
+        raise TypeError("x and codebook must have the same dtype")
+    k, n_c, sd, stride = _codebook_layout(codebook)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if x.numel() % sd:
+        raise ValueError("x's element count is not a multiple of sub_dim")
+    n = x.numel() // sd
+    if group_len is None:
+        group_len = max(n, 1)
+    gptr = None
+    if group_map is not None:
+        if group_map.dtype != torch.int32 or not group_map.is_cuda or not group_map.is_contiguous():
+            raise ValueError("group_map must be a contiguous int32 device tensor")
+        if group_map.numel() < -(-n // group_len):
+            raise ValueError("group_map needs one entry per group")
+        gptr = group_map.data_ptr()
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint32, device=x.device)
+    elif out.dtype != torch.uint32 or out.numel() != n or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint32 tensor with one entry per sub-vector")
+    encode_raw(x.data_ptr(), codebook.data_ptr(), n, sd, n_c, dt, stride, k, group_len, gptr,
+               out.data_ptr(), _stream_of(x.device, stream))
+    return out
+
+
+def decode(idx: torch.Tensor, codebook: torch.Tensor, *, group_len: Optional[int] = None,
+           group_map: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Gather codebook rows by index: [N] uint32 -> [N, sub_dim] (checking aid)."""
+    if not (idx.is_cuda and codebook.is_cuda):
+        raise ValueError("idx and codebook must be device tensors")
+    if idx.dtype not in (torch.uint32, torch.int32) or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous uint32 tensor")
+    dt = _dtype_code(codebook.dtype)
+    k, n_c, sd, stride = _codebook_layout(codebook)
+    n = idx.numel()
+    if group_len is None:
+        group_len = max(n, 1)
+    gptr = None
+    if group_map is not None:
+        if group_map.dtype != torch.int32 or not group_map.is_cuda or not group_map.is_contiguous():
+            raise ValueError("group_map must be a contiguous int32 device tensor")
+        if group_map.numel() < -(-n // group_len):
+            raise ValueError("group_map needs one entry per group")
+        gptr = group_map.data_ptr()
+    if out is None:
+        out = torch.empty((n, sd), dtype=codebook.dtype, device=idx.device)
+    elif out.dtype != codebook.dtype or out.numel() != n * sd or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [N, sub_dim] tensor of the codebook dtype")
+    decode_raw(idx.data_ptr(), codebook.data_ptr(), n, sd, n_c, dt, stride, k, group_len, gptr,
+               out.data_ptr(), _stream_of(idx.device, stream))
+    return out

@@ -1,0 +1,108 @@
+// vq_capi.cpp -- the extern "C" entry points declared in include/vq.h.
+//
+// Validates every argument on the host, before any HIP call, then hands the
+// launch to the kernel launchers.  Nothing is allocated and no state is kept
+// except the per-thread last HIP error.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vq.h"
+#include "vq_launch.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int64_t kMaxGrid = 0x7fffffffLL;
+
+vq_status check_common(const void *codebook, int64_t n, int32_t sub_dim, int32_t n_centroids,
+                       vq_dtype dtype, int64_t codebook_stride, int64_t n_codebooks,
+                       int64_t group_len, const int32_t *group_map, vqk::Layout *l) {
+  if (sub_dim != 4 && sub_dim != 8) return VQ_ERR_UNSUPPORTED;
+  if (dtype != VQ_F16 && dtype != VQ_BF16) return VQ_ERR_UNSUPPORTED;
+  if (n_centroids > VQ_MAX_CENTROIDS) return VQ_ERR_UNSUPPORTED;
+  if (n < 0 || n_centroids < 1 || n_codebooks < 1 || group_len < 1) return VQ_ERR_INVALID_ARG;
+  if (n > INT64_MAX / 64) return VQ_ERR_INVALID_ARG;  // n * sub_dim * 2 bytes must not overflow
+  const int64_t row_elems = static_cast<int64_t>(n_centroids) * sub_dim;
+  if (n_codebooks > 1) {
+    if (codebook_stride < row_elems) return VQ_ERR_INVALID_ARG;
+    if (codebook_stride > (INT64_MAX - row_elems) / (n_codebooks - 1)) return VQ_ERR_INVALID_ARG;
+  }
+  const int64_t n_groups = n == 0 ? 0 : (n - 1) / group_len + 1;
+  if (!group_map && n_groups > n_codebooks) return VQ_ERR_INVALID_ARG;
+  if (n > 0 && !codebook) return VQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(codebook) % 2 != 0) return VQ_ERR_MISALIGNED;
+  if (group_map && reinterpret_cast<uintptr_t>(group_map) % 4 != 0) return VQ_ERR_MISALIGNED;
+  l->n = n;
+  l->sub_dim = sub_dim;
+  l->n_centroids = n_centroids;
+  l->bf16 = dtype == VQ_BF16 ? 1 : 0;
+  l->codebook_stride = n_codebooks > 1 ? codebook_stride : row_elems;
+  l->n_codebooks = n_codebooks;
+  l->group_len = group_len;
+  l->n_groups = n_groups;
+  return VQ_OK;
+}
+
+vq_status device_result(hipError_t e) {
+  if (e == hipSuccess) return VQ_OK;
+  g_last_hip_error = static_cast<int32_t>(e);
+  return VQ_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+vq_status vq_encode(const void *x, const void *codebook, int64_t n, int32_t sub_dim,
+                    int32_t n_centroids, vq_dtype dtype, int64_t codebook_stride,
+                    int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
+                    uint32_t *out_idx, void *stream) {
+  vqk::Layout l;
+  vq_status st = check_common(codebook, n, sub_dim, n_centroids, dtype, codebook_stride,
+                              n_codebooks, group_len, group_map, &l);
+  if (st != VQ_OK) return st;
+  if (n > 0 && (!x || !out_idx)) return VQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(x) % (2 * sub_dim) != 0) return VQ_ERR_MISALIGNED;
+  if (reinterpret_cast<uintptr_t>(out_idx) % 4 != 0) return VQ_ERR_MISALIGNED;
+  if (n == 0) return VQ_OK;
+  if (vqk::encode_grid(l) > kMaxGrid) return VQ_ERR_INVALID_ARG;
+  (void)hipGetLastError();  // drop a stale error so it is not reported as ours
+  return device_result(
+      vqk::launch_encode(x, codebook, group_map, out_idx, l, static_cast<hipStream_t>(stream)));
+}
+
+vq_status vq_decode(const uint32_t *idx, const void *codebook, int64_t n, int32_t sub_dim,
+                    int32_t n_centroids, vq_dtype dtype, int64_t codebook_stride,
+                    int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
+                    void *out_x, void *stream) {
+  vqk::Layout l;
+  vq_status st = check_common(codebook, n, sub_dim, n_centroids, dtype, codebook_stride,
+                              n_codebooks, group_len, group_map, &l);
+  if (st != VQ_OK) return st;
+  if (n > 0 && (!idx || !out_x)) return VQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(idx) % 4 != 0) return VQ_ERR_MISALIGNED;
+  if (reinterpret_cast<uintptr_t>(out_x) % 2 != 0) return VQ_ERR_MISALIGNED;
+  if (n == 0) return VQ_OK;
+  if ((n + 255) / 256 > kMaxGrid) return VQ_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return device_result(
+      vqk::launch_decode(idx, codebook, group_map, out_x, l, static_cast<hipStream_t>(stream)));
+}
+
+const char *vq_status_str(int32_t status) {
+  switch (status) {
+    case VQ_OK: return "ok";
+    case VQ_ERR_INVALID_ARG: return "invalid argument";
+    case VQ_ERR_UNSUPPORTED: return "unsupported sub_dim, dtype or n_centroids";
+    case VQ_ERR_MISALIGNED: return "misaligned pointer";
+    case VQ_ERR_DEVICE: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t vq_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t vq_abi_version(void) { return VQ_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// Internal interface between the C-ABI front end (vq_capi.cpp) and the
+// kernel launchers.  Arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vqk {
+
+struct Layout {
+  int64_t n;               // sub-vectors
+  int32_t sub_dim;         // 4 or 8
+  int32_t n_centroids;     // 1 .. 65536
+  int32_t bf16;            // 0 = fp16, 1 = bf16
+  int64_t codebook_stride; // elements between codebook slots
+  int64_t n_codebooks;     // slots in the codebook buffer
+  int64_t group_len;       // sub-vectors per group
+  int64_t n_groups;        // ceil(n / group_len)
+};
+
+// Number of workgroups the encode launch uses for `l` (the host checks that
+// it fits the grid before launching).
+int64_t encode_grid(const Layout &l);
+
+hipError_t launch_encode(const void *x, const void *codebook, const int32_t *group_map,
+                         uint32_t *out_idx, const Layout &l, hipStream_t stream);
+
+hipError_t launch_decode(const uint32_t *idx, const void *codebook, const int32_t *group_map,
+                         void *out_x, const Layout &l, hipStream_t stream);
+
+}  // namespace vqk

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/vq.h declares, and
+reject bad arguments on the host before any HIP call (so these calls never
+touch a device; the pointers below are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vq.h")
+
+vq = pytest.importorskip("product_vq_kv_amd")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED = 0, -1, -2, -3
+FAKE = 0x10000  # aligned, never dereferenced by a rejected call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(vq_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == ["vq_abi_version", "vq_decode", "vq_encode",
+                                    "vq_last_hip_error", "vq_status_str"]
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(vq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert vq.lib.vq_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, 99):
+        assert isinstance(vq.lib.vq_status_str(code), bytes)
+    assert vq.lib.vq_status_str(-3) == b"misaligned pointer"
+    assert vq.lib.vq_last_hip_error() == 0
+
+
+def enc(**over):
+    a = dict(x=FAKE, cb=FAKE, n=1024, sd=8, n_c=256, dt=0, stride=0, k=1, glen=1024, gmap=None,
+             out=FAKE, stream=None)
+    a.update(over)
+    return vq.lib.vq_encode(a["x"], a["cb"], a["n"], a["sd"], a["n_c"], a["dt"], a["stride"],
+                            a["k"], a["glen"], a["gmap"], a["out"], a["stream"])
+
+
+def dec(**over):
+    a = dict(idx=FAKE, cb=FAKE, n=1024, sd=8, n_c=256, dt=0, stride=0, k=1, glen=1024, gmap=None,
+             out=FAKE, stream=None)
+    a.update(over)
+    return vq.lib.vq_decode(a["idx"], a["cb"], a["n"], a["sd"], a["n_c"], a["dt"], a["stride"],
+                            a["k"], a["glen"], a["gmap"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(sd=2), UNSUPPORTED), (dict(sd=16), UNSUPPORTED), (dict(sd=0), UNSUPPORTED),
+    (dict(dt=2), UNSUPPORTED), (dict(dt=-1), UNSUPPORTED),
+    (dict(n_c=65537), UNSUPPORTED), (dict(n_c=0), INVALID), (dict(n_c=-5), INVALID),
+    (dict(n=-1), INVALID), (dict(k=0), INVALID), (dict(glen=0), INVALID),
+    (dict(x=None), INVALID), (dict(cb=None), INVALID), (dict(out=None), INVALID),
+    (dict(x=FAKE + 8), MISALIGNED), (dict(sd=4, x=FAKE + 4), MISALIGNED),
+    (dict(cb=FAKE + 1), MISALIGNED), (dict(out=FAKE + 2), MISALIGNED),
+    (dict(gmap=FAKE + 2, glen=100), MISALIGNED),
+    # two groups but one codebook slot and no map
+    (dict(glen=512), INVALID),
+    # several slots need a stride of at least n_centroids * sub_dim
+    (dict(k=2, glen=512, stride=256 * 8 - 1), INVALID),
+    # n * sub_dim * 2 bytes would overflow
+    (dict(n=2 ** 62), INVALID),
+    # grid would exceed 2^31 - 1 workgroups: 2^31 one-row groups
+    (dict(n=2 ** 31, glen=1, k=2 ** 31), INVALID),
+])
+def test_encode_rejects_on_host(over, code):
+    assert enc(**over) == code
+
+
+@pytest.mark.parametrize("over", [dict(n=0), dict(n=0, x=None, cb=None, out=None),
+                                  dict(n=0, sd=4, dt=1, n_c=65536)])
+def test_encode_empty_is_ok_without_launch(over):
+    assert enc(**over) == OK
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(sd=3), UNSUPPORTED), (dict(dt=5), UNSUPPORTED), (dict(n_c=0), INVALID),
+    (dict(idx=None), INVALID), (dict(out=None), INVALID), (dict(idx=FAKE + 2), MISALIGNED),
+    (dict(out=FAKE + 1), MISALIGNED), (dict(glen=10), INVALID),
+])
+def test_decode_rejects_on_host(over, code):
+    assert dec(**over) == code
+
+
+def test_decode_empty_is_ok():
+    assert dec(n=0) == OK
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(16, 8, dtype=torch.float16)
+    cb = torch.zeros(4, 8, dtype=torch.float16)
+    with pytest.raises(ValueError, match="device"):
+        vq.encode(x, cb)
+    with pytest.raises(ValueError, match="device"):
+        vq.decode(torch.zeros(16, dtype=torch.uint32), cb)
+
+
+def test_vqerror_message_names_the_status():
+    e = vq.VQError(-3, "vq_encode")
+    assert "VQ_ERR_MISALIGNED" in str(e) and "misaligned" in str(e)

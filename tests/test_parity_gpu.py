@@ -1,0 +1,223 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Small seeded cases span several tiles (1024 sub-vectors per workgroup) and
+LDS chunks (1024 centroids), with ragged tails, groups that do not align with
+tiles, padded slot strides, group maps with invalid slots, duplicate rows,
+non-finite values and the largest codebook the ABI allows.  The five full-size
+workloads run in the launch configuration the benchmark times; the oracle
+checks every row of the smaller ones and a seeded sample (plus the first and
+last tiles of several groups) of the full cache.  Acceptance rule: see
+tests/parity.py.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import product_vq_kv_amd as vq  # noqa: E402  (raises if the library is missing)
+
+DEV = torch.device("cuda:0")
+
+
+def to_dev(wl):
+    tdt = torch.float16 if wl.dtype == W.F16 else torch.bfloat16
+    x = torch.from_numpy(wl.x.view(np.int16)).view(tdt).to(DEV)
+    cb = torch.from_numpy(wl.codebook.view(np.int16)).view(tdt).to(DEV)
+    stride = wl.codebook_stride
+    need = wl.n_codebooks * stride
+    if cb.numel() < need:   # the last slot may be stored without its padding
+        cb = torch.cat([cb, torch.zeros(need - cb.numel(), dtype=tdt, device=DEV)])
+    cb3 = cb[:need].view(wl.n_codebooks, stride)[:, : wl.n_centroids * wl.sub_dim]
+    cb3 = cb3.view(wl.n_codebooks, wl.n_centroids, wl.sub_dim)
+    gmap = None if wl.group_map is None else torch.from_numpy(wl.group_map).to(DEV)
+    return x, cb3, gmap
+
+
+def gpu_encode(wl):
+    x, cb3, gmap = to_dev(wl)
+    cb = cb3[0] if wl.n_codebooks == 1 else cb3
+    out = vq.encode(x, cb, group_len=wl.group_len, group_map=gmap)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint32)
+
+
+def assert_parity(wl, got, rows=None):
+    rep = parity.compare(wl, got, rows)
+    print(f"[parity] {wl.name}: {rep.summary()}", flush=True)
+    assert rep.ok, rep.summary()
+    return rep
+
+
+SMALL = [
+    # (seed, n, sd, n_c, dtype, extra)
+    (1, 1, 8, 256, W.F16, {}),
+    (2, 255, 4, 256, W.F16, {}),
+    (3, 1024, 8, 256, W.F16, {}),
+    (4, 1025, 4, 256, W.BF16, {}),
+    (5, 5000, 8, 7, W.F16, {}),
+    (6, 3333, 4, 1, W.F16, {}),
+    (7, 4099, 8, 9, W.BF16, {}),
+    (8, 2500, 8, 1023, W.F16, {}),
+    (9, 2500, 4, 1024, W.BF16, {}),
+    (10, 2500, 8, 1025, W.F16, {}),
+    (11, 3000, 8, 4096, W.BF16, dict(dup_frac=0.05)),
+    (12, 7000, 4, 300, W.F16, dict(n_codebooks=7, group_len=1000, stride_pad=5)),
+    (13, 7000, 8, 64, W.BF16, dict(n_codebooks=3, group_len=3, use_map=True)),
+    (14, 9000, 8, 256, W.F16, dict(n_codebooks=4, group_len=2048, use_map=True, stride_pad=8)),
+    (15, 20000, 4, 256, W.F16, dict(dup_frac=0.2, scale=10.0)),
+    (16, 1500, 8, 256, W.F16, dict(scale=1e-3)),
+    (17, 1500, 4, 2, W.F16, {}),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}_n{c[1]}_sd{c[2]}_nc{c[3]}" for c in SMALL])
+def test_small_cases_match_oracle(case):
+    seed, n, sd, n_c, dt, extra = case
+    wl = W.random_case(seed, n, sd, n_c, dt, **extra)
+    print(f"[case] {wl.name} {extra}", flush=True)
+    got = gpu_encode(wl)
+    rep = assert_parity(wl, got)
+    assert rep.equal == rep.rows, "the direct-form kernel should be bit-identical"
+
+
+def test_max_centroids():
+    wl = W.random_case(30, 2100, 8, 65536, W.BF16, dup_frac=0.01)
+    print(f"[case] {wl.name}", flush=True)
+    assert_parity(wl, gpu_encode(wl))
+
+
+def test_bad_slots_give_sentinel():
+    wl = W.random_case(31, 5000, 8, 32, W.F16, n_codebooks=3, group_len=700, use_map=True)
+    wl.group_map = np.array([0, 2, -1, 1, 3, 2, 7, 0], np.int32)
+    got = gpu_encode(wl)
+    g = np.arange(wl.n) // wl.group_len
+    bad = np.isin(g, [2, 4, 6])
+    assert np.all(got[bad] == vq.BAD_SLOT)
+    assert_parity(wl, got)
+
+
+def test_exact_ties_on_a_coarse_grid():
+    r = np.random.default_rng(32)
+    for sd, dt in ((4, W.F16), (8, W.BF16)):
+        kx = 64 * r.integers(-2, 3, size=(6000, sd))
+        kc = 64 * r.integers(-2, 3, size=(200, sd))
+        bits = W.to_f16_bits if dt == W.F16 else W.to_bf16_bits
+        wl = W.Workload("grid ties", bits(kx / 64.0).reshape(-1, sd), bits(kc / 64.0).reshape(-1),
+                        sd, 200, dt, 200 * sd, 1, 6000)
+        rep = assert_parity(wl, gpu_encode(wl))
+        assert rep.equal == rep.rows
+
+
+def test_non_finite_values():
+    sd, n_c = 8, 40
+    r = np.random.default_rng(33)
+    x = r.standard_normal((3000, sd))
+    x[::7, 3] = np.nan
+    x[::11, 0] = np.inf
+    x[::13, 5] = -np.inf
+    c = r.standard_normal((n_c, sd))
+    c[0, 2] = np.nan
+    c[5, 1] = np.inf
+    c[9, :] = np.inf
+    for dt, bits in ((W.F16, W.to_f16_bits), (W.BF16, W.to_bf16_bits)):
+        wl = W.Workload("non-finite", bits(x).reshape(-1, sd), bits(c).reshape(-1), sd, n_c, dt,
+                        n_c * sd, 1, 3000)
+        rep = assert_parity(wl, gpu_encode(wl))
+        assert rep.equal == rep.rows
+
+
+def test_overflowing_and_subnormal_distances_bf16():
+    sd, n_c = 4, 16
+    r = np.random.default_rng(34)
+    x = np.concatenate([1e37 * r.standard_normal((500, sd)), 1e-20 * r.standard_normal((500, sd))])
+    c = np.concatenate([1e37 * r.standard_normal((8, sd)), 1e-20 * r.standard_normal((8, sd))])
+    wl = W.Workload("extremes", W.to_bf16_bits(x).reshape(-1, sd), W.to_bf16_bits(c).reshape(-1),
+                    sd, n_c, W.BF16, n_c * sd, 1, 1000)
+    rep = assert_parity(wl, gpu_encode(wl))
+    assert rep.equal == rep.rows
+
+
+def test_decode_matches_oracle_gather():
+    wl = W.random_case(35, 9000, 8, 100, W.BF16, n_codebooks=3, group_len=3500, stride_pad=4)
+    x, cb3, gmap = to_dev(wl)
+    idx = vq.encode(x, cb3, group_len=wl.group_len)
+    idx_np = idx.cpu().numpy().view(np.uint32).copy()
+    idx_np[::97] = 100            # out of range -> zero row
+    idx_np[5] = 0xFFFFFFFF
+    idx_t = torch.from_numpy(idx_np.view(np.int32)).to(DEV).view(torch.uint32)
+    rec = vq.decode(idx_t, cb3, group_len=wl.group_len)
+    torch.cuda.synchronize()
+    want = oracle.decode(idx_np, wl.codebook, 8, 100, wl.dtype, **wl.kwargs())
+    assert np.array_equal(rec.cpu().view(torch.int16).numpy().view(np.uint16), want)
+
+
+def test_empty_input_launches_nothing():
+    x = torch.empty(0, 8, dtype=torch.float16, device=DEV)
+    cb = torch.zeros(256, 8, dtype=torch.float16, device=DEV)
+    out = vq.encode(x, cb)
+    assert out.numel() == 0
+
+
+def test_misaligned_x_raises():
+    x = torch.zeros(1025 * 8, dtype=torch.float16, device=DEV)[4:4 + 1024 * 8]
+    cb = torch.zeros(256, 8, dtype=torch.float16, device=DEV)
+    with pytest.raises(vq.VQError, match="MISALIGNED"):
+        vq.encode(x, cb)
+
+
+def test_no_device_memory_is_allocated():
+    wl = W.random_case(36, 50000, 4, 256, W.F16)
+    x, cb3, _ = to_dev(wl)
+    out = torch.empty(wl.n, dtype=torch.uint32, device=DEV)
+    vq.encode(x, cb3[0], out=out)          # first launch loads the code object
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(3):
+        vq.encode(x, cb3[0], out=out)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_full_size_config_every_row(cfg):
+    wl = W.config(cfg)
+    print(f"[config {cfg}] {wl.name} n={wl.n}", flush=True)
+    got = gpu_encode(wl)
+    ref = parity.oracle_indices(wl)
+    rep = parity.compare(wl, got, ref_idx=ref)
+    print(f"[parity] {wl.name}: {rep.summary()}", flush=True)
+    assert rep.ok, rep.summary()
+    # the pages' own criterion: reconstruction MSE of both index sets
+    xf = W.bits_to_f32(wl.x, wl.dtype).astype(np.float64)
+    cbf = W.bits_to_f32(wl.codebook, wl.dtype).astype(np.float64).reshape(-1, wl.sub_dim)
+    mse_gpu = np.mean((xf - cbf[got]) ** 2)
+    mse_ref = np.mean((xf - cbf[ref]) ** 2)
+    print(f"[config {cfg}] mse gpu={mse_gpu:.6e} oracle={mse_ref:.6e} "
+          f"equal rows {rep.equal}/{rep.rows}", flush=True)
+    assert abs(mse_gpu - mse_ref) <= 1e-6 * mse_ref
+
+
+def test_full_cache_sampled_rows():
+    wl = W.config(4)
+    print(f"[config 4] {wl.name} n={wl.n}", flush=True)
+    got = gpu_encode(wl)
+    r = np.random.default_rng(44)
+    rows = [r.choice(wl.n, size=1 << 17, replace=False)]
+    for g in (0, 1, 127, 128, 200, 255):      # first and last tiles of some groups
+        lo = g * wl.group_len
+        rows += [np.arange(lo, lo + 1024), np.arange(lo + wl.group_len - 1024, lo + wl.group_len)]
+    rows = np.unique(np.concatenate(rows))
+    assert_parity(wl, got, rows)

@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
 # Pages' own figure for the same workload, on an Apple-Silicon GPU (context):
 # 1,048,576 sub-vectors in 7.98 ms (post's "The Numbers" throughput table).
 PAGES_FALCON_SUBVEC_PER_S = 1048576 / 7.98e-3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_falcon3_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_falcon3_traffic.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "product_vq_kv_amd", "csrc", "vq_encode.hip")
 
 
@@ -53,8 +53,9 @@ def traffic_bytes_per_launch():
     None when there is none or the kernel source changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            rows = [ln for ln in f if ln.strip() and not ln.startswith("#")]
+        t = json.loads(rows[-1])
+    except (OSError, ValueError, IndexError):
         return None
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None

@@ -9,7 +9,9 @@ Flags:
   * -ffp-contract=off: the only fused operations are the explicit fmaf calls,
     so the distance arithmetic is exactly the documented sequence;
   * -fno-gpu-flush-denormals-to-zero: fp32 subnormals are kept, as IEEE (and
-    the CPU reference) does.
+    the CPU reference) does;
+  * -mllvm -amdgpu-mfma-vgpr-form: matrix-core results land in ordinary VGPRs,
+    so the VALU reduction reads them without v_accvgpr_read copies.
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -66,10 +66,19 @@ vq_status vq_encode(const void *x, const void *codebook, int64_t n, int32_t sub_
   if (reinterpret_cast<uintptr_t>(x) % (2 * sub_dim) != 0) return VQ_ERR_MISALIGNED;
   if (reinterpret_cast<uintptr_t>(out_idx) % 4 != 0) return VQ_ERR_MISALIGNED;
   if (n == 0) return VQ_OK;
-  if (vqk::encode_grid(l) > kMaxGrid) return VQ_ERR_INVALID_ARG;
+  if (vqk::encode_grid(l) > kMaxGrid || vqk::encode_mfma_grid(l) > kMaxGrid)
+    return VQ_ERR_INVALID_ARG;
   (void)hipGetLastError();  // drop a stale error so it is not reported as ours
+#ifdef VQ_ENCODE_DIRECT_ONLY
   return device_result(
       vqk::launch_encode(x, codebook, group_map, out_idx, l, static_cast<hipStream_t>(stream)));
+#else
+  if (vqk::encode_mfma_supported(l))
+    return device_result(vqk::launch_encode_mfma(x, codebook, group_map, out_idx, l,
+                                                 static_cast<hipStream_t>(stream)));
+  return device_result(
+      vqk::launch_encode(x, codebook, group_map, out_idx, l, static_cast<hipStream_t>(stream)));
+#endif
 }
 
 vq_status vq_decode(const uint32_t *idx, const void *codebook, int64_t n, int32_t sub_dim,

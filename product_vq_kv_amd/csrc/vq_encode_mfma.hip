@@ -1,0 +1,647 @@
+// vq_encode_mfma.hip -- product-VQ encode on gfx950 matrix cores, exact result.
+//
+// The operation (VeloxQuant-MLX blog, "I Wrote a Metal Kernel to Stop My Mac
+// From OOMing", sections "What quantize_vq Was Doing Wrong" and "The Kernel: 18
+// Lines of MSL") is the strict-< argmin over centroids of the fp32 distance
+// d = x_i - c_i, dist = fma(d, d, dist) (components in order).  This kernel
+// returns exactly that index; it uses the matrix cores only to find, cheaply,
+// the few centroids that can possibly win.
+//
+// Stage 1 (one v_mfma_f32_32x32x8 per 32 centroids x 32 sub-vectors):
+//   M(c) = C(c) - x.c, with C(c) = |c|^2/2 shrunk by the error bound below.
+//   Products of fp16/bf16 inputs are exact in fp32; the matrix unit's
+//   accumulation of the m = sub_dim + 1 nonzero terms errs by at most
+//   eta_m (sum |terms|), eta_m = 2 (m + 1) u, u = 2^-24 (one rounding of at
+//   most 2u per addition, in any order; measured below 5u on gfx950).  Each
+//   lane owns 16 of the 32 rows of a block (its "group"); the group minimum
+//   of M minus a(g) b(x), with a(g) >= kappa max_{c in g} |c| and b(x) >= |x|,
+//   bounds every centroid of the group from below:
+//       L(g) <= s(c) = |c|^2/2 - x.c   for all c in g,
+//   and |x - c|^2 = |x|^2 + 2 s(c), so ranking by s is ranking by distance.
+//   Per sub-vector the lanes keep the smallest group bound m1, its group g1
+//   and the second smallest group bound m2.
+// Stage 2 (exact): the 16 rows of g1 are evaluated in the fixed fp32
+//   arithmetic above (8 rows on each lane of the pair that shares the
+//   sub-vector).  With D the smallest such distance, the oracle's winner c*
+//   satisfies s(c*) <= U = (D (1 + 2 gamma) - |x|^2_low) / 2, gamma = (sub_dim
+//   + 2) u (rounding bound of the fp32 distance), so its group's bound is
+//   <= U.  If m2 > U no centroid outside g1 can be c*, and the lowest-index
+//   minimum over g1 is the answer, bit for bit.  Otherwise the sub-vector is
+//   ambiguous: every group whose bound is <= U is recomputed exactly (the
+//   bounds are recomputed on the matrix cores), which again contains c*.
+//   Non-finite or huge values take a full exact strict-< scan.
+// Exact duplicate rows: a row bit-identical to an earlier row has the same
+//   fp32 distance and can never win the strict-< scan; such rows are found
+//   with an LDS hash table per workgroup and excluded from stage 1 (C = +inf),
+//   so they do not make every nearby sub-vector ambiguous.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "vq_launch.h"
+
+namespace vqk {
+namespace {
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kMfmaMaxCentroids = 4096;    // whole codebook slot resident in LDS
+constexpr int kRows32MaxCentroids = 1024;  // up to here an fp32 copy is kept too
+constexpr float kU = 5.9604644775390625e-08f;       // 2^-24
+constexpr float kTau = 7.174648137343064e-43f;      // 2^-140: absolute slack
+constexpr float kNormCap = 1.2676506002282294e30f;  // 2^100: beyond it, exact path
+constexpr float kNormUp = 1.0000038146972656f;      // 1 + 2^-18: upward norm margin
+constexpr float kNegMax = -3.4028234663852886e38f;  // med3(a, b, kNegMax) = min(a, b)
+
+template <int SD>
+struct Consts {
+  static constexpr float kEta = (2.0f * (SD + 2) + 2.0f) * kU;  // eta_m + 2u (final fma)
+  static constexpr float kKappa = 1.125f * kEta;                // > eta / (1 - u)
+  static constexpr float kHalfShrink = 0.5f * (1.0f - kEta - 9.5367431640625e-07f);
+  static constexpr float kGamma2 = 2.0f * (SD + 2) * kU * 1.01f;  // >= 1/(1-gamma) - 1
+};
+
+template <bool BF16>
+__device__ __forceinline__ float widen(uint16_t v) {
+  if constexpr (BF16) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+  } else {
+    return static_cast<float>(__builtin_bit_cast(_Float16, v));
+  }
+}
+
+template <int SD>
+__device__ __forceinline__ float sqdist(const float (&xv)[SD], const float (&c)[SD]) {
+  float d = xv[0] - c[0];
+  float acc = d * d;  // = fma(d, d, +0)
+#pragma unroll
+  for (int i = 1; i < SD; ++i) {
+    d = xv[i] - c[i];
+    acc = __builtin_fmaf(d, d, acc);
+  }
+  return acc;
+}
+
+// Element j of the 16-bit values packed in w (two per word).
+__device__ __forceinline__ uint16_t half_of(const uint32_t *w, int j) {
+  return static_cast<uint16_t>((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1]);
+}
+
+template <int SD, bool BF16>
+__device__ __forceinline__ void widen_words(const uint32_t *w, uint16_t flip, float (&v)[SD]) {
+#pragma unroll
+  for (int i = 0; i < SD; ++i) v[i] = widen<BF16>(half_of(w, i) ^ flip);
+}
+
+template <int SD>
+__device__ __forceinline__ uint32_t hash_row(const uint4 &q) {
+  uint32_t h = 0x9e3779b9u;
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < SD / 2; ++i) {
+    h ^= w[i];
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+  }
+  return h * 0xc2b2ae35u;
+}
+
+template <int SD>
+__device__ __forceinline__ bool same_row(const uint4 &a, const uint4 &b) {
+  return (SD == 4) ? (a.x == b.x && a.y == b.y)
+                   : (a.x == b.x && a.y == b.y && a.z == b.z && a.w == b.w);
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma(const uint2 &a, const uint2 &b, const f32x16 &c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(f16x4, a),
+                                                __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+}
+
+// Minimum of the 16 values (finite or +inf).  The first step is a med3 with
+// -FLT_MAX, which equals min for such values and needs no NaN quieting.
+__device__ __forceinline__ float min16(const f32x16 &v) {
+  float a = __builtin_amdgcn_fmed3f(v[0], v[1], kNegMax);
+  a = fminf(fminf(a, v[2]), v[3]);
+  a = fminf(fminf(a, v[4]), v[5]);
+  a = fminf(fminf(a, v[6]), v[7]);
+  a = fminf(fminf(a, v[8]), v[9]);
+  a = fminf(fminf(a, v[10]), v[11]);
+  a = fminf(fminf(a, v[12]), v[13]);
+  return fminf(fminf(a, v[14]), v[15]);
+}
+
+// Per-workgroup LDS (dynamic) for one codebook slot of n_c centroids, padded
+// to n_cpad = roundup(n_c, 32):
+//   rows [n_cpad] uint4     A operand: halves 0..7 = -c_0 .. -c_{SD-1}, zero
+//                           padded (K = 8; lane half h reads halves 4h..4h+3);
+//   cval [n_cpad] float     C operand: shrunk |c|^2/2, +inf for padding and
+//                           duplicate rows;
+//   gan  [n_cpad/16] float  per 16-row group: kappa max |c| (rounded up);
+//   c32  [n_cpad][SD] float the centroids in fp32 (ROWS32 only);
+//   hash [hash_slots] int   duplicate detection while staging.
+template <int SD, bool ROWS32>
+struct Lds {
+  uint4 *rows;
+  float *cval;
+  float *gan;
+  float *c32;
+  int *hash;
+  __device__ Lds(uint4 *base, int n_cpad) {
+    rows = base;
+    cval = reinterpret_cast<float *>(rows + n_cpad);
+    gan = cval + n_cpad;
+    c32 = gan + n_cpad / 16;
+    hash = reinterpret_cast<int *>(c32 + (ROWS32 ? n_cpad * SD : 0));
+  }
+  static size_t bytes(int n_cpad, int hash_slots) {
+    return static_cast<size_t>(n_cpad) * (16 + 4 + (ROWS32 ? 4 * SD : 0)) +
+           static_cast<size_t>(n_cpad / 16) * 4 + static_cast<size_t>(hash_slots) * 4;
+  }
+};
+
+// Group (16 rows) of row r: block r/32, half ((r%32)/4)%2.
+__device__ __forceinline__ int group_of(int r) { return 2 * (r >> 5) + ((r >> 2) & 1); }
+
+// Centroid c as fp32, from the fp32 copy or widened from the staged -c bits.
+template <int SD, bool BF16, bool ROWS32>
+__device__ __forceinline__ void centroid(const Lds<SD, ROWS32> &s, int c, float (&v)[SD]) {
+  if constexpr (ROWS32) {
+#pragma unroll
+    for (int q = 0; q < SD / 4; ++q) {
+      const float4 w = *reinterpret_cast<const float4 *>(s.c32 + c * SD + 4 * q);
+      v[4 * q] = w.x;
+      v[4 * q + 1] = w.y;
+      v[4 * q + 2] = w.z;
+      v[4 * q + 3] = w.w;
+    }
+  } else {
+    const uint4 q = s.rows[c];
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    widen_words<SD, BF16>(w, 0x8000u, v);
+  }
+}
+
+// Stage one codebook slot.  Returns true when some centroid has a non-finite
+// or huge norm: then every sub-vector of the slot takes the full exact scan.
+template <int SD, bool BF16, bool ROWS32, int BLOCK>
+__device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_cpad,
+                               const Lds<SD, ROWS32> &s, int hash_slots) {
+  using K = Consts<SD>;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < hash_slots; i += BLOCK) s.hash[i] = -1;
+  for (int i = tid; i < n_cpad / 16; i += BLOCK) s.gan[i] = 0.0f;
+  __syncthreads();
+  int flag = 0;
+  for (int r = tid; r < n_cpad; r += BLOCK) {
+    uint16_t k8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float v[SD];
+#pragma unroll
+    for (int i = 0; i < SD; ++i) v[i] = 0.0f;
+    float cv = __builtin_inff();
+    if (r < n_c) {
+      // element loads: a slot only has to be 2-byte aligned
+      const uint16_t *p = cb + static_cast<int64_t>(r) * SD;
+#pragma unroll
+      for (int i = 0; i < SD; ++i) {
+        const uint16_t e = p[i];
+        v[i] = widen<BF16>(e);
+        k8[i] = e ^ 0x8000u;  // -c, exact
+      }
+      float n2c = v[0] * v[0];
+#pragma unroll
+      for (int i = 1; i < SD; ++i) n2c = __builtin_fmaf(v[i], v[i], n2c);
+      if (!(n2c <= kNormCap)) {
+        flag = 1;
+      } else {
+        cv = n2c * K::kHalfShrink - 2.0f * kTau;
+        const float an = __builtin_sqrtf(n2c) * kNormUp * K::kKappa;
+        // non-negative floats order like their bit patterns
+        atomicMax(reinterpret_cast<int *>(&s.gan[group_of(r)]), __float_as_int(an));
+      }
+    }
+    s.rows[r] = make_uint4(k8[0] | (static_cast<uint32_t>(k8[1]) << 16),
+                           k8[2] | (static_cast<uint32_t>(k8[3]) << 16),
+                           k8[4] | (static_cast<uint32_t>(k8[5]) << 16),
+                           k8[6] | (static_cast<uint32_t>(k8[7]) << 16));
+    s.cval[r] = cv;
+    if constexpr (ROWS32) {
+#pragma unroll
+      for (int q = 0; q < SD / 4; ++q)
+        *reinterpret_cast<float4 *>(s.c32 + r * SD + 4 * q) =
+            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+  }
+  const bool exact = __syncthreads_or(flag) != 0;
+  if (!exact) {
+    // A row bit-identical to an earlier row can never win the strict-< scan.
+    // Open addressing, at most half full: each distinct row value keeps the
+    // smallest index that has it.
+    const int mask = hash_slots - 1;
+    for (int r = tid; r < n_c; r += BLOCK) {
+      const uint4 q = s.rows[r];
+      int slot = static_cast<int>(hash_row<SD>(q)) & mask;
+      for (int probe = 0; probe < hash_slots; ++probe) {
+        const int old = atomicCAS(&s.hash[slot], -1, r);
+        if (old == -1) break;
+        if (same_row<SD>(s.rows[old], q)) {
+          atomicMin(&s.hash[slot], r);
+          break;
+        }
+        slot = (slot + 1) & mask;
+      }
+    }
+    __syncthreads();
+    for (int r = tid; r < n_c; r += BLOCK) {
+      const uint4 q = s.rows[r];
+      int slot = static_cast<int>(hash_row<SD>(q)) & mask;
+      int first = r;
+      for (int probe = 0; probe < hash_slots; ++probe) {
+        const int v = s.hash[slot];
+        if (v < 0) break;
+        if (same_row<SD>(s.rows[v], q)) {
+          first = v;
+          break;
+        }
+        slot = (slot + 1) & mask;
+      }
+      if (first < r) s.cval[r] = __builtin_inff();
+    }
+    __syncthreads();
+  }
+  return exact;
+}
+
+// Lowest-index strict-< minimum of the exact distance over 4 consecutive rows
+// from c0 (rows >= n_c excluded); rows are visited in ascending order.
+template <int SD, bool BF16, bool ROWS32>
+__device__ __forceinline__ void exact4(const Lds<SD, ROWS32> &s, const float (&xv)[SD], int c0,
+                                       int n_c, float &best, int &bi) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = c0 + i;
+    float cv[SD];
+    centroid<SD, BF16, ROWS32>(s, min(c, n_c - 1), cv);
+    float d = sqdist<SD>(xv, cv);
+    d = (c < n_c) ? d : __builtin_inff();
+    const bool lt = d < best;
+    best = lt ? d : best;
+    bi = lt ? c : bi;
+  }
+}
+
+// Combine (distance, index) over the two lanes of a pair: smaller distance,
+// then lower index.
+__device__ __forceinline__ void pair_min(float &best, int &bi) {
+  const float ob = __shfl_xor(best, 32);
+  const int oi = __shfl_xor(bi, 32);
+  const bool take = ob < best || (ob == best && oi < bi);
+  best = take ? ob : best;
+  bi = take ? oi : bi;
+}
+
+// The full sub-vector of a column from the two halves held by the pair.
+template <int SD, bool BF16>
+__device__ __forceinline__ void column_x(const uint2 &own, int h, float (&xv)[SD]) {
+  const uint2 o = make_uint2(__shfl_xor(own.x, 32), __shfl_xor(own.y, 32));
+  uint32_t w[4];
+  const uint2 lo = (h == 0) ? own : o;
+  w[0] = lo.x;
+  w[1] = lo.y;
+  if constexpr (SD == 4) {
+    w[2] = w[3] = 0;
+  } else {
+    const uint2 hi = (h == 0) ? o : own;
+    w[2] = hi.x;
+    w[3] = hi.y;
+  }
+  widen_words<SD, BF16>(w, 0, xv);
+}
+
+// One tile: every wave encodes T columns of 32 sub-vectors.
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32>
+__device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64_t gend, int n_c,
+                            int n_cpad, const Lds<SD, ROWS32> &s, bool exact_tile,
+                            uint32_t *__restrict__ out) {
+  using K = Consts<SD>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int h = lane >> 5;  // half of the block's rows / K slots this lane holds
+  const int col = lane & 31;
+  const int nblk = n_cpad / 32;
+
+  uint2 bop[T];  // this lane's K slots 4h..4h+3 of its column
+  float bn[T];   // upper bound of |x|
+  float m1[T], m2[T];
+  int g1[T];
+  uint32_t full = 0;  // bit t: column t takes the full exact scan
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t row = tbase + (wave * T + t) * 32 + col;
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (row < gend) {
+      if constexpr (SD == 4) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(x + row * 4);
+        w[0] = q.x;
+        w[1] = q.y;
+      } else {
+        const uint4 q = *reinterpret_cast<const uint4 *>(x + row * 8);
+        w[0] = q.x;
+        w[1] = q.y;
+        w[2] = q.z;
+        w[3] = q.w;
+      }
+    }
+    float xv[SD];
+    widen_words<SD, BF16>(w, 0, xv);
+    float n2x = xv[0] * xv[0];
+#pragma unroll
+    for (int i = 1; i < SD; ++i) n2x = __builtin_fmaf(xv[i], xv[i], n2x);
+    const bool ex = !(n2x <= kNormCap) || exact_tile;
+    full |= (ex ? 1u : 0u) << t;
+    bn[t] = ex ? 0.0f : __builtin_sqrtf(n2x) * kNormUp;
+    if constexpr (SD == 4) {
+      bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(0, 0);
+    } else {
+      bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(w[2], w[3]);
+    }
+    m1[t] = __builtin_inff();
+    m2[t] = __builtin_inff();
+    g1[t] = 0;
+  }
+
+  const uint2 *arow = reinterpret_cast<const uint2 *>(s.rows) + 2 * col + h;
+  auto c_operand = [&](int blk) {
+    f32x16 cop;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 q = *reinterpret_cast<const float4 *>(&s.cval[blk * 32 + 8 * j + 4 * h]);
+      cop[4 * j + 0] = q.x;
+      cop[4 * j + 1] = q.y;
+      cop[4 * j + 2] = q.z;
+      cop[4 * j + 3] = q.w;
+    }
+    return cop;
+  };
+
+  // ---- stage 1: group lower bounds on the matrix cores ---------------------
+  if (!exact_tile) {
+    for (int blk = 0; blk < nblk; ++blk) {
+      const uint2 aop = arow[blk * 64];
+      const f32x16 cop = c_operand(blk);
+      const float an = s.gan[2 * blk + h];
+      const int grp = 2 * blk + h;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
+        m2[t] = __builtin_amdgcn_fmed3f(m1[t], m2[t], mb);
+        g1[t] = (mb < m1[t]) ? grp : g1[t];
+        m1[t] = __builtin_amdgcn_fmed3f(m1[t], mb, kNegMax);
+      }
+    }
+  }
+
+  // ---- stage 2: exact resolution (lanes col and col+32 share a column) -----
+  float best[T], U[T];
+  int bi[T];
+  uint32_t amb = 0;  // bit t: column t is ambiguous across groups
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    float xv[SD];
+    column_x<SD, BF16>(bop[t], h, xv);
+    const float om1 = __shfl_xor(m1[t], 32);
+    const float om2 = __shfl_xor(m2[t], 32);
+    const int og1 = __shfl_xor(g1[t], 32);
+    const bool mine = m1[t] < om1;
+    const bool theirs = om1 < m1[t];
+    const int cg1 = mine ? g1[t] : (theirs ? og1 : min(g1[t], og1));
+    const float cm2 = mine ? fminf(m2[t], om1) : (theirs ? fminf(om2, m1[t]) : m1[t]);
+    // rows of group cg1 (block b, half hh): b*32 + 8j + 4hh + i; this lane
+    // takes j = 2h and 2h + 1, in ascending row order
+    const int c0 = (cg1 >> 1) * 32 + 16 * h + 4 * (cg1 & 1);
+    best[t] = __builtin_inff();
+    bi[t] = 0x7fffffff;
+    exact4<SD, BF16, ROWS32>(s, xv, c0, n_c, best[t], bi[t]);
+    exact4<SD, BF16, ROWS32>(s, xv, c0 + 8, n_c, best[t], bi[t]);
+    pair_min(best[t], bi[t]);
+    float n2x = xv[0] * xv[0];
+#pragma unroll
+    for (int i = 1; i < SD; ++i) n2x = __builtin_fmaf(xv[i], xv[i], n2x);
+    const float xl = n2x * (1.0f - (SD + 2) * kU);
+    // s(c*) <= (best (1 + 2 gamma) - |x|^2) / 2; the two rounded operations
+    // below are covered by (best + xl) 2u, kTau covers subnormal steps.
+    float u = (best[t] * (1.0f + K::kGamma2) - xl) * 0.5f;
+    u = u + (best[t] + xl) * (2.0f * kU) + kTau;
+    U[t] = u;
+    if (!(best[t] < __builtin_inff())) full |= 1u << t;
+    if (!((full >> t) & 1u) && !(cm2 > u)) amb |= 1u << t;
+  }
+
+  // ---- ambiguous columns: every group whose bound can reach U contains the
+  // oracle's winner if any does; recompute those groups exactly ------------
+  if (__any(amb != 0)) {
+    float fb[T];
+    int fi[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      fb[t] = __builtin_inff();
+      fi[t] = 0x7fffffff;
+    }
+    for (int blk = 0; blk < nblk; ++blk) {
+      const uint2 aop = arow[blk * 64];
+      const f32x16 cop = c_operand(blk);
+      const float an = s.gan[2 * blk + h];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        if (__any((amb >> t) & 1u)) {
+          const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
+          const bool cand = ((amb >> t) & 1u) && mb <= U[t];
+          if (__any(cand)) {
+            float xv[SD];
+            column_x<SD, BF16>(bop[t], h, xv);
+            if (cand) {
+              const int c0 = blk * 32 + 4 * h;
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                exact4<SD, BF16, ROWS32>(s, xv, c0 + 8 * j, n_c, fb[t], fi[t]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      pair_min(fb[t], fi[t]);
+      const bool a = (amb >> t) & 1u;
+      best[t] = a ? fb[t] : best[t];
+      bi[t] = a ? fi[t] : bi[t];
+    }
+  }
+
+  // ---- non-finite or huge values: full exact strict-< scan, split by parity
+  if (__any(full != 0)) {
+    float fb[T];
+    int fi[T];
+    float xv[T][SD];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      fb[t] = __builtin_inff();
+      fi[t] = 0x7fffffff;
+      column_x<SD, BF16>(bop[t], h, xv[t]);
+    }
+    // same trip count on both lanes of a pair; lane h takes rows c0 + h
+    for (int c0 = 0; c0 < n_c; c0 += 2) {
+      const int c = c0 + h;
+      float cv[SD];
+      centroid<SD, BF16, ROWS32>(s, min(c, n_c - 1), cv);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        float d = sqdist<SD>(xv[t], cv);
+        d = (c < n_c) ? d : __builtin_inff();
+        const bool lt = d < fb[t];
+        fb[t] = lt ? d : fb[t];
+        fi[t] = lt ? c : fi[t];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      pair_min(fb[t], fi[t]);
+      const bool f = (full >> t) & 1u;
+      best[t] = f ? fb[t] : best[t];
+      bi[t] = f ? fi[t] : bi[t];
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t row = tbase + (wave * T + t) * 32 + col;
+    if (row < gend && h == 0) out[row] = (bi[t] == 0x7fffffff) ? 0u : static_cast<uint32_t>(bi[t]);
+  }
+}
+
+// Persistent workgroups: workgroup w encodes tiles [w*k, (w+1)*k) of the
+// group-major tile sequence and stages a codebook slot only when it changes.
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32>
+__global__ void __launch_bounds__(BLOCK)
+encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ codebook,
+                   int64_t n, int n_c, int64_t cb_stride, int64_t n_codebooks, int64_t group_len,
+                   int64_t tiles_per_group, int64_t total_tiles, int64_t tiles_per_wg,
+                   const int32_t *__restrict__ group_map, uint32_t *__restrict__ out,
+                   int hash_slots) {
+  constexpr int kTile = (BLOCK / 64) * T * 32;
+  extern __shared__ uint4 lds_raw[];
+  const int n_cpad = (n_c + 31) & ~31;
+  const Lds<SD, ROWS32> s(lds_raw, n_cpad);
+
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * tiles_per_wg;
+  const int64_t last = min(first + tiles_per_wg, total_tiles);
+  int64_t staged = -1;
+  bool exact_tile = false;
+  for (int64_t tile = first; tile < last; ++tile) {
+    const int64_t g = tile / tiles_per_group;
+    const int64_t gstart = g * group_len;
+    const int64_t gend = min(gstart + group_len, n);
+    const int64_t tbase = gstart + (tile - g * tiles_per_group) * kTile;
+    if (tbase >= gend) continue;  // uniform: tile past a short group's end
+    const int64_t slot = group_map ? static_cast<int64_t>(group_map[g]) : g;
+    if (slot < 0 || slot >= n_codebooks) {
+      for (int64_t r = tbase + threadIdx.x; r < min(tbase + kTile, gend); r += BLOCK)
+        out[r] = 0xFFFFFFFFu;
+      continue;  // uniform
+    }
+    if (slot != staged) {
+      __syncthreads();  // every wave is done with the previous slot
+      exact_tile = stage_codebook<SD, BF16, ROWS32, BLOCK>(codebook + slot * cb_stride, n_c,
+                                                           n_cpad, s, hash_slots);
+      staged = slot;
+    }
+    encode_tile<SD, T, BLOCK, BF16, ROWS32>(x, tbase, gend, n_c, n_cpad, s, exact_tile, out);
+  }
+}
+
+template <int BLOCK>
+constexpr int tile_of(int T) { return (BLOCK / 64) * T * 32; }
+
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32>
+hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_map, uint32_t *out,
+                    const Layout &l, hipStream_t stream, int64_t cus) {
+  constexpr int kTile = tile_of<BLOCK>(T);
+  const int64_t span = l.group_len < l.n ? l.group_len : l.n;
+  const int64_t tiles_per_group = (span + kTile - 1) / kTile;
+  const int64_t total_tiles = tiles_per_group * l.n_groups;
+  const int n_cpad = (l.n_centroids + 31) & ~31;
+  int hash_slots = 64;
+  while (hash_slots < 2 * l.n_centroids) hash_slots <<= 1;
+  const size_t lds = Lds<SD, ROWS32>::bytes(n_cpad, hash_slots);
+  auto kern = encode_mfma_kernel<SD, T, BLOCK, BF16, ROWS32>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, BLOCK, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) per_cu = 1;
+  const int64_t wgs = std::min<int64_t>(total_tiles, cus * per_cu);
+  const int64_t tiles_per_wg = (total_tiles + wgs - 1) / wgs;
+  const int64_t grid = (total_tiles + tiles_per_wg - 1) / tiles_per_wg;
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(BLOCK), lds, stream,
+                     static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(codebook),
+                     l.n, l.n_centroids, l.codebook_stride, l.n_codebooks, l.group_len,
+                     tiles_per_group, total_tiles, tiles_per_wg, group_map, out, hash_slots);
+  return hipGetLastError();
+}
+
+int cu_count() {
+  static int cached = 0;
+  if (cached > 0) return cached;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  cached = cus;
+  return cus;
+}
+
+template <int SD, bool BF16>
+hipError_t launch_sd(const void *x, const void *codebook, const int32_t *group_map, uint32_t *out,
+                     const Layout &l, hipStream_t stream) {
+  const int64_t cus = cu_count();
+  if (l.n_centroids > kRows32MaxCentroids)
+    return launch_t<SD, 4, 1024, BF16, false>(x, codebook, group_map, out, l, stream, cus);
+  return launch_t<SD, 4, 256, BF16, true>(x, codebook, group_map, out, l, stream, cus);
+}
+
+}  // namespace
+
+bool encode_mfma_supported(const Layout &l) { return l.n_centroids <= kMfmaMaxCentroids; }
+
+int64_t encode_mfma_grid(const Layout &l) {
+  // upper bound on the workgroups of any plan above (one tile per workgroup)
+  const int64_t tile = tile_of<256>(4);
+  const int64_t span = l.group_len < l.n ? l.group_len : l.n;
+  return (span + tile - 1) / tile * l.n_groups;
+}
+
+hipError_t launch_encode_mfma(const void *x, const void *codebook, const int32_t *group_map,
+                              uint32_t *out_idx, const Layout &l, hipStream_t stream) {
+  if (l.sub_dim == 4) {
+    return l.bf16 ? launch_sd<4, true>(x, codebook, group_map, out_idx, l, stream)
+                  : launch_sd<4, false>(x, codebook, group_map, out_idx, l, stream);
+  }
+  return l.bf16 ? launch_sd<8, true>(x, codebook, group_map, out_idx, l, stream)
+                : launch_sd<8, false>(x, codebook, group_map, out_idx, l, stream);
+}
+
+}  // namespace vqk

@@ -25,6 +25,13 @@ int64_t encode_grid(const Layout &l);
 hipError_t launch_encode(const void *x, const void *codebook, const int32_t *group_map,
                          uint32_t *out_idx, const Layout &l, hipStream_t stream);
 
+// The matrix-core encode keeps the whole codebook slot in LDS: up to 4096 centroids.
+bool encode_mfma_supported(const Layout &l);
+int64_t encode_mfma_grid(const Layout &l);
+
+hipError_t launch_encode_mfma(const void *x, const void *codebook, const int32_t *group_map,
+                              uint32_t *out_idx, const Layout &l, hipStream_t stream);
+
 hipError_t launch_decode(const uint32_t *idx, const void *codebook, const int32_t *group_map,
                          void *out_x, const Layout &l, hipStream_t stream);
 

@@ -85,7 +85,7 @@ def test_small_cases_match_oracle(case):
     print(f"[case] {wl.name} {extra}", flush=True)
     got = gpu_encode(wl)
     rep = assert_parity(wl, got)
-    assert rep.equal == rep.rows, "the direct-form kernel should be bit-identical"
+    assert rep.equal == rep.rows, "the encode is exact: every index must equal the oracle's"
 
 
 def test_max_centroids():
@@ -132,6 +132,58 @@ def test_non_finite_values():
                         n_c * sd, 1, 3000)
         rep = assert_parity(wl, gpu_encode(wl))
         assert rep.equal == rep.rows
+
+
+@pytest.mark.parametrize("n_c", [41, 40])
+def test_non_finite_values_odd_codebook(n_c):
+    # non-finite x takes the full exact scan, split over a lane pair: an odd
+    # number of centroids gives the two lanes different halves
+    sd = 4
+    r = np.random.default_rng(37)
+    x = r.standard_normal((5000, sd))
+    x[::5, 1] = np.nan
+    x[::9, 2] = np.inf
+    c = r.standard_normal((n_c, sd))
+    wl = W.Workload("non-finite x, odd n_c", W.to_f16_bits(x).reshape(-1, sd),
+                    W.to_f16_bits(c).reshape(-1), sd, n_c, W.F16, n_c * sd, 1, 5000)
+    rep = assert_parity(wl, gpu_encode(wl))
+    assert rep.equal == rep.rows
+
+
+@pytest.mark.parametrize("sd,dt", [(4, W.F16), (8, W.BF16)])
+def test_near_tied_centroids_across_groups(sd, dt):
+    # centroids in pairs one or two ulps apart, placed in different 16-row
+    # groups, and sub-vectors sitting between them: most columns are ambiguous
+    # after the matrix-core stage and must be resolved exactly
+    r = np.random.default_rng(38 + sd)
+    n_c = 512
+    base = r.standard_normal((n_c // 2, sd))
+    bits = W.to_f16_bits if dt == W.F16 else W.to_bf16_bits
+    a = bits(base).reshape(-1, sd)
+    b = a.copy()
+    b[:, 0] = b[:, 0] + r.integers(1, 3, size=b.shape[0]).astype(np.uint16)   # +1..2 ulp
+    cb = np.empty((n_c, sd), np.uint16)
+    perm = r.permutation(n_c)
+    cb[perm[: n_c // 2]] = a
+    cb[perm[n_c // 2:]] = b
+    xf = W.bits_to_f32(a, dt).astype(np.float64)
+    pick = r.integers(0, n_c // 2, size=20000)
+    x = xf[pick] + 1e-3 * r.standard_normal((20000, sd))
+    wl = W.Workload("near-tied pairs", bits(x).reshape(-1, sd), cb.reshape(-1), sd, n_c, dt,
+                    n_c * sd, 1, 20000)
+    rep = assert_parity(wl, gpu_encode(wl))
+    assert rep.equal == rep.rows
+
+
+def test_huge_codebook_norms_odd_bf16():
+    sd, n_c = 8, 33
+    r = np.random.default_rng(39)
+    x = 1e25 * r.standard_normal((3000, sd))
+    c = 1e25 * r.standard_normal((n_c, sd))
+    wl = W.Workload("huge norms", W.to_bf16_bits(x).reshape(-1, sd), W.to_bf16_bits(c).reshape(-1),
+                    sd, n_c, W.BF16, n_c * sd, 1, 3000)
+    rep = assert_parity(wl, gpu_encode(wl))
+    assert rep.equal == rep.rows
 
 
 def test_overflowing_and_subnormal_distances_bf16():

@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
 # 1,048,576 sub-vectors in 7.98 ms (post's "The Numbers" throughput table).
 PAGES_FALCON_SUBVEC_PER_S = 1048576 / 7.98e-3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_falcon3_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "product_vq_kv_amd", "csrc", "vq_encode.hip")
+KERNEL_SOURCES = os.path.join(ROOT, "product_vq_kv_amd", "csrc")
 
 
 def log(msg: str) -> None:
@@ -44,8 +44,14 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every HIP/C++ source of the library (any change invalidates
+    counter figures taken on an earlier build)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_bytes_per_launch():

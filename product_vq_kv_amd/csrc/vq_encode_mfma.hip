@@ -342,7 +342,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
   float bn[T];   // upper bound of |x|
   float m1[T], m2[T];
   int g1[T];
-  uint32_t full = 0;  // bit t: column t takes the full exact scan
+  uint32_t full_bits = 0;  // bit t: column t takes the full exact scan
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int64_t row = tbase + (wave * T + t) * 32 + col;
@@ -366,7 +366,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
 #pragma unroll
     for (int i = 1; i < SD; ++i) n2x = __builtin_fmaf(xv[i], xv[i], n2x);
     const bool ex = !(n2x <= kNormCap) || exact_tile;
-    full |= (ex ? 1u : 0u) << t;
+    full_bits |= (ex ? 1u : 0u) << t;
     bn[t] = ex ? 0.0f : __builtin_sqrtf(n2x) * kNormUp;
     if constexpr (SD == 4) {
       bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(0, 0);
@@ -409,10 +409,8 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
     }
   }
 
-  // ---- stage 2: exact resolution (lanes col and col+32 share a column) -----
-  float best[T], U[T];
-  int bi[T];
-  uint32_t amb = 0;  // bit t: column t is ambiguous across groups
+  // ---- stage 2: exact resolution, one column at a time (lanes col and
+  // col+32 share a column) ---------------------------------------------------
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     float xv[SD];
@@ -427,103 +425,63 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
     // rows of group cg1 (block b, half hh): b*32 + 8j + 4hh + i; this lane
     // takes j = 2h and 2h + 1, in ascending row order
     const int c0 = (cg1 >> 1) * 32 + 16 * h + 4 * (cg1 & 1);
-    best[t] = __builtin_inff();
-    bi[t] = 0x7fffffff;
-    exact4<SD, BF16, ROWS32>(s, xv, c0, n_c, best[t], bi[t]);
-    exact4<SD, BF16, ROWS32>(s, xv, c0 + 8, n_c, best[t], bi[t]);
-    pair_min(best[t], bi[t]);
+    float best = __builtin_inff();
+    int bi = 0x7fffffff;
+    exact4<SD, BF16, ROWS32>(s, xv, c0, n_c, best, bi);
+    exact4<SD, BF16, ROWS32>(s, xv, c0 + 8, n_c, best, bi);
+    pair_min(best, bi);
     float n2x = xv[0] * xv[0];
 #pragma unroll
     for (int i = 1; i < SD; ++i) n2x = __builtin_fmaf(xv[i], xv[i], n2x);
     const float xl = n2x * (1.0f - (SD + 2) * kU);
     // s(c*) <= (best (1 + 2 gamma) - |x|^2) / 2; the two rounded operations
     // below are covered by (best + xl) 2u, kTau covers subnormal steps.
-    float u = (best[t] * (1.0f + K::kGamma2) - xl) * 0.5f;
-    u = u + (best[t] + xl) * (2.0f * kU) + kTau;
-    U[t] = u;
-    if (!(best[t] < __builtin_inff())) full |= 1u << t;
-    if (!((full >> t) & 1u) && !(cm2 > u)) amb |= 1u << t;
-  }
+    float U = (best * (1.0f + K::kGamma2) - xl) * 0.5f;
+    U = U + (best + xl) * (2.0f * kU) + kTau;
+    const bool full = ((full_bits >> t) & 1u) || !(best < __builtin_inff());
+    const bool amb = !full && !(cm2 > U);
 
-  // ---- ambiguous columns: every group whose bound can reach U contains the
-  // oracle's winner if any does; recompute those groups exactly ------------
-  if (__any(amb != 0)) {
-    float fb[T];
-    int fi[T];
+    // ambiguous: every group whose bound can reach U contains the oracle's
+    // winner if any does; those groups are recomputed exactly
+    if (__any(amb)) {
+      float fb = __builtin_inff();
+      int fi = 0x7fffffff;
+      for (int blk = 0; blk < nblk; ++blk) {
+        const uint2 aop = arow[blk * 64];
+        const f32x16 cop = c_operand(blk);
+        const float an = s.gan[2 * blk + h];
+        const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
+        if (amb && mb <= U) {
+          const int r0 = blk * 32 + 4 * h;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      fb[t] = __builtin_inff();
-      fi[t] = 0x7fffffff;
-    }
-    for (int blk = 0; blk < nblk; ++blk) {
-      const uint2 aop = arow[blk * 64];
-      const f32x16 cop = c_operand(blk);
-      const float an = s.gan[2 * blk + h];
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        if (__any((amb >> t) & 1u)) {
-          const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
-          const bool cand = ((amb >> t) & 1u) && mb <= U[t];
-          if (__any(cand)) {
-            float xv[SD];
-            column_x<SD, BF16>(bop[t], h, xv);
-            if (cand) {
-              const int c0 = blk * 32 + 4 * h;
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                exact4<SD, BF16, ROWS32>(s, xv, c0 + 8 * j, n_c, fb[t], fi[t]);
-            }
-          }
+          for (int j = 0; j < 4; ++j) exact4<SD, BF16, ROWS32>(s, xv, r0 + 8 * j, n_c, fb, fi);
         }
       }
+      pair_min(fb, fi);
+      best = amb ? fb : best;
+      bi = amb ? fi : bi;
     }
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      pair_min(fb[t], fi[t]);
-      const bool a = (amb >> t) & 1u;
-      best[t] = a ? fb[t] : best[t];
-      bi[t] = a ? fi[t] : bi[t];
-    }
-  }
-
-  // ---- non-finite or huge values: full exact strict-< scan, split by parity
-  if (__any(full != 0)) {
-    float fb[T];
-    int fi[T];
-    float xv[T][SD];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      fb[t] = __builtin_inff();
-      fi[t] = 0x7fffffff;
-      column_x<SD, BF16>(bop[t], h, xv[t]);
-    }
-    // same trip count on both lanes of a pair; lane h takes rows c0 + h
-    for (int c0 = 0; c0 < n_c; c0 += 2) {
-      const int c = c0 + h;
-      float cv[SD];
-      centroid<SD, BF16, ROWS32>(s, min(c, n_c - 1), cv);
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        float d = sqdist<SD>(xv[t], cv);
+    // non-finite or huge values: full exact strict-< scan, split by parity
+    if (__any(full)) {
+      float fb = __builtin_inff();
+      int fi = 0x7fffffff;
+      // same trip count on both lanes of a pair; lane h takes rows r0 + h
+      for (int r0 = 0; r0 < n_c; r0 += 2) {
+        const int c = r0 + h;
+        float cv[SD];
+        centroid<SD, BF16, ROWS32>(s, min(c, n_c - 1), cv);
+        float d = sqdist<SD>(xv, cv);
         d = (c < n_c) ? d : __builtin_inff();
-        const bool lt = d < fb[t];
-        fb[t] = lt ? d : fb[t];
-        fi[t] = lt ? c : fi[t];
+        const bool lt = d < fb;
+        fb = lt ? d : fb;
+        fi = lt ? c : fi;
       }
+      pair_min(fb, fi);
+      best = full ? fb : best;
+      bi = full ? fi : bi;
     }
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      pair_min(fb[t], fi[t]);
-      const bool f = (full >> t) & 1u;
-      best[t] = f ? fb[t] : best[t];
-      bi[t] = f ? fi[t] : bi[t];
-    }
-  }
-
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
     const int64_t row = tbase + (wave * T + t) * 32 + col;
-    if (row < gend && h == 0) out[row] = (bi[t] == 0x7fffffff) ? 0u : static_cast<uint32_t>(bi[t]);
+    if (row < gend && h == 0) out[row] = (bi == 0x7fffffff) ? 0u : static_cast<uint32_t>(bi);
   }
 }
 

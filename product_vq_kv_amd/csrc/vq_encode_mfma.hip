@@ -281,17 +281,18 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
 }
 
 // Lowest-index strict-< minimum of the exact distance over 4 consecutive rows
-// from c0 (rows >= n_c excluded); rows are visited in ascending order.
-template <int SD, bool BF16, bool ROWS32>
+// from c0; rows are visited in ascending order.  With MASK, rows >= n_c (the
+// padding of the last block) are excluded; without it every row is < n_c.
+template <int SD, bool BF16, bool ROWS32, bool MASK = true>
 __device__ __forceinline__ void exact4(const Lds<SD, ROWS32> &s, const float (&xv)[SD], int c0,
                                        int n_c, float &best, int &bi) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = c0 + i;
     float cv[SD];
-    centroid<SD, BF16, ROWS32>(s, min(c, n_c - 1), cv);
+    centroid<SD, BF16, ROWS32>(s, MASK ? min(c, n_c - 1) : c, cv);
     float d = sqdist<SD>(xv, cv);
-    d = (c < n_c) ? d : __builtin_inff();
+    if (MASK) d = (c < n_c) ? d : __builtin_inff();
     const bool lt = d < best;
     best = lt ? d : best;
     bi = lt ? c : bi;
@@ -340,6 +341,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
 
   uint2 bop[T];  // this lane's K slots 4h..4h+3 of its column
   float bn[T];   // upper bound of |x|
+  float nx2[T];  // fp32 |x|^2 as the exact stage computes it
   float m1[T], m2[T];
   int g1[T];
   uint32_t full_bits = 0;  // bit t: column t takes the full exact scan
@@ -365,6 +367,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
     float n2x = xv[0] * xv[0];
 #pragma unroll
     for (int i = 1; i < SD; ++i) n2x = __builtin_fmaf(xv[i], xv[i], n2x);
+    nx2[t] = n2x;
     const bool ex = !(n2x <= kNormCap) || exact_tile;
     full_bits |= (ex ? 1u : 0u) << t;
     bn[t] = ex ? 0.0f : __builtin_sqrtf(n2x) * kNormUp;
@@ -427,13 +430,15 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
     const int c0 = (cg1 >> 1) * 32 + 16 * h + 4 * (cg1 & 1);
     float best = __builtin_inff();
     int bi = 0x7fffffff;
-    exact4<SD, BF16, ROWS32>(s, xv, c0, n_c, best, bi);
-    exact4<SD, BF16, ROWS32>(s, xv, c0 + 8, n_c, best, bi);
+    if (n_c & 31) {  // uniform: the last block has padding rows
+      exact4<SD, BF16, ROWS32, true>(s, xv, c0, n_c, best, bi);
+      exact4<SD, BF16, ROWS32, true>(s, xv, c0 + 8, n_c, best, bi);
+    } else {
+      exact4<SD, BF16, ROWS32, false>(s, xv, c0, n_c, best, bi);
+      exact4<SD, BF16, ROWS32, false>(s, xv, c0 + 8, n_c, best, bi);
+    }
     pair_min(best, bi);
-    float n2x = xv[0] * xv[0];
-#pragma unroll
-    for (int i = 1; i < SD; ++i) n2x = __builtin_fmaf(xv[i], xv[i], n2x);
-    const float xl = n2x * (1.0f - (SD + 2) * kU);
+    const float xl = nx2[t] * (1.0f - (SD + 2) * kU);
     // s(c*) <= (best (1 + 2 gamma) - |x|^2) / 2; the two rounded operations
     // below are covered by (best + xl) 2u, kTau covers subnormal steps.
     float U = (best * (1.0f + K::kGamma2) - xl) * 0.5f;

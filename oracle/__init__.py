@@ -11,9 +11,14 @@ function computes, and which passage of the VeloxQuant-MLX blog post "I Wrote
 a Metal Kernel to Stop My Mac From OOMing" it follows, is stated in the C
 file's header.
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-(exact integer brute force, hand-built known answers, the sub_dim = 1
-boundary-sum special case, conversion against library routines).
+Parity status: every function here is pinned.  ``tests/test_oracle_pins.py``
+pins the search (exact integer brute force, hand-built known answers, the
+sub_dim = 1 boundary-sum special case, conversion against library routines);
+``tests/test_oracle_smooth_pack.py`` pins smoothing, the search over fp32
+sub-vectors and the packed code stream (numpy's float32 multiply and
+little-endian packbits, the pages' worked packing examples, exact rational
+brute force).  ``tests/test_oracle_mutants.py`` checks that planted mistakes
+fail those pins.
 """
 from __future__ import annotations
 
@@ -65,6 +70,19 @@ def _load():
         lib.vqo_sqdist.restype = ctypes.c_float
         lib.vqo_to_f32.argtypes = [ctypes.c_uint16, i32]
         lib.vqo_to_f32.restype = ctypes.c_float
+        lib.vqo_smooth.argtypes = [p, i64, i32, i32, p, i32, i64, i64, i64, p, p]
+        lib.vqo_smooth.restype = i32
+        lib.vqo_encode_f32.argtypes = [p, p, i64, i32, i32, i32, i64, i64, i64, p, p, p, p]
+        lib.vqo_encode_f32.restype = i32
+        lib.vqo_packed_bytes.argtypes = [i64, i32]
+        lib.vqo_packed_bytes.restype = i64
+        lib.vqo_pack.argtypes = [p, i64, i32, p]
+        lib.vqo_pack.restype = i32
+        lib.vqo_unpack.argtypes = [p, i64, i32, p]
+        lib.vqo_unpack.restype = i32
+        lib.vqo_encode_packed.argtypes = [p, p, i64, i32, i32, i32, i64, i64, i64, p, p, i32,
+                                          i64, i32, p]
+        lib.vqo_encode_packed.restype = i32
         _lib = lib
         return lib
 
@@ -241,3 +259,120 @@ def sqdist_rows(x, codebook, rows, idx, sub_dim, dtype, *, codebook_stride=None,
 def to_f32(bits: int, dtype: int) -> float:
     """The oracle's own fp16/bf16 -> fp32 widening of one value."""
     return float(_load().vqo_to_f32(int(bits) & 0xFFFF, dtype))
+
+
+# ---------------------------------------------------------------------------
+# Smoothing and packed codes (the steps either side of the search)
+# ---------------------------------------------------------------------------
+
+def _scale_arr(channel_scale):
+    if channel_scale is None:
+        return None
+    return np.ascontiguousarray(channel_scale, dtype=np.float32).reshape(-1)
+
+
+def smooth(x, sub_dim, dtype, *, channel_scale=None, head_dim=None, scale_stride=0,
+           n_codebooks=1, group_len=None, group_map=None):
+    """Smoothed fp32 sub-vectors [n, sub_dim]: each channel times its factor."""
+    x = _u16(x).reshape(-1)
+    n = x.size // sub_dim
+    head_dim = sub_dim if head_dim is None else head_dim
+    glen = max(n, 1) if group_len is None else group_len
+    gmap = None if group_map is None else np.ascontiguousarray(group_map, dtype=np.int32)
+    sc = _scale_arr(channel_scale)
+    out = np.empty((n, sub_dim), dtype=np.float32)
+    if n:
+        rc = _load().vqo_smooth(_ptr(x), n, sub_dim, dtype, _ptr(sc), head_dim, scale_stride,
+                                n_codebooks, glen, _ptr(gmap), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def encode_f32(xs, codebook, sub_dim, n_centroids, dtype, *, codebook_stride=None,
+               n_codebooks=1, group_len=None, group_map=None, want_top2=False, threads=1):
+    """The search over fp32 sub-vectors; (idx, best, second) with want_top2."""
+    xs = np.ascontiguousarray(xs, dtype=np.float32).reshape(-1, sub_dim)
+    n = xs.shape[0]
+    cb = _u16(codebook).reshape(-1)
+    stride = n_centroids * sub_dim if codebook_stride is None else codebook_stride
+    glen = max(n, 1) if group_len is None else group_len
+    gmap = None if group_map is None else np.ascontiguousarray(group_map, dtype=np.int32)
+    lib = _load()
+    out = np.empty(n, dtype=np.uint32)
+    best = np.empty(n, dtype=np.float32) if want_top2 else None
+    second = np.empty(n, dtype=np.float32) if want_top2 else None
+    bounds = np.linspace(0, n, max(1, threads if n >= 4096 else 1) + 1).astype(np.int64)
+    errs = []
+
+    def work(lo, hi):
+        g = np.arange(lo, hi, dtype=np.int64) // glen
+        slots = (gmap[g] if gmap is not None else g).astype(np.int32)
+        rc = lib.vqo_encode_f32(_ptr(xs[lo:hi]), _ptr(cb), hi - lo, sub_dim, n_centroids, dtype,
+                                stride, n_codebooks, 1, _ptr(slots), out[lo:hi].ctypes.data,
+                                None if best is None else best[lo:hi].ctypes.data,
+                                None if second is None else second[lo:hi].ctypes.data)
+        if rc != 0:
+            errs.append(rc)
+
+    ts = [threading.Thread(target=work, args=(int(bounds[i]), int(bounds[i + 1])))
+          for i in range(len(bounds) - 1) if bounds[i + 1] > bounds[i]]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    if errs:
+        raise ValueError("oracle rejected its arguments")
+    return (out, best, second) if want_top2 else out
+
+
+def packed_bytes(n: int, code_bits: int) -> int:
+    return int(_load().vqo_packed_bytes(n, code_bits))
+
+
+def pack(codes, code_bits: int) -> np.ndarray:
+    """LSB-first bit stream of the low ``code_bits`` bits of every code."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint32).reshape(-1)
+    out = np.empty(packed_bytes(codes.size, code_bits), dtype=np.uint8)
+    if _load().vqo_pack(_ptr(codes), codes.size, code_bits, _ptr(out)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def unpack(stream, n: int, code_bits: int) -> np.ndarray:
+    stream = np.ascontiguousarray(stream, dtype=np.uint8).reshape(-1)
+    if stream.size < packed_bytes(n, code_bits):
+        raise ValueError("stream shorter than n codes")
+    out = np.empty(n, dtype=np.uint32)
+    if _load().vqo_unpack(_ptr(stream), n, code_bits, _ptr(out)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def encode_packed(x, codebook, sub_dim, n_centroids, dtype, *, channel_scale=None,
+                  head_dim=None, scale_stride=0, code_bits=8, codebook_stride=None,
+                  n_codebooks=1, group_len=None, group_map=None, threads=1):
+    """Smooth, search and pack: the stored code stream for raw keys ``x``.
+
+    ``threads == 1`` is the single C routine; otherwise the same three steps
+    run with the search sliced over threads (identical result).
+    """
+    x, cb, n, stride, glen, gmap = _common(x, codebook, sub_dim, n_centroids,
+                                           codebook_stride, n_codebooks, group_len, group_map)
+    head_dim = sub_dim if head_dim is None else head_dim
+    sc = _scale_arr(channel_scale)
+    if threads <= 1:
+        out = np.empty(packed_bytes(n, code_bits), dtype=np.uint8)
+        rc = _load().vqo_encode_packed(_ptr(x), _ptr(cb), n, sub_dim, n_centroids, dtype, stride,
+                                       n_codebooks, glen, _ptr(gmap), _ptr(sc), head_dim,
+                                       scale_stride, code_bits, _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return out
+    if code_bits < 32 and n_centroids > (1 << code_bits):
+        raise ValueError("oracle rejected its arguments")
+    xs = smooth(x, sub_dim, dtype, channel_scale=sc, head_dim=head_dim, scale_stride=scale_stride,
+                n_codebooks=n_codebooks, group_len=glen, group_map=gmap)
+    idx = encode_f32(xs, cb, sub_dim, n_centroids, dtype, codebook_stride=stride,
+                     n_codebooks=n_codebooks, group_len=glen, group_map=gmap, threads=threads)
+    return pack(idx, code_bits)

@@ -38,6 +38,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define VQO_F16 0
@@ -208,4 +209,195 @@ int vqo_decode(const uint32_t *idx, const uint16_t *codebook, int64_t n, int sub
         for (int i = 0; i < sub_dim; ++i) dst[i] = src[i];
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * The two steps on either side of the search in a VecInfer key cache.
+ *
+ * Smoothing (VeloxQuant-MLX blog, post introducing the library's nine
+ * algorithms, section "VecInfer -- 16x with Metal acceleration": a scale per
+ * channel tames the outlier channels that defeat plain VQ; "I Wrote a Metal
+ * Kernel to Stop My Mac From OOMing", section "How to Use This Today": the
+ * cache is configured with calibrated smooth factors, and section "What's
+ * Next: Phase 2": the attention LUT is built from the correspondingly
+ * transformed query q_tilde).  Reading taken: every channel of a key is
+ * multiplied by its own fp32 factor (one IEEE multiply, rounded to nearest
+ * even) before the search, and the search then runs on those fp32 values
+ * exactly as in vqo_encode.  Smoothing by a divisor s is the multiplier 1/s.
+ * The key cache is laid out [..][tokens][head_dim] and cut into sub-vectors
+ * along head_dim, so component i of sub-vector r is channel
+ * (r mod (head_dim / sub_dim)) * sub_dim + i.  The factor vector is chosen by
+ * the codebook slot of the sub-vector: slot s uses
+ * channel_scale[s * scale_stride .. + head_dim) (scale_stride 0 = one vector
+ * for every slot).
+ *
+ * Packed codes ("I Wrote a Metal Kernel ...", section "What Even Is a KV
+ * Cache And Why Should You Care": a 128-dim fp16 key becomes 16 indices of 8
+ * bits; "How I built VeloxQuant-MLX -- KV cache compression for LLMs running
+ * on your Mac", section "The Bit-Packing Problem": b-bit indices are packed
+ * back to back into bytes, least significant bit first, an index may straddle
+ * a byte boundary).  Code r occupies bits r*b .. r*b + b - 1 of the stream,
+ * bit k of the stream being bit (k mod 8) of byte k / 8; the unused high bits
+ * of the last byte are zero.  A sub-vector whose slot is out of range gets a
+ * code of b one-bits (the low b bits of the 0xFFFFFFFF sentinel).
+ * ------------------------------------------------------------------------ */
+
+/* Distance from an fp32 sub-vector to one fp16/bf16 centroid: the same
+ * sequence as vqo_sqdist with the sub-vector already in fp32. */
+static float sqdist_f32(const float *xs, const uint16_t *crow, int sub_dim, int dtype)
+{
+    float dist = 0.0f;
+    for (int i = 0; i < sub_dim; ++i) {
+        float d = xs[i] - widen(crow[i], dtype);
+        dist = fmaf(d, d, dist);
+    }
+    return dist;
+}
+
+/*
+ * Smoothed sub-vectors: xs[r][i] = fp32(x[r][i]) * factor of its channel.
+ * channel_scale NULL means every factor is 1 (xs is the exact widening).
+ * Rows whose slot is out of range are filled with NaN.  head_dim must be a
+ * positive multiple of sub_dim.  Returns 0, or -1 on a bad argument.
+ */
+int vqo_smooth(const uint16_t *x, int64_t n, int sub_dim, int dtype,
+               const float *channel_scale, int head_dim, int64_t scale_stride,
+               int64_t n_codebooks, int64_t group_len, const int32_t *group_map, float *xs)
+{
+    if (n < 0 || sub_dim < 1 || (dtype != VQO_F16 && dtype != VQO_BF16) ||
+        n_codebooks < 1 || group_len < 1 || head_dim < sub_dim || head_dim % sub_dim ||
+        scale_stride < 0)
+        return -1;
+    const int n_sub = head_dim / sub_dim;
+    for (int64_t r = 0; r < n; ++r) {
+        int64_t slot;
+        float *dst = xs + r * sub_dim;
+        if (!slot_of(r, group_len, group_map, n_codebooks, &slot)) {
+            for (int i = 0; i < sub_dim; ++i) dst[i] = NAN;
+            continue;
+        }
+        const int64_t ch0 = (r % n_sub) * sub_dim;
+        for (int i = 0; i < sub_dim; ++i) {
+            float v = widen(x[r * sub_dim + i], dtype);
+            if (channel_scale) v = v * channel_scale[slot * scale_stride + ch0 + i];
+            dst[i] = v;
+        }
+    }
+    return 0;
+}
+
+/*
+ * The search of vqo_encode over fp32 sub-vectors xs [n][sub_dim] against
+ * fp16/bf16 codebook slots.  best_out and second_out may be NULL; when given
+ * they receive the winning distance and the minimum over every other centroid
+ * (as in vqo_encode_top2).
+ */
+int vqo_encode_f32(const float *xs, const uint16_t *codebook, int64_t n, int sub_dim,
+                   int n_centroids, int dtype, int64_t codebook_stride, int64_t n_codebooks,
+                   int64_t group_len, const int32_t *group_map, uint32_t *out,
+                   float *best_out, float *second_out)
+{
+    if (!args_ok(n, sub_dim, n_centroids, dtype, n_codebooks, group_len)) return -1;
+    for (int64_t r = 0; r < n; ++r) {
+        int64_t slot;
+        if (!slot_of(r, group_len, group_map, n_codebooks, &slot)) {
+            out[r] = VQO_BAD_SLOT;
+            if (best_out) best_out[r] = NAN;
+            if (second_out) second_out[r] = NAN;
+            continue;
+        }
+        const uint16_t *cb = codebook + slot * codebook_stride;
+        const float *xr = xs + r * sub_dim;
+        float best = INFINITY;
+        uint32_t best_idx = 0;
+        for (int c = 0; c < n_centroids; ++c) {
+            float dist = sqdist_f32(xr, cb + (int64_t)c * sub_dim, sub_dim, dtype);
+            if (dist < best) {
+                best = dist;
+                best_idx = (uint32_t)c;
+            }
+        }
+        out[r] = best_idx;
+        if (best_out) best_out[r] = best;
+        if (second_out) {
+            float second = INFINITY;
+            for (int c = 0; c < n_centroids; ++c) {
+                if ((uint32_t)c == best_idx) continue;
+                float dist = sqdist_f32(xr, cb + (int64_t)c * sub_dim, sub_dim, dtype);
+                if (dist < second) second = dist;
+            }
+            second_out[r] = second;
+        }
+    }
+    return 0;
+}
+
+/* Bytes of a stream of n codes of code_bits bits. */
+int64_t vqo_packed_bytes(int64_t n, int code_bits)
+{
+    return (n * code_bits + 7) / 8;
+}
+
+/*
+ * Pack n codes into the LSB-first bit stream, one bit at a time: bit k of
+ * code r goes to stream bit r*code_bits + k.  Only the low code_bits bits of
+ * each code are kept.  out receives vqo_packed_bytes(n, code_bits) bytes.
+ */
+int vqo_pack(const uint32_t *codes, int64_t n, int code_bits, uint8_t *out)
+{
+    if (n < 0 || code_bits < 1 || code_bits > 32) return -1;
+    memset(out, 0, (size_t)vqo_packed_bytes(n, code_bits));
+    for (int64_t r = 0; r < n; ++r) {
+        for (int k = 0; k < code_bits; ++k) {
+            int64_t bit = r * code_bits + k;
+            uint32_t b = (codes[r] >> k) & 1u;
+            out[bit / 8] |= (uint8_t)(b << (bit % 8));
+        }
+    }
+    return 0;
+}
+
+/* Inverse of vqo_pack. */
+int vqo_unpack(const uint8_t *in, int64_t n, int code_bits, uint32_t *codes)
+{
+    if (n < 0 || code_bits < 1 || code_bits > 32) return -1;
+    for (int64_t r = 0; r < n; ++r) {
+        uint32_t c = 0;
+        for (int k = 0; k < code_bits; ++k) {
+            int64_t bit = r * code_bits + k;
+            c |= (uint32_t)((in[bit / 8] >> (bit % 8)) & 1u) << k;
+        }
+        codes[r] = c;
+    }
+    return 0;
+}
+
+/*
+ * Smooth, search, pack: the encode of a VecInfer key cache from raw keys to
+ * stored codes.  Requires n_centroids <= 2^code_bits.  out_codes receives
+ * vqo_packed_bytes(n, code_bits) bytes.  Returns 0, -1 on a bad argument, -2
+ * when scratch memory cannot be had.
+ */
+int vqo_encode_packed(const uint16_t *x, const uint16_t *codebook, int64_t n, int sub_dim,
+                      int n_centroids, int dtype, int64_t codebook_stride, int64_t n_codebooks,
+                      int64_t group_len, const int32_t *group_map, const float *channel_scale,
+                      int head_dim, int64_t scale_stride, int code_bits, uint8_t *out_codes)
+{
+    if (!args_ok(n, sub_dim, n_centroids, dtype, n_codebooks, group_len) ||
+        code_bits < 1 || code_bits > 32 ||
+        (code_bits < 32 && (int64_t)n_centroids > ((int64_t)1 << code_bits)))
+        return -1;
+    float *xs = malloc((size_t)(n > 0 ? n : 1) * sub_dim * sizeof(float));
+    uint32_t *idx = malloc((size_t)(n > 0 ? n : 1) * sizeof(uint32_t));
+    int rc = (xs && idx) ? 0 : -2;
+    if (rc == 0)
+        rc = vqo_smooth(x, n, sub_dim, dtype, channel_scale, head_dim, scale_stride,
+                        n_codebooks, group_len, group_map, xs);
+    if (rc == 0)
+        rc = vqo_encode_f32(xs, codebook, n, sub_dim, n_centroids, dtype, codebook_stride,
+                            n_codebooks, group_len, group_map, idx, NULL, NULL);
+    if (rc == 0) rc = vqo_pack(idx, n, code_bits, out_codes);
+    free(xs);
+    free(idx);
+    return rc;
 }

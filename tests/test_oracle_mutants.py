@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_pins as pins
+from tests import test_oracle_smooth_pack as sp
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "vq_oracle.c")
 
@@ -37,6 +38,21 @@ MUTANTS = {
                          "float best = INFINITY;\n        uint32_t best_idx = (uint32_t)(n_centroids - 1);\n        for (int c = 0; c < n_centroids; ++c) {\n            float dist = vqo_sqdist(xr, cb + (int64_t)c * sub_dim, sub_dim, dtype);\n            if (dist < best) {\n                best = dist;\n                best_idx = (uint32_t)c;\n            }\n        }\n        out[r] = best_idx;"),
     "decode_accepts_n_centroids": ("idx[r] >= (uint32_t)n_centroids", "idx[r] > (uint32_t)n_centroids"),
     "bf16_wrong_half": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    # smoothing, the fp32 search and the packed stream
+    "pack_msb_first": ("out[bit / 8] |= (uint8_t)(b << (bit % 8));",
+                       "out[bit / 8] |= (uint8_t)(b << (7 - bit % 8));"),
+    "pack_drops_top_bit": ("for (int k = 0; k < code_bits; ++k) {\n            int64_t bit = r * code_bits + k;\n            uint32_t b",
+                           "for (int k = 0; k + 1 < code_bits; ++k) {\n            int64_t bit = r * code_bits + k;\n            uint32_t b"),
+    "smooth_channel_unscaled": ("const int64_t ch0 = (r % n_sub) * sub_dim;",
+                                "const int64_t ch0 = (r % n_sub);"),
+    "smooth_ignores_slot": ("channel_scale[slot * scale_stride + ch0 + i]", "channel_scale[ch0 + i]"),
+    "smooth_adds": ("v = v * channel_scale[", "v = v + channel_scale["),
+    "f32_search_plus": ("float d = xs[i] - widen(crow[i], dtype);",
+                        "float d = xs[i] + widen(crow[i], dtype);"),
+    "f32_bad_slot_zero": ("out[r] = VQO_BAD_SLOT;\n            if (best_out)",
+                          "out[r] = 0;\n            if (best_out)"),
+    "top2_second_counts_winner": ("if ((uint32_t)c == best_idx) continue;\n                float dist = sqdist_f32",
+                                  "float dist = sqdist_f32"),
 }
 
 PIN_TESTS = [
@@ -51,6 +67,14 @@ PIN_TESTS = [
     lambda: pins.test_group_slots_select_the_right_codebook(),
     lambda: pins.test_decode_gathers_rows_and_zeroes_bad_indices(),
     lambda: pins.test_bf16_widening_matches_torch_every_pattern(),
+    lambda: sp.test_pack_golden_examples_from_the_pages(),
+    lambda: [sp.test_pack_matches_numpy_little_endian_bits(b) for b in (1, 3, 8, 13, 32)],
+    lambda: sp.test_smooth_matches_numpy_float32_multiply_in_cache_layout(),
+    lambda: sp.test_power_of_two_factors_equal_encode_of_prescaled_keys(),
+    lambda: sp.test_smoothed_search_against_exact_rational_brute_force(oracle.F16),
+    lambda: sp.test_factor_vector_follows_the_codebook_slot(),
+    lambda: sp.test_bad_slot_gets_all_ones_code_and_threads_agree(),
+    lambda: sp.test_encode_f32_top2_second_is_the_runner_up(),
 ]
 
 

@@ -55,8 +55,10 @@ typedef enum {
 typedef enum {
     VQ_OK = 0,
     VQ_ERR_INVALID_ARG = -1, /* null pointer with n > 0, bad count, stride or group layout */
-    VQ_ERR_UNSUPPORTED = -2, /* sub_dim not 4 or 8, unknown dtype, n_centroids > 65536 */
-    VQ_ERR_MISALIGNED = -3,  /* x not aligned to 2*sub_dim bytes, codebook to 2, idx/out to 4 */
+    VQ_ERR_UNSUPPORTED = -2, /* sub_dim not 4 or 8, unknown dtype, n_centroids > 65536,
+                                packed groups not ending on a 32-bit word of the stream */
+    VQ_ERR_MISALIGNED = -3,  /* x not aligned to 2*sub_dim bytes, codebook to 2,
+                                idx/out/codes/factors to 4 */
     VQ_ERR_DEVICE = -4       /* the HIP launch failed; see vq_last_hip_error() */
 } vq_status;
 
@@ -64,7 +66,8 @@ typedef enum {
  * a valid slot (outside [0, n_codebooks)). */
 #define VQ_BAD_SLOT 0xFFFFFFFFu
 #define VQ_MAX_CENTROIDS 65536
-#define VQ_ABI_VERSION 1
+#define VQ_MAX_HEAD_DIM 4096
+#define VQ_ABI_VERSION 2
 
 /*
  * vq_encode -- nearest-centroid index of every sub-vector.
@@ -91,6 +94,54 @@ vq_status vq_encode(const void *x, const void *codebook, int64_t n, int32_t sub_
                     int32_t n_centroids, vq_dtype dtype, int64_t codebook_stride,
                     int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
                     uint32_t *out_idx, void *stream);
+
+/*
+ * vq_encode_packed -- vq_encode with the two steps either side of the search
+ * in a VecInfer key cache fused in: per-channel smoothing on load and packed
+ * b-bit codes on store.
+ *
+ * Smoothing: VeloxQuant-MLX blog, post introducing the library's nine
+ * algorithms, section "VecInfer -- 16x with Metal acceleration" (a scale per
+ * channel handles the outlier channels that defeat plain VQ), and "I Wrote a
+ * Metal Kernel to Stop My Mac From OOMing", section "How to Use This Today"
+ * (the cache takes calibrated smooth factors).  Every channel of a key is
+ * multiplied by its fp32 factor (one IEEE multiply, round to nearest even)
+ * and the search of vq_encode runs on those fp32 values with the same
+ * arithmetic and tie rule.  Smoothing by a divisor s is the factor 1/s (the
+ * matching query transform, q_tilde of the post's section "What's Next:
+ * Phase 2", is then q * s).  Keys are laid out [..][tokens][head_dim] and cut
+ * along head_dim, so component i of sub-vector r is channel
+ * (r mod (head_dim/sub_dim)) * sub_dim + i, and sub-vector r uses the factor
+ * vector of its codebook slot k: channel_scale + k * scale_stride.
+ *
+ * Codes: "I Wrote a Metal Kernel ...", section "What Even Is a KV Cache And
+ * Why Should You Care" (16 indices of 8 bits per 128-dim key: 16x), and "How
+ * I built VeloxQuant-MLX -- KV cache compression for LLMs running on your
+ * Mac", section "The Bit-Packing Problem" (indices packed back to back, least
+ * significant bit first, crossing byte boundaries).  Code r occupies bits
+ * r*code_bits .. r*code_bits + code_bits - 1 of out_codes, bit k being bit
+ * k mod 8 of byte k / 8; the unused high bits of the last byte are written as
+ * zero.  A group whose slot is invalid gets codes of code_bits one-bits.
+ *
+ *   channel_scale  device fp32 factors, aligned to 4 bytes, or NULL (no
+ *                  smoothing: the codes are vq_encode's indices).
+ *   head_dim       channels per key, a multiple of sub_dim, <= VQ_MAX_HEAD_DIM
+ *                  (ignored when channel_scale is NULL).
+ *   scale_stride   floats between the factor vectors of consecutive slots;
+ *                  0 = one vector [head_dim] for every slot.
+ *   code_bits      1 .. 32 with n_centroids <= 2^code_bits (8 for the pages'
+ *                  256-centroid codebooks).
+ *   out_codes      device, ceil(n*code_bits/8) bytes, aligned to 4 bytes; no
+ *                  byte beyond that length is written.
+ *   other arguments as for vq_encode.
+ * With several groups, group_len*code_bits must be a multiple of 32 (groups
+ * start on a 32-bit word of the stream), else VQ_ERR_UNSUPPORTED.
+ */
+vq_status vq_encode_packed(const void *x, const void *codebook, int64_t n, int32_t sub_dim,
+                           int32_t n_centroids, vq_dtype dtype, int64_t codebook_stride,
+                           int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
+                           const float *channel_scale, int32_t head_dim, int64_t scale_stride,
+                           int32_t code_bits, void *out_codes, void *stream);
 
 /*
  * vq_decode -- gather used to check encode: row n of out_x is centroid idx[n]

@@ -9,6 +9,7 @@ is missing or cannot be loaded, importing this package raises.
     import torch, product_vq_kv_amd as vq
     idx = vq.encode(keys_subvectors, codebook)          # uint32 [N]
     rec = vq.decode(idx, codebook)                      # gather, for checking
+    codes = vq.encode_packed(keys, codebook, channel_scale=f, code_bits=8)  # uint8 stream
 
 ``encode`` follows the encode step of VecInfer product vector quantization as
 the VeloxQuant-MLX blog post "I Wrote a Metal Kernel to Stop My Mac From
@@ -24,13 +25,15 @@ from typing import Optional
 
 import torch  # loads the HIP runtime that libvq.so binds to (same soname)
 
-__all__ = ["encode", "decode", "encode_raw", "decode_raw", "VQError", "lib", "LIB_PATH",
-           "F16", "BF16", "BAD_SLOT", "MAX_CENTROIDS", "STATUS"]
+__all__ = ["encode", "decode", "encode_packed", "packed_bytes", "encode_raw", "decode_raw",
+           "encode_packed_raw", "VQError", "lib", "LIB_PATH", "F16", "BF16", "BAD_SLOT",
+           "MAX_CENTROIDS", "MAX_HEAD_DIM", "STATUS"]
 
 F16 = 0
 BF16 = 1
 BAD_SLOT = 0xFFFFFFFF
 MAX_CENTROIDS = 65536
+MAX_HEAD_DIM = 4096
 STATUS = {0: "VQ_OK", -1: "VQ_ERR_INVALID_ARG", -2: "VQ_ERR_UNSUPPORTED",
           -3: "VQ_ERR_MISALIGNED", -4: "VQ_ERR_DEVICE"}
 
@@ -47,6 +50,9 @@ _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
 lib.vq_encode.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _p, _p]
 lib.vq_encode.restype = _i32
+lib.vq_encode_packed.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _p, _i32,
+                                 _i64, _i32, _p, _p]
+lib.vq_encode_packed.restype = _i32
 lib.vq_decode.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _p, _p]
 lib.vq_decode.restype = _i32
 lib.vq_status_str.argtypes = [_i32]
@@ -78,6 +84,18 @@ def encode_raw(x_ptr: int, codebook_ptr: int, n: int, sub_dim: int, n_centroids:
     """Direct call of ``vq_encode`` with integer pointers (raises on error)."""
     _check(lib.vq_encode(x_ptr, codebook_ptr, n, sub_dim, n_centroids, dtype, codebook_stride,
                          n_codebooks, group_len, group_map_ptr, out_ptr, stream), "vq_encode")
+
+
+def encode_packed_raw(x_ptr: int, codebook_ptr: int, n: int, sub_dim: int, n_centroids: int,
+                      dtype: int, codebook_stride: int, n_codebooks: int, group_len: int,
+                      group_map_ptr: Optional[int], scale_ptr: Optional[int], head_dim: int,
+                      scale_stride: int, code_bits: int, out_ptr: int,
+                      stream: Optional[int]) -> None:
+    """Direct call of ``vq_encode_packed`` with integer pointers (raises on error)."""
+    _check(lib.vq_encode_packed(x_ptr, codebook_ptr, n, sub_dim, n_centroids, dtype,
+                                codebook_stride, n_codebooks, group_len, group_map_ptr, scale_ptr,
+                                head_dim, scale_stride, code_bits, out_ptr, stream),
+           "vq_encode_packed")
 
 
 def decode_raw(idx_ptr: int, codebook_ptr: int, n: int, sub_dim: int, n_centroids: int,
@@ -117,6 +135,84 @@ def _stream_of(device: torch.device, stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _group_map_ptr(group_map, n: int, group_len: int) -> Optional[int]:
+    if group_map is None:
+        return None
+    if group_map.dtype != torch.int32 or not group_map.is_cuda or not group_map.is_contiguous():
+        raise ValueError("group_map must be a contiguous int32 device tensor")
+    if group_map.numel() < -(-n // group_len):
+        raise ValueError("group_map needs one entry per group")
+    return group_map.data_ptr()
+
+
+def _keys(x: torch.Tensor, codebook: torch.Tensor):
+    """(dtype code, n_codebooks, n_centroids, sub_dim, stride, n) for encode."""
+    if not (x.is_cuda and codebook.is_cuda):
+        raise ValueError("x and codebook must be device tensors (no CPU path exists)")
+    dt = _dtype_code(x.dtype)
+    if codebook.dtype != x.dtype:
+        raise TypeError("x and codebook must have the same dtype")
+    k, n_c, sd, stride = _codebook_layout(codebook)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if x.numel() % sd:
+        raise ValueError("x's element count is not a multiple of sub_dim")
+    return dt, k, n_c, sd, stride, x.numel() // sd
+
+
+def packed_bytes(n: int, code_bits: int) -> int:
+    """Length of the code stream of n codes of code_bits bits."""
+    return (n * code_bits + 7) // 8
+
+
+def encode_packed(x: torch.Tensor, codebook: torch.Tensor, *,
+                  channel_scale: Optional[torch.Tensor] = None, head_dim: Optional[int] = None,
+                  code_bits: int = 8, group_len: Optional[int] = None,
+                  group_map: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Smoothed, packed encode: a uint8 code stream of ceil(N*code_bits/8) bytes.
+
+    channel_scale  fp32 factors [head_dim] (one vector) or [slots, head_dim]
+                   (one per codebook slot); every key channel is multiplied by
+                   its factor before the search.  None: no smoothing.
+    head_dim       channels per key; defaults to the factors' last dimension,
+                   or to x's last dimension.
+    code_bits      bits per code (n_centroids <= 2^code_bits); codes are
+                   packed back to back, least significant bit first.
+    Other arguments as for ``encode``.
+    """
+    dt, k, n_c, sd, stride, n = _keys(x, codebook)
+    if group_len is None:
+        group_len = max(n, 1)
+    gptr = _group_map_ptr(group_map, n, group_len)
+    sptr, sstride = None, 0
+    if channel_scale is not None:
+        if (channel_scale.dtype != torch.float32 or not channel_scale.is_cuda
+                or channel_scale.stride(-1) != 1 or channel_scale.dim() not in (1, 2)):
+            raise ValueError("channel_scale must be a float32 device tensor [head_dim] or "
+                             "[slots, head_dim] with unit channel stride")
+        hd = channel_scale.shape[-1]
+        if head_dim is not None and head_dim != hd:
+            raise ValueError("head_dim differs from channel_scale's last dimension")
+        head_dim = hd
+        if channel_scale.dim() == 2:
+            if channel_scale.shape[0] < k:
+                raise ValueError("channel_scale needs one factor vector per codebook slot")
+            sstride = channel_scale.stride(0)
+        sptr = channel_scale.data_ptr()
+    if head_dim is None:
+        head_dim = x.shape[-1] if x.dim() > 1 else sd
+    nbytes = packed_bytes(n, code_bits)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    elif out.dtype != torch.uint8 or out.numel() < nbytes or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous uint8 tensor of at least {nbytes} bytes")
+    encode_packed_raw(x.data_ptr(), codebook.data_ptr(), n, sd, n_c, dt, stride, k, group_len,
+                      gptr, sptr, head_dim, sstride, code_bits, out.data_ptr(),
+                      _stream_of(x.device, stream))
+    return out
+
+
 def encode(x: torch.Tensor, codebook: torch.Tensor, *, group_len: Optional[int] = None,
            group_map: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
            stream=None) -> torch.Tensor:
@@ -129,26 +225,10 @@ def encode(x: torch.Tensor, codebook: torch.Tensor, *, group_len: Optional[int] 
     group_len sub-vectors per group when several codebook slots are used:
               sub-vector n uses slot group_map[n // group_len] (or n // group_len).
     """
-    if not (x.is_cuda and codebook.is_cuda):
-        raise ValueError("x and codebook must be device tensors (no CPU path exists)")
-    dt = _dtype_code(x.dtype)
-    if codebook.dtype != x.dtype:
-        raise TypeError("x and codebook must have the same dtype")
-    k, n_c, sd, stride = _codebook_layout(codebook)
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous")
-    if x.numel() % sd:
-        raise ValueError("x's element count is not a multiple of sub_dim")
-    n = x.numel() // sd
+    dt, k, n_c, sd, stride, n = _keys(x, codebook)
     if group_len is None:
         group_len = max(n, 1)
-    gptr = None
-    if group_map is not None:
-        if group_map.dtype != torch.int32 or not group_map.is_cuda or not group_map.is_contiguous():
-            raise ValueError("group_map must be a contiguous int32 device tensor")
-        if group_map.numel() < -(-n // group_len):
-            raise ValueError("group_map needs one entry per group")
-        gptr = group_map.data_ptr()
+    gptr = _group_map_ptr(group_map, n, group_len)
     if out is None:
         out = torch.empty(n, dtype=torch.uint32, device=x.device)
     elif out.dtype != torch.uint32 or out.numel() != n or not out.is_contiguous():
@@ -171,13 +251,7 @@ def decode(idx: torch.Tensor, codebook: torch.Tensor, *, group_len: Optional[int
     n = idx.numel()
     if group_len is None:
         group_len = max(n, 1)
-    gptr = None
-    if group_map is not None:
-        if group_map.dtype != torch.int32 or not group_map.is_cuda or not group_map.is_contiguous():
-            raise ValueError("group_map must be a contiguous int32 device tensor")
-        if group_map.numel() < -(-n // group_len):
-            raise ValueError("group_map needs one entry per group")
-        gptr = group_map.data_ptr()
+    gptr = _group_map_ptr(group_map, n, group_len)
     if out is None:
         out = torch.empty((n, sd), dtype=codebook.dtype, device=idx.device)
     elif out.dtype != codebook.dtype or out.numel() != n * sd or not out.is_contiguous():

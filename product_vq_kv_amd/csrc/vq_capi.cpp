@@ -14,6 +14,7 @@ namespace {
 thread_local int32_t g_last_hip_error = 0;
 
 constexpr int64_t kMaxGrid = 0x7fffffffLL;
+static_assert(VQ_MAX_HEAD_DIM == vqk::kMaxHeadDim, "factor staging limit");
 
 vq_status check_common(const void *codebook, int64_t n, int32_t sub_dim, int32_t n_centroids,
                        vq_dtype dtype, int64_t codebook_stride, int64_t n_codebooks,
@@ -50,6 +51,23 @@ vq_status device_result(hipError_t e) {
   return VQ_ERR_DEVICE;
 }
 
+// Encode launch for validated arguments with n > 0: the matrix-core kernel
+// while the codebook slot fits its LDS plan, the direct kernel beyond.
+vq_status launch(const void *x, const void *codebook, const int32_t *group_map, void *out,
+                 const vqk::Layout &l, const vqk::Codes &codes, void *stream) {
+  if (vqk::encode_grid(l) > kMaxGrid || vqk::encode_mfma_grid(l) > kMaxGrid)
+    return VQ_ERR_INVALID_ARG;
+  (void)hipGetLastError();  // drop a stale error so it is not reported as ours
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+#ifdef VQ_ENCODE_DIRECT_ONLY
+  return device_result(vqk::launch_encode(x, codebook, group_map, out, l, codes, s));
+#else
+  if (vqk::encode_mfma_supported(l))
+    return device_result(vqk::launch_encode_mfma(x, codebook, group_map, out, l, codes, s));
+  return device_result(vqk::launch_encode(x, codebook, group_map, out, l, codes, s));
+#endif
+}
+
 }  // namespace
 
 extern "C" {
@@ -66,19 +84,38 @@ vq_status vq_encode(const void *x, const void *codebook, int64_t n, int32_t sub_
   if (reinterpret_cast<uintptr_t>(x) % (2 * sub_dim) != 0) return VQ_ERR_MISALIGNED;
   if (reinterpret_cast<uintptr_t>(out_idx) % 4 != 0) return VQ_ERR_MISALIGNED;
   if (n == 0) return VQ_OK;
-  if (vqk::encode_grid(l) > kMaxGrid || vqk::encode_mfma_grid(l) > kMaxGrid)
-    return VQ_ERR_INVALID_ARG;
-  (void)hipGetLastError();  // drop a stale error so it is not reported as ours
-#ifdef VQ_ENCODE_DIRECT_ONLY
-  return device_result(
-      vqk::launch_encode(x, codebook, group_map, out_idx, l, static_cast<hipStream_t>(stream)));
-#else
-  if (vqk::encode_mfma_supported(l))
-    return device_result(vqk::launch_encode_mfma(x, codebook, group_map, out_idx, l,
-                                                 static_cast<hipStream_t>(stream)));
-  return device_result(
-      vqk::launch_encode(x, codebook, group_map, out_idx, l, static_cast<hipStream_t>(stream)));
-#endif
+  return launch(x, codebook, group_map, out_idx, l, vqk::plain_codes(l), stream);
+}
+
+vq_status vq_encode_packed(const void *x, const void *codebook, int64_t n, int32_t sub_dim,
+                           int32_t n_centroids, vq_dtype dtype, int64_t codebook_stride,
+                           int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
+                           const float *channel_scale, int32_t head_dim, int64_t scale_stride,
+                           int32_t code_bits, void *out_codes, void *stream) {
+  vqk::Layout l;
+  vq_status st = check_common(codebook, n, sub_dim, n_centroids, dtype, codebook_stride,
+                              n_codebooks, group_len, group_map, &l);
+  if (st != VQ_OK) return st;
+  if (code_bits < 1 || code_bits > 32) return VQ_ERR_INVALID_ARG;
+  if (code_bits < 32 && n_centroids > (1 << code_bits)) return VQ_ERR_INVALID_ARG;
+  if (channel_scale) {
+    if (head_dim < sub_dim || head_dim % sub_dim != 0 || head_dim > VQ_MAX_HEAD_DIM)
+      return VQ_ERR_INVALID_ARG;
+    if (scale_stride < 0) return VQ_ERR_INVALID_ARG;
+    if (n_codebooks > 1 && scale_stride > (INT64_MAX - head_dim) / (n_codebooks - 1))
+      return VQ_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(channel_scale) % 4 != 0) return VQ_ERR_MISALIGNED;
+  }
+  if (n > 0 && (!x || !out_codes)) return VQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(x) % (2 * sub_dim) != 0) return VQ_ERR_MISALIGNED;
+  if (reinterpret_cast<uintptr_t>(out_codes) % 4 != 0) return VQ_ERR_MISALIGNED;
+  // a group boundary inside a 32-bit word of the stream would be written by
+  // two workgroups
+  if (l.n_groups > 1 && ((group_len % 32) * code_bits) % 32 != 0) return VQ_ERR_UNSUPPORTED;
+  if (n == 0) return VQ_OK;
+  const vqk::Codes codes{channel_scale, channel_scale ? scale_stride : 0,
+                         channel_scale ? head_dim : sub_dim, code_bits};
+  return launch(x, codebook, group_map, out_codes, l, codes, stream);
 }
 
 vq_status vq_decode(const uint32_t *idx, const void *codebook, int64_t n, int32_t sub_dim,
@@ -103,7 +140,8 @@ const char *vq_status_str(int32_t status) {
   switch (status) {
     case VQ_OK: return "ok";
     case VQ_ERR_INVALID_ARG: return "invalid argument";
-    case VQ_ERR_UNSUPPORTED: return "unsupported sub_dim, dtype or n_centroids";
+    case VQ_ERR_UNSUPPORTED:
+      return "unsupported sub_dim, dtype, n_centroids or packed group layout";
     case VQ_ERR_MISALIGNED: return "misaligned pointer";
     case VQ_ERR_DEVICE: return "HIP launch failed";
     default: return "unknown status";

@@ -25,10 +25,14 @@
 //     the minimum strictly decreased.  That group holds the first occurrence
 //     of the minimum; it is recomputed from LDS with the identical instruction
 //     sequence (so the same bits) and the lowest index whose distance equals
-//     the minimum is the answer -- exactly the strict-< scan's result.
+//     the minimum is the answer -- exactly the strict-< scan's result;
+//   * smoothed keys (SCALED): each component is multiplied by its channel's
+//     fp32 factor (staged in LDS per slot) right after widening, and the
+//     search runs on those fp32 values with the same instruction sequence.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "vq_codes.h"
 #include "vq_launch.h"
 
 namespace vqk {
@@ -93,14 +97,16 @@ __device__ __forceinline__ void load_x(const uint16_t *__restrict__ x, int64_t r
   }
 }
 
-template <int SD, int S, bool BF16>
+template <int SD, int S, bool BF16, bool SCALED>
 __global__ void __launch_bounds__(kBlock)
 encode_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ codebook,
               int64_t n, int n_c, int64_t cb_stride, int64_t n_codebooks, int64_t group_len,
               uint32_t tiles_per_group, const int32_t *__restrict__ group_map,
-              uint32_t *__restrict__ out, int chunk) {
+              uint8_t *__restrict__ out, int chunk, const float *__restrict__ scale,
+              int64_t scale_stride, int head_dim, int code_bits) {
   extern __shared__ float4 lds4[];
   float *lds = reinterpret_cast<float *>(lds4);
+  float *lds_scale = lds + chunk * SD;  // smoothed keys: the slot's factors
   constexpr int kTile = kBlock * S;
 
   const uint32_t b = blockIdx.x;
@@ -111,14 +117,12 @@ encode_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ codeb
   const int64_t tbase = gstart + static_cast<int64_t>(t) * kTile;
   if (tbase >= gend) return;  // whole workgroup: tile past its group's end
   const int tid = threadIdx.x;
+  const int64_t half0 = tbase + (tid & ~31);  // first row of this lane's half-wave
 
   const int64_t slot = group_map ? static_cast<int64_t>(group_map[g]) : static_cast<int64_t>(g);
   if (slot < 0 || slot >= n_codebooks) {
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int64_t row = tbase + s * kBlock + tid;
-      if (row < gend) out[row] = 0xFFFFFFFFu;
-    }
+    for (int s = 0; s < S; ++s) store_codes32(0xFFFFFFFFu, half0 + s * kBlock, gend, code_bits, true, out);
     return;  // whole workgroup
   }
   const uint16_t *__restrict__ cb = codebook + slot * cb_stride;
@@ -132,6 +136,20 @@ encode_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ codeb
     } else {
 #pragma unroll
       for (int i = 0; i < SD; ++i) xv[s][i] = 0.0f;
+    }
+  }
+  if constexpr (SCALED) {
+    const float *__restrict__ f = scale + slot * scale_stride;
+    for (int i = tid; i < head_dim; i += kBlock) lds_scale[i] = f[i];
+    __syncthreads();
+    const int n_sub = head_dim / SD;
+    const float inv_n_sub = 1.0f / static_cast<float>(n_sub);
+    const int tmod = static_cast<int>(tbase % n_sub);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int m = mod_small(tmod + s * kBlock + tid, n_sub, inv_n_sub);
+#pragma unroll
+      for (int i = 0; i < SD; ++i) xv[s][i] = xv[s][i] * lds_scale[m * SD + i];
     }
   }
 
@@ -200,18 +218,15 @@ encode_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ codeb
   }
 
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int64_t row = tbase + s * kBlock + tid;
-    if (row < gend) out[row] = res[s];
-  }
+  for (int s = 0; s < S; ++s) store_codes32(res[s], half0 + s * kBlock, gend, code_bits, true, out);
 }
 
 template <int SD>
 constexpr int sub_vectors_per_lane() { return 4; }
 
-template <int SD, bool BF16>
-hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_map,
-                    uint32_t *out, const Layout &l, hipStream_t stream) {
+template <int SD, bool BF16, bool SCALED>
+hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_map, void *out,
+                    const Layout &l, const Codes &codes, hipStream_t stream) {
   constexpr int S = sub_vectors_per_lane<SD>();
   constexpr int kTile = kBlock * S;
   const int64_t span = l.group_len < l.n ? l.group_len : l.n;
@@ -219,13 +234,23 @@ hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_ma
   const int64_t grid = tiles_per_group * l.n_groups;
   const int chunk_raw = l.n_centroids < kChunkMax ? l.n_centroids : kChunkMax;
   const int chunk = (chunk_raw + kGroup - 1) / kGroup * kGroup;
-  const size_t lds_bytes = static_cast<size_t>(chunk) * SD * sizeof(float);
-  hipLaunchKernelGGL((encode_kernel<SD, S, BF16>), dim3(static_cast<uint32_t>(grid)),
+  const size_t lds_bytes =
+      (static_cast<size_t>(chunk) * SD + (SCALED ? codes.head_dim : 0)) * sizeof(float);
+  hipLaunchKernelGGL((encode_kernel<SD, S, BF16, SCALED>), dim3(static_cast<uint32_t>(grid)),
                      dim3(kBlock), lds_bytes, stream,
                      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(codebook),
                      l.n, l.n_centroids, l.codebook_stride, l.n_codebooks, l.group_len,
-                     static_cast<uint32_t>(tiles_per_group), group_map, out, chunk);
+                     static_cast<uint32_t>(tiles_per_group), group_map,
+                     static_cast<uint8_t *>(out), chunk, codes.scale, codes.scale_stride,
+                     codes.head_dim, codes.code_bits);
   return hipGetLastError();
+}
+
+template <int SD, bool BF16>
+hipError_t launch_scaled(const void *x, const void *codebook, const int32_t *group_map, void *out,
+                         const Layout &l, const Codes &codes, hipStream_t stream) {
+  return codes.scale ? launch_t<SD, BF16, true>(x, codebook, group_map, out, l, codes, stream)
+                     : launch_t<SD, BF16, false>(x, codebook, group_map, out, l, codes, stream);
 }
 
 }  // namespace
@@ -238,13 +263,13 @@ int64_t encode_grid(const Layout &l) {
 }
 
 hipError_t launch_encode(const void *x, const void *codebook, const int32_t *group_map,
-                         uint32_t *out_idx, const Layout &l, hipStream_t stream) {
+                         void *out, const Layout &l, const Codes &codes, hipStream_t stream) {
   if (l.sub_dim == 4) {
-    return l.bf16 ? launch_t<4, true>(x, codebook, group_map, out_idx, l, stream)
-                  : launch_t<4, false>(x, codebook, group_map, out_idx, l, stream);
+    return l.bf16 ? launch_scaled<4, true>(x, codebook, group_map, out, l, codes, stream)
+                  : launch_scaled<4, false>(x, codebook, group_map, out, l, codes, stream);
   }
-  return l.bf16 ? launch_t<8, true>(x, codebook, group_map, out_idx, l, stream)
-                : launch_t<8, false>(x, codebook, group_map, out_idx, l, stream);
+  return l.bf16 ? launch_scaled<8, true>(x, codebook, group_map, out, l, codes, stream)
+                : launch_scaled<8, false>(x, codebook, group_map, out, l, codes, stream);
 }
 
 }  // namespace vqk

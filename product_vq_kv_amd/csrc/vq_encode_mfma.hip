@@ -34,18 +34,33 @@
 //   fp32 distance and can never win the strict-< scan; such rows are found
 //   with an LDS hash table per workgroup and excluded from stage 1 (C = +inf),
 //   so they do not make every nearby sub-vector ambiguous.
+// Smoothed keys (SCALED): the search runs on x~ = x * f (fp32, per-channel
+//   factors f).  x~ is not an fp16/bf16 value, so stage 1 splits it exactly
+//   as x~ = hi + lo + e with hi = rn(x~), lo = rn(x~ - hi) in the element
+//   type (both subtractions are exact) and multiplies [hi, lo] by [-c, -c]:
+//   2 sub_dim products, which fill the K = 8 slots at sub_dim 4 and take the
+//   K = 16 instruction (same issue cost) at sub_dim 8.  The bound uses
+//   eta for 2 sub_dim + 1 terms and |x| replaced by |(|hi| + |lo|)|, and the
+//   residual adds |e . c| <= max|c| sum|e_i|.  Stage 2 recomputes x~ in fp32
+//   and is unchanged.  (Measured on gfx950 for both instruction shapes: the
+//   accumulation error stays below 4 u sum|terms| plus a fraction of the
+//   smallest subnormal.)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
+#include "vq_codes.h"
 #include "vq_launch.h"
 
 namespace vqk {
 namespace {
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMfmaMaxCentroids = 4096;    // whole codebook slot resident in LDS
@@ -55,14 +70,24 @@ constexpr float kTau = 7.174648137343064e-43f;      // 2^-140: absolute slack
 constexpr float kNormCap = 1.2676506002282294e30f;  // 2^100: beyond it, exact path
 constexpr float kNormUp = 1.0000038146972656f;      // 1 + 2^-18: upward norm margin
 constexpr float kNegMax = -3.4028234663852886e38f;  // med3(a, b, kNegMax) = min(a, b)
+constexpr float kFltMax = 3.4028234663852886e38f;
+constexpr float kBnUp = 1.0000019073486328f;        // 1 + 2^-19
 
-template <int SD>
+// SD: sub-vector length; NT: products per matrix-core dot (SD, or 2 SD for
+// the hi/lo split of smoothed keys).
+template <int SD, int NT>
 struct Consts {
-  static constexpr float kEta = (2.0f * (SD + 2) + 2.0f) * kU;  // eta_m + 2u (final fma)
+  static constexpr float kEta = (2.0f * (NT + 2) + 2.0f) * kU;  // eta_m + 2u (final fma)
   static constexpr float kKappa = 1.125f * kEta;                // > eta / (1 - u)
+  static constexpr float kInvKappaUp = (1.0f / kKappa) * 1.0000152587890625f;  // >= 1/kappa
   static constexpr float kHalfShrink = 0.5f * (1.0f - kEta - 9.5367431640625e-07f);
   static constexpr float kGamma2 = 2.0f * (SD + 2) * kU * 1.01f;  // >= 1/(1-gamma) - 1
 };
+
+// Matrix-core operands: 4 halves per lane (K = 8), or 8 (K = 16) for the
+// smoothed sub_dim 8 path.
+template <int SD, bool SCALED>
+using Op = std::conditional_t<(SD == 8 && SCALED), uint4, uint2>;
 
 template <bool BF16>
 __device__ __forceinline__ float widen(uint16_t v) {
@@ -70,6 +95,17 @@ __device__ __forceinline__ float widen(uint16_t v) {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);
   } else {
     return static_cast<float>(__builtin_bit_cast(_Float16, v));
+  }
+}
+
+// fp32 -> element bits, rounded to nearest even (overflow gives +-inf).
+template <bool BF16>
+__device__ __forceinline__ uint16_t narrow(float v) {
+  if constexpr (BF16) {
+    const uint32_t u = __float_as_uint(v);
+    return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  } else {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
   }
 }
 
@@ -126,6 +162,17 @@ __device__ __forceinline__ f32x16 mfma(const uint2 &a, const uint2 &b, const f32
   }
 }
 
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma(const uint4 &a, const uint4 &b, const f32x16 &c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
 // Minimum of the 16 values (finite or +inf).  The first step is a med3 with
 // -FLT_MAX, which equals min for such values and needs no NaN quieting.
 __device__ __forceinline__ float min16(const f32x16 &v) {
@@ -147,7 +194,9 @@ __device__ __forceinline__ float min16(const f32x16 &v) {
 //                           duplicate rows;
 //   gan  [n_cpad/16] float  per 16-row group: kappa max |c| (rounded up);
 //   c32  [n_cpad][SD] float the centroids in fp32 (ROWS32 only);
-//   hash [hash_slots] int   duplicate detection while staging.
+//   hash [hash_slots] int   duplicate detection while staging;
+//   scale [head_dim] float  the slot's channel factors (smoothed keys only).
+// gan is padded to a multiple of 4 floats so every region is 16-byte aligned.
 template <int SD, bool ROWS32>
 struct Lds {
   uint4 *rows;
@@ -155,16 +204,20 @@ struct Lds {
   float *gan;
   float *c32;
   int *hash;
-  __device__ Lds(uint4 *base, int n_cpad) {
+  float *scale;
+  static constexpr int gan_len(int n_cpad) { return (n_cpad / 16 + 3) & ~3; }
+  __device__ Lds(uint4 *base, int n_cpad, int hash_slots) {
     rows = base;
     cval = reinterpret_cast<float *>(rows + n_cpad);
     gan = cval + n_cpad;
-    c32 = gan + n_cpad / 16;
+    c32 = gan + gan_len(n_cpad);
     hash = reinterpret_cast<int *>(c32 + (ROWS32 ? n_cpad * SD : 0));
+    scale = reinterpret_cast<float *>(hash + hash_slots);
   }
-  static size_t bytes(int n_cpad, int hash_slots) {
+  static size_t bytes(int n_cpad, int hash_slots, int scale_len) {
     return static_cast<size_t>(n_cpad) * (16 + 4 + (ROWS32 ? 4 * SD : 0)) +
-           static_cast<size_t>(n_cpad / 16) * 4 + static_cast<size_t>(hash_slots) * 4;
+           static_cast<size_t>(gan_len(n_cpad)) * 4 + static_cast<size_t>(hash_slots) * 4 +
+           static_cast<size_t>(scale_len) * 4;
   }
 };
 
@@ -190,15 +243,18 @@ __device__ __forceinline__ void centroid(const Lds<SD, ROWS32> &s, int c, float 
   }
 }
 
-// Stage one codebook slot.  Returns true when some centroid has a non-finite
-// or huge norm: then every sub-vector of the slot takes the full exact scan.
-template <int SD, bool BF16, bool ROWS32, int BLOCK>
+// Stage one codebook slot (and, for smoothed keys, its channel factors).
+// Returns true when some centroid has a non-finite or huge norm: then every
+// sub-vector of the slot takes the full exact scan.
+template <int SD, int NT, bool BF16, bool ROWS32, int BLOCK>
 __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_cpad,
-                               const Lds<SD, ROWS32> &s, int hash_slots) {
-  using K = Consts<SD>;
+                               const Lds<SD, ROWS32> &s, int hash_slots,
+                               const float *__restrict__ scale, int scale_len) {
+  using K = Consts<SD, NT>;
   const int tid = threadIdx.x;
   for (int i = tid; i < hash_slots; i += BLOCK) s.hash[i] = -1;
   for (int i = tid; i < n_cpad / 16; i += BLOCK) s.gan[i] = 0.0f;
+  for (int i = tid; i < scale_len; i += BLOCK) s.scale[i] = scale ? scale[i] : 1.0f;
   __syncthreads();
   int flag = 0;
   for (int r = tid; r < n_cpad; r += BLOCK) {
@@ -327,23 +383,51 @@ __device__ __forceinline__ void column_x(const uint2 &own, int h, float (&xv)[SD
   widen_words<SD, BF16>(w, 0, xv);
 }
 
+// Channel factors of sub-slot m (channels m*SD .. m*SD + SD - 1).
+template <int SD, bool ROWS32>
+__device__ __forceinline__ void factors(const Lds<SD, ROWS32> &s, int m, float (&f)[SD]) {
+#pragma unroll
+  for (int q = 0; q < SD / 4; ++q) {
+    const float4 w = *reinterpret_cast<const float4 *>(s.scale + m * SD + 4 * q);
+    f[4 * q] = w.x;
+    f[4 * q + 1] = w.y;
+    f[4 * q + 2] = w.z;
+    f[4 * q + 3] = w.w;
+  }
+}
+
+// Channel layout of smoothed keys: row r is sub-slot r mod n_sub of its key.
+struct Smooth {
+  int n_sub;
+  float inv_n_sub;
+};
+
 // One tile: every wave encodes T columns of 32 sub-vectors.
-template <int SD, int T, int BLOCK, bool BF16, bool ROWS32>
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
 __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64_t gend, int n_c,
                             int n_cpad, const Lds<SD, ROWS32> &s, bool exact_tile,
-                            uint32_t *__restrict__ out) {
-  using K = Consts<SD>;
+                            const Smooth sm, int code_bits, uint8_t *__restrict__ out) {
+  using K = Consts<SD, SCALED ? 2 * SD : SD>;
+  using OpT = Op<SD, SCALED>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;  // half of the block's rows / K slots this lane holds
   const int col = lane & 31;
   const int nblk = n_cpad / 32;
 
-  uint2 bop[T];  // this lane's K slots 4h..4h+3 of its column
-  float bn[T];   // upper bound of |x|
-  float nx2[T];  // fp32 |x|^2 as the exact stage computes it
+  OpT bop[T];    // this lane's K slots of its column
+  uint2 xw[T];   // smoothed keys: the raw words stage 2 rebuilds x~ from
+  float bn[T];   // upper bound of |x| (plus the split residual when smoothed)
+  float nx2[T];  // plain keys: fp32 |x|^2 as the exact stage computes it
   float m1[T], m2[T];
   int g1[T];
+  uint32_t codes[T];
+  int m0 = 0;    // smoothed keys: sub-slot of this lane's column 0
+  if constexpr (SCALED) {
+    const int64_t first = tbase + wave * T * 32 + col;
+    m0 = mod_small(static_cast<int>(tbase % sm.n_sub) + static_cast<int>(first - tbase), sm.n_sub,
+                   sm.inv_n_sub);
+  }
   uint32_t full_bits = 0;  // bit t: column t takes the full exact scan
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -362,26 +446,103 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
         w[3] = q.w;
       }
     }
-    float xv[SD];
-    widen_words<SD, BF16>(w, 0, xv);
-    float n2x = xv[0] * xv[0];
+    if constexpr (SCALED) {
+      // the pair splits the components: lane h smooths and splits components
+      // h*E .. h*E + E - 1 (x~ = hi + lo + e exactly), then each lane trades
+      // the half of the other operand for the half it lacks: h = 0 builds the
+      // hi operand, h = 1 the lo operand
+      constexpr int E = SD / 2;
+      const int m = mod_small(m0 + 32 * t, sm.n_sub, sm.inv_n_sub);
+      // this lane's E components: words 0 .. E/2-1 (h = 0) or E/2 .. E-1
+      // (a mask select: a select between array elements becomes an indexed
+      // load from private memory)
+      const uint32_t upper = 0u - static_cast<uint32_t>(h);
+      uint32_t ow[E / 2];
 #pragma unroll
-    for (int i = 1; i < SD; ++i) n2x = __builtin_fmaf(xv[i], xv[i], n2x);
-    nx2[t] = n2x;
-    const bool ex = !(n2x <= kNormCap) || exact_tile;
-    full_bits |= (ex ? 1u : 0u) << t;
-    bn[t] = ex ? 0.0f : __builtin_sqrtf(n2x) * kNormUp;
-    if constexpr (SD == 4) {
-      bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(0, 0);
+      for (int q = 0; q < E / 2; ++q) ow[q] = (w[q] & ~upper) | (w[E / 2 + q] & upper);
+      float xo[E], f[E];
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        xo[i] = widen<BF16>(half_of(ow, i));
+        f[i] = s.scale[m * SD + h * E + i];
+      }
+      uint32_t hw[E / 2], lw[E / 2];
+      float nv2 = 0.0f, esum = 0.0f;
+      bool fin = true;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const float xt = xo[i] * f[i];
+        const uint16_t hb = narrow<BF16>(xt);
+        const float hf = widen<BF16>(hb);
+        const float r = xt - hf;
+        const uint16_t lb = narrow<BF16>(r);
+        const float lf = widen<BF16>(lb);
+        esum += __builtin_fabsf(r - lf);
+        const float v = __builtin_fabsf(hf) + __builtin_fabsf(lf);
+        nv2 = __builtin_fmaf(v, v, nv2);
+        fin = fin && (__builtin_fabsf(hf) <= kFltMax);
+        if (i & 1) {
+          hw[i >> 1] |= static_cast<uint32_t>(hb) << 16;
+          lw[i >> 1] |= static_cast<uint32_t>(lb) << 16;
+        } else {
+          hw[i >> 1] = hb;
+          lw[i >> 1] = lb;
+        }
+      }
+      uint32_t keep[E / 2], got[E / 2];
+#pragma unroll
+      for (int q = 0; q < E / 2; ++q) {
+        keep[q] = (h == 0) ? hw[q] : lw[q];
+        got[q] = static_cast<uint32_t>(__shfl_xor(static_cast<int>((h == 0) ? lw[q] : hw[q]), 32));
+      }
+      nv2 = nv2 + __shfl_xor(nv2, 32);
+      esum = esum + __shfl_xor(esum, 32);
+      fin = fin && (__shfl_xor(fin ? 1 : 0, 32) != 0);
+      const bool ex = !fin || !(nv2 <= kNormCap) || exact_tile;
+      full_bits |= (ex ? 1u : 0u) << t;
+      bn[t] = ex ? 0.0f
+                 : __builtin_fmaf(esum, K::kInvKappaUp, __builtin_sqrtf(nv2) * kNormUp) * kBnUp;
+      // components 0 .. E-1 come from lane h = 0, E .. SD-1 from lane h = 1
+      if constexpr (SD == 4) {
+        bop[t] = (h == 0) ? make_uint2(keep[0], got[0]) : make_uint2(got[0], keep[0]);
+        xw[t] = make_uint2(w[0], w[1]);
+      } else {
+        bop[t] = (h == 0) ? make_uint4(keep[0], keep[1], got[0], got[1])
+                          : make_uint4(got[0], got[1], keep[0], keep[1]);
+        xw[t] = make_uint2((w[0] & ~upper) | (w[2] & upper), (w[1] & ~upper) | (w[3] & upper));
+      }
     } else {
-      bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(w[2], w[3]);
+      float xv[SD];
+      widen_words<SD, BF16>(w, 0, xv);
+      float n2x = xv[0] * xv[0];
+#pragma unroll
+      for (int i = 1; i < SD; ++i) n2x = __builtin_fmaf(xv[i], xv[i], n2x);
+      nx2[t] = n2x;
+      const bool ex = !(n2x <= kNormCap) || exact_tile;
+      full_bits |= (ex ? 1u : 0u) << t;
+      bn[t] = ex ? 0.0f : __builtin_sqrtf(n2x) * kNormUp;
+      if constexpr (SD == 4) {
+        bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(0, 0);
+      } else {
+        bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(w[2], w[3]);
+      }
     }
     m1[t] = __builtin_inff();
     m2[t] = __builtin_inff();
     g1[t] = 0;
   }
 
-  const uint2 *arow = reinterpret_cast<const uint2 *>(s.rows) + 2 * col + h;
+  // A operand of block blk: -c for this lane's row; the plain form holds
+  // the lane's half of the K slots, the smoothed form -c in both halves
+  auto a_operand = [&](int blk) -> OpT {
+    if constexpr (SCALED && SD == 8) {
+      return s.rows[blk * 32 + col];
+    } else if constexpr (SCALED) {
+      return reinterpret_cast<const uint2 *>(s.rows)[blk * 64 + 2 * col];
+    } else {
+      return reinterpret_cast<const uint2 *>(s.rows)[blk * 64 + 2 * col + h];
+    }
+  };
   auto c_operand = [&](int blk) {
     f32x16 cop;
 #pragma unroll
@@ -398,7 +559,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
   // ---- stage 1: group lower bounds on the matrix cores ---------------------
   if (!exact_tile) {
     for (int blk = 0; blk < nblk; ++blk) {
-      const uint2 aop = arow[blk * 64];
+      const OpT aop = a_operand(blk);
       const f32x16 cop = c_operand(blk);
       const float an = s.gan[2 * blk + h];
       const int grp = 2 * blk + h;
@@ -417,7 +578,20 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     float xv[SD];
-    column_x<SD, BF16>(bop[t], h, xv);
+    if constexpr (SCALED) {
+      if constexpr (SD == 4) {
+        const uint32_t w[4] = {xw[t].x, xw[t].y, 0, 0};
+        widen_words<SD, BF16>(w, 0, xv);
+      } else {
+        column_x<SD, BF16>(xw[t], h, xv);
+      }
+      float f[SD];
+      factors<SD, ROWS32>(s, mod_small(m0 + 32 * t, sm.n_sub, sm.inv_n_sub), f);
+#pragma unroll
+      for (int i = 0; i < SD; ++i) xv[i] = xv[i] * f[i];
+    } else {
+      column_x<SD, BF16>(bop[t], h, xv);
+    }
     const float om1 = __shfl_xor(m1[t], 32);
     const float om2 = __shfl_xor(m2[t], 32);
     const int og1 = __shfl_xor(g1[t], 32);
@@ -438,7 +612,15 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
       exact4<SD, BF16, ROWS32, false>(s, xv, c0 + 8, n_c, best, bi);
     }
     pair_min(best, bi);
-    const float xl = nx2[t] * (1.0f - (SD + 2) * kU);
+    float n2x;
+    if constexpr (SCALED) {
+      n2x = xv[0] * xv[0];
+#pragma unroll
+      for (int i = 1; i < SD; ++i) n2x = __builtin_fmaf(xv[i], xv[i], n2x);
+    } else {
+      n2x = nx2[t];
+    }
+    const float xl = n2x * (1.0f - (SD + 2) * kU);
     // s(c*) <= (best (1 + 2 gamma) - |x|^2) / 2; the two rounded operations
     // below are covered by (best + xl) 2u, kTau covers subnormal steps.
     float U = (best * (1.0f + K::kGamma2) - xl) * 0.5f;
@@ -452,7 +634,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
       float fb = __builtin_inff();
       int fi = 0x7fffffff;
       for (int blk = 0; blk < nblk; ++blk) {
-        const uint2 aop = arow[blk * 64];
+        const OpT aop = a_operand(blk);
         const f32x16 cop = c_operand(blk);
         const float an = s.gan[2 * blk + h];
         const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
@@ -485,24 +667,57 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
       best = full ? fb : best;
       bi = full ? fi : bi;
     }
-    const int64_t row = tbase + (wave * T + t) * 32 + col;
-    if (row < gend && h == 0) out[row] = (bi == 0x7fffffff) ? 0u : static_cast<uint32_t>(bi);
+    codes[t] = (bi == 0x7fffffff) ? 0u : static_cast<uint32_t>(bi);
+  }
+
+  // ---- store: outside the column loop, one width branch ---------------------
+  if constexpr (SCALED) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      store_codes32(codes[t], tbase + (wave * T + t) * 32, gend, code_bits, h == 0, out);
+  } else if (h == 0) {
+    const int64_t row0 = tbase + wave * T * 32 + col;
+    if (code_bits == 32) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        if (row0 + 32 * t < gend) reinterpret_cast<uint32_t *>(out)[row0 + 32 * t] = codes[t];
+    } else if (code_bits == 16) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        if (row0 + 32 * t < gend)
+          reinterpret_cast<uint16_t *>(out)[row0 + 32 * t] = static_cast<uint16_t>(codes[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        if (row0 + 32 * t < gend) out[row0 + 32 * t] = static_cast<uint8_t>(codes[t]);
+    }
   }
 }
 
 // Persistent workgroups: workgroup w encodes tiles [w*k, (w+1)*k) of the
 // group-major tile sequence and stages a codebook slot only when it changes.
-template <int SD, int T, int BLOCK, bool BF16, bool ROWS32>
-__global__ void __launch_bounds__(BLOCK)
+// At least 4 waves per SIMD (at most 128 VGPRs): the matrix-core stream and
+// the VALU stream of different waves overlap only with that many.
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
+__global__ void __launch_bounds__(BLOCK, 4)
 encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ codebook,
                    int64_t n, int n_c, int64_t cb_stride, int64_t n_codebooks, int64_t group_len,
                    int64_t tiles_per_group, int64_t total_tiles, int64_t tiles_per_wg,
-                   const int32_t *__restrict__ group_map, uint32_t *__restrict__ out,
-                   int hash_slots) {
+                   const int32_t *__restrict__ group_map, uint8_t *__restrict__ out,
+                   int hash_slots, const float *__restrict__ scale, int64_t scale_stride,
+                   int head_dim, int code_bits) {
   constexpr int kTile = (BLOCK / 64) * T * 32;
   extern __shared__ uint4 lds_raw[];
   const int n_cpad = (n_c + 31) & ~31;
-  const Lds<SD, ROWS32> s(lds_raw, n_cpad);
+  const Lds<SD, ROWS32> s(lds_raw, n_cpad, hash_slots);
+  const int scale_len = SCALED ? head_dim : 0;
+  Smooth sm{1, 1.0f};
+  if constexpr (SCALED) {
+    sm.n_sub = head_dim / SD;
+    sm.inv_n_sub = 1.0f / static_cast<float>(sm.n_sub);
+  }
+  const int wave = threadIdx.x >> 6;
+  const int h = (threadIdx.x >> 5) & 1;
 
   const int64_t first = static_cast<int64_t>(blockIdx.x) * tiles_per_wg;
   const int64_t last = min(first + tiles_per_wg, total_tiles);
@@ -516,26 +731,36 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     if (tbase >= gend) continue;  // uniform: tile past a short group's end
     const int64_t slot = group_map ? static_cast<int64_t>(group_map[g]) : g;
     if (slot < 0 || slot >= n_codebooks) {
-      for (int64_t r = tbase + threadIdx.x; r < min(tbase + kTile, gend); r += BLOCK)
-        out[r] = 0xFFFFFFFFu;
+      if constexpr (SCALED) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          store_codes32(0xFFFFFFFFu, tbase + (wave * T + t) * 32, gend, code_bits, h == 0, out);
+      } else {
+        // all-one codes of 1, 2 or 4 bytes: every byte of the range is 0xFF
+        const int64_t bpc = code_bits / 8;
+        const int64_t bend = min(tbase + kTile, gend) * bpc;
+        for (int64_t b = tbase * bpc + threadIdx.x; b < bend; b += BLOCK) out[b] = 0xFFu;
+      }
       continue;  // uniform
     }
     if (slot != staged) {
       __syncthreads();  // every wave is done with the previous slot
-      exact_tile = stage_codebook<SD, BF16, ROWS32, BLOCK>(codebook + slot * cb_stride, n_c,
-                                                           n_cpad, s, hash_slots);
+      exact_tile = stage_codebook<SD, SCALED ? 2 * SD : SD, BF16, ROWS32, BLOCK>(
+          codebook + slot * cb_stride, n_c, n_cpad, s, hash_slots,
+          (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len);
       staged = slot;
     }
-    encode_tile<SD, T, BLOCK, BF16, ROWS32>(x, tbase, gend, n_c, n_cpad, s, exact_tile, out);
+    encode_tile<SD, T, BLOCK, BF16, ROWS32, SCALED>(x, tbase, gend, n_c, n_cpad, s, exact_tile,
+                                                    sm, code_bits, out);
   }
 }
 
 template <int BLOCK>
 constexpr int tile_of(int T) { return (BLOCK / 64) * T * 32; }
 
-template <int SD, int T, int BLOCK, bool BF16, bool ROWS32>
-hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_map, uint32_t *out,
-                    const Layout &l, hipStream_t stream, int64_t cus) {
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
+hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_map, void *out,
+                    const Layout &l, const Codes &codes, hipStream_t stream, int64_t cus) {
   constexpr int kTile = tile_of<BLOCK>(T);
   const int64_t span = l.group_len < l.n ? l.group_len : l.n;
   const int64_t tiles_per_group = (span + kTile - 1) / kTile;
@@ -543,8 +768,8 @@ hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_ma
   const int n_cpad = (l.n_centroids + 31) & ~31;
   int hash_slots = 64;
   while (hash_slots < 2 * l.n_centroids) hash_slots <<= 1;
-  const size_t lds = Lds<SD, ROWS32>::bytes(n_cpad, hash_slots);
-  auto kern = encode_mfma_kernel<SD, T, BLOCK, BF16, ROWS32>;
+  const size_t lds = Lds<SD, ROWS32>::bytes(n_cpad, hash_slots, SCALED ? codes.head_dim : 0);
+  auto kern = encode_mfma_kernel<SD, T, BLOCK, BF16, ROWS32, SCALED>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -561,7 +786,9 @@ hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_ma
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(BLOCK), lds, stream,
                      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(codebook),
                      l.n, l.n_centroids, l.codebook_stride, l.n_codebooks, l.group_len,
-                     tiles_per_group, total_tiles, tiles_per_wg, group_map, out, hash_slots);
+                     tiles_per_group, total_tiles, tiles_per_wg, group_map,
+                     static_cast<uint8_t *>(out), hash_slots, codes.scale, codes.scale_stride,
+                     codes.head_dim, codes.code_bits);
   return hipGetLastError();
 }
 
@@ -577,13 +804,32 @@ int cu_count() {
   return cus;
 }
 
-template <int SD, bool BF16>
-hipError_t launch_sd(const void *x, const void *codebook, const int32_t *group_map, uint32_t *out,
-                     const Layout &l, hipStream_t stream) {
+// Columns per wave: the smoothed sub_dim 8 form holds twice the operand
+// registers per column.
+template <int SD, bool SCALED, bool ROWS32>
+constexpr int columns() { return (SCALED && SD == 8) ? 2 : 4; }
+
+template <int SD, bool BF16, bool SCALED>
+hipError_t launch_sd(const void *x, const void *codebook, const int32_t *group_map, void *out,
+                     const Layout &l, const Codes &codes, hipStream_t stream) {
   const int64_t cus = cu_count();
   if (l.n_centroids > kRows32MaxCentroids)
-    return launch_t<SD, 4, 1024, BF16, false>(x, codebook, group_map, out, l, stream, cus);
-  return launch_t<SD, 4, 256, BF16, true>(x, codebook, group_map, out, l, stream, cus);
+    return launch_t<SD, columns<SD, SCALED, false>(), 1024, BF16, false, SCALED>(
+        x, codebook, group_map, out, l, codes, stream, cus);
+  return launch_t<SD, columns<SD, SCALED, true>(), 256, BF16, true, SCALED>(
+      x, codebook, group_map, out, l, codes, stream, cus);
+}
+
+// The plain kernel handles unsmoothed keys with 8, 16 or 32-bit codes (one
+// store per sub-vector); factors, or other code widths, take the fused
+// kernel, which stages unit factors when none are given.
+template <int SD, bool BF16>
+hipError_t launch_scaled(const void *x, const void *codebook, const int32_t *group_map, void *out,
+                         const Layout &l, const Codes &codes, hipStream_t stream) {
+  const int b = codes.code_bits;
+  const bool fused = codes.scale != nullptr || (b != 8 && b != 16 && b != 32);
+  return fused ? launch_sd<SD, BF16, true>(x, codebook, group_map, out, l, codes, stream)
+               : launch_sd<SD, BF16, false>(x, codebook, group_map, out, l, codes, stream);
 }
 
 }  // namespace
@@ -592,19 +838,20 @@ bool encode_mfma_supported(const Layout &l) { return l.n_centroids <= kMfmaMaxCe
 
 int64_t encode_mfma_grid(const Layout &l) {
   // upper bound on the workgroups of any plan above (one tile per workgroup)
-  const int64_t tile = tile_of<256>(4);
+  const int64_t tile = tile_of<256>(1);
   const int64_t span = l.group_len < l.n ? l.group_len : l.n;
   return (span + tile - 1) / tile * l.n_groups;
 }
 
 hipError_t launch_encode_mfma(const void *x, const void *codebook, const int32_t *group_map,
-                              uint32_t *out_idx, const Layout &l, hipStream_t stream) {
+                              void *out, const Layout &l, const Codes &codes,
+                              hipStream_t stream) {
   if (l.sub_dim == 4) {
-    return l.bf16 ? launch_sd<4, true>(x, codebook, group_map, out_idx, l, stream)
-                  : launch_sd<4, false>(x, codebook, group_map, out_idx, l, stream);
+    return l.bf16 ? launch_scaled<4, true>(x, codebook, group_map, out, l, codes, stream)
+                  : launch_scaled<4, false>(x, codebook, group_map, out, l, codes, stream);
   }
-  return l.bf16 ? launch_sd<8, true>(x, codebook, group_map, out_idx, l, stream)
-                : launch_sd<8, false>(x, codebook, group_map, out_idx, l, stream);
+  return l.bf16 ? launch_scaled<8, true>(x, codebook, group_map, out, l, codes, stream)
+                : launch_scaled<8, false>(x, codebook, group_map, out, l, codes, stream);
 }
 
 }  // namespace vqk

@@ -18,19 +18,34 @@ struct Layout {
   int64_t n_groups;        // ceil(n / group_len)
 };
 
+// Smoothing and output format of an encode.
+struct Codes {
+  const float *scale;    // per-slot channel factors (device), or nullptr
+  int64_t scale_stride;  // floats between slots' factor vectors
+  int32_t head_dim;      // channels per key vector (multiple of sub_dim)
+  int32_t code_bits;     // 1 .. 32; 32 = one uint32 index per sub-vector
+};
+
+// Plain encode: no factors, uint32 indices.
+inline Codes plain_codes(const Layout &l) { return Codes{nullptr, 0, l.sub_dim, 32}; }
+
+// Largest head_dim the kernels stage factors for.
+constexpr int kMaxHeadDim = 4096;
+
 // Number of workgroups the encode launch uses for `l` (the host checks that
 // it fits the grid before launching).
 int64_t encode_grid(const Layout &l);
 
 hipError_t launch_encode(const void *x, const void *codebook, const int32_t *group_map,
-                         uint32_t *out_idx, const Layout &l, hipStream_t stream);
+                         void *out, const Layout &l, const Codes &codes, hipStream_t stream);
 
 // The matrix-core encode keeps the whole codebook slot in LDS: up to 4096 centroids.
 bool encode_mfma_supported(const Layout &l);
 int64_t encode_mfma_grid(const Layout &l);
 
 hipError_t launch_encode_mfma(const void *x, const void *codebook, const int32_t *group_map,
-                              uint32_t *out_idx, const Layout &l, hipStream_t stream);
+                              void *out, const Layout &l, const Codes &codes,
+                              hipStream_t stream);
 
 hipError_t launch_decode(const uint32_t *idx, const void *codebook, const int32_t *group_map,
                          void *out_x, const Layout &l, hipStream_t stream);

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == ["vq_abi_version", "vq_decode", "vq_encode",
-                                    "vq_last_hip_error", "vq_status_str"]
+                                    "vq_encode_packed", "vq_last_hip_error", "vq_status_str"]
 
 
 def test_library_exports_every_declared_function():
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert vq.lib.vq_abi_version() == 1
+    assert vq.lib.vq_abi_version() == 2
     for code in (0, -1, -2, -3, -4, 99):
         assert isinstance(vq.lib.vq_status_str(code), bytes)
     assert vq.lib.vq_status_str(-3) == b"misaligned pointer"
@@ -50,6 +50,15 @@ def enc(**over):
     a.update(over)
     return vq.lib.vq_encode(a["x"], a["cb"], a["n"], a["sd"], a["n_c"], a["dt"], a["stride"],
                             a["k"], a["glen"], a["gmap"], a["out"], a["stream"])
+
+
+def enc_packed(**over):
+    a = dict(x=FAKE, cb=FAKE, n=1024, sd=8, n_c=256, dt=0, stride=0, k=1, glen=1024, gmap=None,
+             scale=FAKE, hd=128, sstride=0, bits=8, out=FAKE, stream=None)
+    a.update(over)
+    return vq.lib.vq_encode_packed(a["x"], a["cb"], a["n"], a["sd"], a["n_c"], a["dt"],
+                                   a["stride"], a["k"], a["glen"], a["gmap"], a["scale"], a["hd"],
+                                   a["sstride"], a["bits"], a["out"], a["stream"])
 
 
 def dec(**over):
@@ -114,3 +123,43 @@ def test_python_wrapper_refuses_cpu_tensors():
 def test_vqerror_message_names_the_status():
     e = vq.VQError(-3, "vq_encode")
     assert "VQ_ERR_MISALIGNED" in str(e) and "misaligned" in str(e)
+
+
+@pytest.mark.parametrize("over,code", [
+    # the checks shared with vq_encode
+    (dict(sd=2), UNSUPPORTED), (dict(n_c=65537, bits=32), UNSUPPORTED), (dict(n=-1), INVALID),
+    (dict(x=None), INVALID), (dict(out=None), INVALID), (dict(x=FAKE + 8), MISALIGNED),
+    # code width
+    (dict(bits=0), INVALID), (dict(bits=33), INVALID), (dict(bits=7), INVALID),
+    (dict(n_c=2, bits=1, scale=None, n=0), OK), (dict(n_c=3, bits=1), INVALID),
+    # smoothing factors
+    (dict(hd=4), INVALID), (dict(hd=12), INVALID), (dict(hd=0), INVALID),
+    (dict(hd=4104), INVALID), (dict(sstride=-1), INVALID), (dict(scale=FAKE + 2), MISALIGNED),
+    (dict(scale=None, hd=0, n=0), OK),
+    # the stream must be 4-byte aligned
+    (dict(out=FAKE + 1), MISALIGNED), (dict(out=FAKE + 2), MISALIGNED),
+    # groups must start on a 32-bit word of the stream
+    (dict(k=2, stride=2048, glen=514, bits=8), UNSUPPORTED),
+    (dict(k=2, stride=2048, glen=521, bits=4, n_c=16), UNSUPPORTED),
+    (dict(k=4, stride=2048, glen=301, bits=8), UNSUPPORTED),
+])
+def test_encode_packed_rejects_on_host(over, code):
+    assert enc_packed(**over) == code
+
+
+def test_encode_packed_empty_is_ok_without_launch():
+    assert enc_packed(n=0, x=None, cb=None, out=None, scale=None) == OK
+
+
+@pytest.mark.parametrize("over", [
+    dict(k=2, stride=2048, glen=520, bits=8), dict(k=2, stride=2048, glen=520, bits=4, n_c=16),
+    dict(k=2, stride=2048, glen=513, bits=32), dict(k=2, stride=2048, glen=1024, n=2048, bits=1, n_c=2),
+])
+def test_encode_packed_word_aligned_groups_pass_validation(over):
+    """Supported group layouts get past every host check; with no device the
+    call then fails at the launch (these fake pointers are never launched on
+    a machine with a GPU)."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("would launch on the fake pointers")
+    assert enc_packed(**over) == -4

@@ -44,6 +44,10 @@ class Workload:
     group_len: int               # sub-vectors per group (group g uses slot g)
     group_map: Optional[np.ndarray] = None
     meta: dict = dataclasses.field(default_factory=dict)
+    # per-channel smoothing factors (fp32 [slots or 1, head_dim]) for the
+    # fused encode; None for the plain search
+    channel_scale: Optional[np.ndarray] = None
+    head_dim: Optional[int] = None
 
     @property
     def n(self) -> int:
@@ -53,6 +57,13 @@ class Workload:
         """Keyword arguments shared by the oracle and the GPU binding."""
         return dict(codebook_stride=self.codebook_stride, n_codebooks=self.n_codebooks,
                     group_len=self.group_len, group_map=self.group_map)
+
+    def packed_kwargs(self) -> dict:
+        """Smoothing arguments of the fused encode (oracle side)."""
+        sc = self.channel_scale
+        return dict(channel_scale=None if sc is None else sc.reshape(-1),
+                    head_dim=self.head_dim if self.head_dim else self.sub_dim,
+                    scale_stride=0 if sc is None or sc.shape[0] == 1 else sc.shape[1])
 
     def sha256(self) -> dict:
         return {"x": hashlib.sha256(self.x.tobytes()).hexdigest()[:16],
@@ -197,6 +208,59 @@ def large_codebook(cfg: int = 5, n: int = 1 << 20) -> Workload:
 
 
 CONFIGS = {1: tiny, 2: llama, 3: falcon, 4: full_cache, 5: large_codebook}
+
+
+# ---------------------------------------------------------------------------
+# Smoothed caches for the fused encode (factors + packed codes)
+# ---------------------------------------------------------------------------
+#
+# The pages give no calibrated smooth factors.  Stand-in recipe: the factor of
+# a channel is 1 / sqrt(s) with s the largest per-head std of that channel
+# (the square-root balance of activation smoothing), rounded to fp32; the
+# codebook is drawn from the smoothed keys' own distribution (std sigma * f),
+# as a calibration on smoothed keys would produce.
+
+def _factors(sigma: np.ndarray) -> np.ndarray:
+    return (1.0 / np.sqrt(sigma.max(axis=0))).astype(np.float32)
+
+
+def falcon_smoothed(cfg: int = 3) -> Workload:
+    """The Falcon3-7B-shape keys of config 3 with per-channel smoothing
+    factors [256] (one codebook slot shared by the 4 KV heads)."""
+    tokens, heads, hd, sd, n_c = 4096, 4, 256, 4, 256
+    sigma = _scaled_cache_scales(_rng(cfg, ROLE_SCALE), _rng(cfg, ROLE_OUTLIER), heads, hd)
+    z = _rng(cfg, ROLE_X).standard_normal((heads, tokens, hd))
+    x = z * sigma[:, None, :]
+    f = _factors(sigma)
+    cb = _scaled_cache_codebook(_rng(cfg, ROLE_CB, 1), sigma * f[None, :], sd, n_c)
+    n = heads * tokens * hd // sd
+    return Workload("falcon3-7b keys, smoothed: 4096 tok x 4 heads x hd256, sd4, n_c256, fp16",
+                    to_f16_bits(x).reshape(-1, sd), to_f16_bits(cb).reshape(-1), sd, n_c, F16,
+                    n_c * sd, 1, n, meta=dict(tokens=tokens, kv_heads=heads, head_dim=hd),
+                    channel_scale=f[None, :], head_dim=hd)
+
+
+def full_cache_smoothed(cfg: int = 4, layers: int = 32, heads: int = 8,
+                        tokens: int = 8192) -> Workload:
+    """Config 4's whole key cache with one smoothing vector and one codebook per
+    (layer, head): factor = 1 / sqrt(that head's channel std)."""
+    base = full_cache(cfg, layers, heads, tokens)
+    sd, n_c, hd = 8, 256, 128
+    scale = np.empty((layers * heads, hd), dtype=np.float32)
+    cb = np.empty((layers * heads, n_c, sd), dtype=np.uint16)
+    for l in range(layers):
+        sigma = _scaled_cache_scales(_rng(cfg, ROLE_SCALE, l), _rng(cfg, ROLE_OUTLIER, l), heads, hd)
+        for h in range(heads):
+            f = (1.0 / np.sqrt(sigma[h])).astype(np.float32)
+            scale[l * heads + h] = f
+            rc = _rng(cfg, ROLE_CB, l, h, 1)
+            cb[l * heads + h] = to_f16_bits(_scaled_cache_codebook(rc, (sigma[h] * f)[None, :],
+                                                                   sd, n_c))
+    base.name = base.name.replace("full cache:", "full cache, smoothed:")
+    base.codebook = cb.reshape(-1)
+    base.channel_scale = scale
+    base.head_dim = hd
+    return base
 
 
 def config(i: int) -> Workload:

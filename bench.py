@@ -17,6 +17,12 @@ roofline position of the encode kernel (algorithmic fp32 flops,
 average duration measured with HIP events on the launch stream, against the
 MI355X fp32 vector peak) and the CPU oracle's rate on a bounded sample on the
 host (``cpu_baseline``).  Other workloads (``--config``) are for exploration.
+
+``--rows`` adds the steps adjacent to the encode, each timed the same way on
+its own synthetic workload and reported under ``"rows"`` in the same line:
+  fused  ``vq_encode_packed``: per-channel smoothing + 8-bit packed codes on
+         the smoothed Falcon3-7B-shape cache.
+``--only ROW`` runs just that row's leg (for profiling its kernel alone).
 """
 from __future__ import annotations
 
@@ -36,6 +42,7 @@ HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
 # 1,048,576 sub-vectors in 7.98 ms (post's "The Numbers" throughput table).
 PAGES_FALCON_SUBVEC_PER_S = 1048576 / 7.98e-3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_falcon3_traffic.txt")
+FUSED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_fused_falcon3_traffic.txt")
 KERNEL_SOURCES = os.path.join(ROOT, "product_vq_kv_amd", "csrc")
 
 
@@ -54,11 +61,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_bytes_per_launch():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+def traffic_bytes_per_launch(path: str = TRAFFIC_FILE):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
     None when there is none or the kernel source changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rows = [ln for ln in f if ln.strip() and not ln.startswith("#")]
         t = json.loads(rows[-1])
     except (OSError, ValueError, IndexError):
@@ -81,6 +88,79 @@ def cpu_baseline(wl, sample_rows: int):
                             f"one thread, {dt:.1f} s")
 
 
+def copy_calibration(torch, dev) -> None:
+    """Plain copy of 256 MiB, five times: the counter scale reference."""
+    src = torch.empty(1 << 26, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 5 x 268435456-byte device copies")
+
+
+def time_launches(fn, steps: int, warmup: int, stream):
+    """(wall seconds per call, event seconds per call) over `steps` calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / steps, e0.elapsed_time(e1) / 1e3 / steps
+
+
+def leg_fused(args, dev, stream):
+    """Smoothed keys, 8-bit codes (vq_encode_packed) on the Falcon3-7B shape."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import product_vq_kv_amd as vq
+    wl = W.falcon_smoothed()
+    log(f"row fused: {wl.name} (n={wl.n})")
+    x = torch.from_numpy(wl.x.view(np.int16)).view(torch.float16).to(dev)
+    cb = torch.from_numpy(wl.codebook.view(np.int16)).view(torch.float16).to(dev)
+    sc = torch.from_numpy(wl.channel_scale[0]).to(dev)
+    bits = 8
+    out = torch.empty(vq.packed_bytes(wl.n, bits), dtype=torch.uint8, device=dev)
+    call = (x.data_ptr(), cb.data_ptr(), wl.n, wl.sub_dim, wl.n_centroids, wl.dtype,
+            wl.codebook_stride, wl.n_codebooks, wl.group_len, None, sc.data_ptr(), wl.head_dim,
+            0, bits, out.data_ptr(), stream.cuda_stream)
+    wall, launch_s = time_launches(lambda: vq.encode_packed_raw(*call), args.steps, args.warmup,
+                                   stream)
+    flops = 3.0 * wl.sub_dim * wl.n_centroids * wl.n
+    algo_bytes = wl.n * (2 * wl.sub_dim + bits / 8) + wl.n_centroids * wl.sub_dim * 2 + wl.head_dim * 4
+    achieved = flops / launch_s / 1e12
+    parity = None
+    if args.cpu_sample > 0:
+        import oracle
+        rows = min(args.cpu_sample // 4, wl.n)
+        ref = oracle.encode_packed(wl.x[:rows], wl.codebook, wl.sub_dim, wl.n_centroids, wl.dtype,
+                                   code_bits=bits, **wl.packed_kwargs())
+        got = out.cpu().numpy()[:ref.size]
+        parity = dict(rows=int(rows), equal=int(np.sum(ref == got)))
+    return {
+        "workload": wl.name + ", 8-bit codes",
+        "value": wl.n / wall,
+        "unit": "sub-vectors/s",
+        "kernel_ms_per_launch": launch_s * 1e3,
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
+                     "traffic": traffic_bytes_per_launch(FUSED_TRAFFIC_FILE)},
+        "algorithmic_gb_per_s": algo_bytes / launch_s / 1e9,
+        "parity_sample": parity,
+    }
+
+
+ROW_LEGS = {"fused": leg_fused}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +171,10 @@ def main() -> int:
                     help="rows the CPU oracle encodes for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter scaling)")
+    ap.add_argument("--rows", default="fused",
+                    help="comma-separated adjacent rows to time after the headline ('' = none)")
+    ap.add_argument("--only", choices=sorted(ROW_LEGS), default=None,
+                    help="run only this row's leg and print its object")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -111,6 +195,12 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        res = ROW_LEGS[args.only](args, dev, torch.cuda.current_stream(dev))
+        if args.copy_calibration:
+            copy_calibration(torch, dev)
+        print(json.dumps({args.only: res}), flush=True)
+        return 0
     wl = W.config(args.config)
     log(f"workload: {wl.name} (n={wl.n})")
     tdt = torch.float16 if wl.dtype == W.F16 else torch.bfloat16
@@ -142,13 +232,7 @@ def main() -> int:
     log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
 
     if args.copy_calibration:
-        # plain copy of 256 MiB, five times: the counter scale reference
-        src = torch.empty(1 << 26, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 5 x 268435456-byte device copies")
+        copy_calibration(torch, dev)
 
     ms_per_step = wall * 1e3 / args.steps
     launch_s = gpu_ms / 1e3 / args.steps
@@ -198,6 +282,11 @@ def main() -> int:
         "parity_sample": parity_sample,
         "vs_baseline_note": "pages' Apple-Silicon Metal kernel on the same shape (context only)",
     }
+    rows = [r for r in args.rows.split(",") if r]
+    if rows:
+        line["rows"] = {}
+        for r in rows:
+            line["rows"][r] = ROW_LEGS[r](args, dev, stream)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -18,7 +18,9 @@ sub_dim = 1 boundary-sum special case, conversion against library routines);
 sub-vectors and the packed code stream (numpy's float32 multiply and
 little-endian packbits, the pages' worked packing examples, exact rational
 brute force).  ``tests/test_oracle_mutants.py`` checks that planted mistakes
-fail those pins.
+fail those pins.  ``oracle/attention.py`` (decode attention over VQ-coded
+caches, float64 numpy from its plain definition) is pinned by
+``tests/test_oracle_attention.py``.
 """
 from __future__ import annotations
 

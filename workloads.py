@@ -299,3 +299,103 @@ def random_case(seed: int, n: int, sub_dim: int, n_centroids: int, dtype: int = 
         raise ValueError("identity group mapping needs one codebook slot per group")
     return Workload(f"random(seed={seed}, n={n}, sd={sub_dim}, n_c={n_centroids})", x, cb,
                     sub_dim, n_centroids, dtype, stride, n_codebooks, group_len, gmap)
+
+
+# ---------------------------------------------------------------------------
+# Decode attention over VQ-coded caches
+# ---------------------------------------------------------------------------
+#
+# The pages ship no calibrated codebooks or caches, so the coded cache is
+# synthetic: key and value codes are drawn directly (uniform over the
+# codebook, or from a skewed law), key codebooks from the smoothed per-channel
+# law of the key generator above, value codebooks N(0, 1), queries N(0, 1)
+# scaled per channel by 1/f so that q~ = q / f stays O(1).  Roles: queries 6,
+# key codes 7, value codes 8, lengths 9 (after the encode roles 0-5).
+
+ROLE_Q, ROLE_KCODE, ROLE_VCODE, ROLE_LEN = 6, 7, 8, 9
+
+
+@dataclasses.dataclass
+class AttnWorkload:
+    name: str
+    q: np.ndarray            # element bits [B, Hq, D]
+    k_codes: np.ndarray      # uint8 [B, Hkv, S, D / k_sub_dim]
+    v_codes: np.ndarray      # uint8 [B, Hkv, S, D / v_sub_dim]
+    k_codebook: np.ndarray   # element bits [Hkv, n_c, k_sub_dim]
+    v_codebook: np.ndarray   # element bits [Hkv, n_c, v_sub_dim]
+    k_scale: Optional[np.ndarray]   # float32 [Hkv, D] or None
+    kv_len: np.ndarray       # int32 [B]
+    dtype: int
+    window: int = 0
+    softmax_scale: Optional[float] = None
+
+    @property
+    def shape(self):
+        B, Hq, D = self.q.shape
+        return B, Hq, self.k_codes.shape[1], D, self.k_codes.shape[2]
+
+    def kwargs(self) -> dict:
+        return dict(k_scale=self.k_scale, kv_len=self.kv_len, window=self.window,
+                    softmax_scale=self.softmax_scale)
+
+
+def attention_case(seed: int, B: int, Hq: int, Hkv: int, D: int, S: int, k_sub_dim: int,
+                   v_sub_dim: int, n_c: int = 256, dtype: int = F16, *, smooth: bool = True,
+                   lens: str = "full", window: int = 0, skew: float = 0.0,
+                   cfg: int = 2000) -> AttnWorkload:
+    """A seeded coded cache.  lens: "full" (every sequence S long), "mixed"
+    (uniform in [1, S]) or "ragged" (mixed plus some empty and some length-1
+    sequences).  skew > 0 draws codes from a Zipf-like law (index c with
+    weight (c + 1)^-skew) instead of uniformly."""
+    rq = np.random.default_rng([cfg, ROLE_Q, seed])
+    sigma = _scaled_cache_scales(_rng(cfg, ROLE_SCALE, seed), _rng(cfg, ROLE_OUTLIER, seed), Hkv, D)
+    if smooth:
+        f = (1.0 / np.sqrt(sigma)).astype(np.float32)
+    else:
+        f = np.ones((Hkv, D), dtype=np.float32)
+    kcb = np.empty((Hkv, n_c, k_sub_dim))
+    rc = _rng(cfg, ROLE_CB, seed)
+    for h in range(Hkv):
+        kcb[h] = _scaled_cache_codebook(rc, (sigma[h] * f[h])[None, :], k_sub_dim, n_c)
+    vcb = rc.standard_normal((Hkv, n_c, v_sub_dim))
+    g = Hq // Hkv
+    qv = rq.standard_normal((B, Hq, D)) / np.repeat(f, g, axis=0)[None, :, :]
+
+    def codes(role, sub_dim):
+        r = np.random.default_rng([cfg, role, seed])
+        shape = (B, Hkv, S, D // sub_dim)
+        if skew > 0:
+            w = (np.arange(n_c) + 1.0) ** -skew
+            return r.choice(n_c, size=shape, p=w / w.sum()).astype(np.uint8)
+        return r.integers(0, n_c, size=shape, dtype=np.int64).astype(np.uint8)
+
+    rl = np.random.default_rng([cfg, ROLE_LEN, seed])
+    if lens == "full":
+        kv_len = np.full(B, S, dtype=np.int32)
+    else:
+        kv_len = rl.integers(1, S + 1, size=B).astype(np.int32)
+        if lens == "ragged" and B >= 3:
+            kv_len[0] = 0
+            kv_len[1] = 1
+            kv_len[2] = S
+    rnd = to_f16_bits if dtype == F16 else to_bf16_bits
+    return AttnWorkload(f"attention(seed={seed}, B={B}, Hq={Hq}, Hkv={Hkv}, D={D}, S={S}, "
+                        f"sd={k_sub_dim}/{v_sub_dim}, n_c={n_c}, lens={lens}, window={window})",
+                        rnd(qv).reshape(B, Hq, D), codes(ROLE_KCODE, k_sub_dim),
+                        codes(ROLE_VCODE, v_sub_dim),
+                        rnd(kcb).reshape(Hkv, n_c, k_sub_dim), rnd(vcb).reshape(Hkv, n_c, v_sub_dim),
+                        f if smooth else None, kv_len, dtype, window)
+
+
+def falcon_decode_attention(B: int = 32, S: int = 4096) -> AttnWorkload:
+    """Falcon3-7B decode step over a VQ-coded cache: 12 query heads sharing 4
+    KV heads (groups of 3), head_dim 256, keys and values in 8-bit codes of
+    sub_dim 4 (the post's VecInfer config), smoothed keys, B sequences whose
+    lengths are uniform in [S/2, S]."""
+    wl = attention_case(1, B, 12, 4, 256, S, 4, 4, 256, F16, smooth=True, lens="full",
+                        cfg=2001)
+    rl = np.random.default_rng([2001, ROLE_LEN, 1])
+    wl.kv_len = rl.integers(S // 2, S + 1, size=B).astype(np.int32)
+    wl.name = (f"falcon3-7b decode attention: {B} seqs x 12 q heads / 4 kv heads, hd256, "
+               f"kv len U[{S // 2}, {S}], 8-bit codes sd4/sd4, smoothed keys, fp16")
+    return wl

@@ -41,6 +41,7 @@
 #ifndef PRODUCT_VQ_KV_AMD_VQ_H
 #define PRODUCT_VQ_KV_AMD_VQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -67,7 +68,9 @@ typedef enum {
 #define VQ_BAD_SLOT 0xFFFFFFFFu
 #define VQ_MAX_CENTROIDS 65536
 #define VQ_MAX_HEAD_DIM 4096
-#define VQ_ABI_VERSION 2
+#define VQ_ATTN_MAX_HEAD_DIM 256
+#define VQ_ATTN_MAX_GROUP 8
+#define VQ_ABI_VERSION 3
 
 /*
  * vq_encode -- nearest-centroid index of every sub-vector.
@@ -142,6 +145,58 @@ vq_status vq_encode_packed(const void *x, const void *codebook, int64_t n, int32
                            int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
                            const float *channel_scale, int32_t head_dim, int64_t scale_stride,
                            int32_t code_bits, void *out_codes, void *stream);
+
+/*
+ * vq_attention_decode -- attention of one new query per sequence over a key /
+ * value cache held as 8-bit product-VQ codes, computed from the codes.
+ *
+ * What it computes ("I Wrote a Metal Kernel to Stop My Mac From OOMing",
+ * section "What's Next: Phase 2": scores from the codebook indices and a
+ * per-query lookup table built from the transformed query, the softmax-
+ * weighted value sum in the same pass, never materializing fp16 keys; blog
+ * index, section "The Kernel's Hot Path": LUT[sub, c] = q_sub . C_k[c]):
+ * for sequence b and query head hq, kv head h = hq / (n_q_heads/n_kv_heads),
+ * attended tokens t in [max(0, L - window), L) with L = kv_len[b] (window 0 =
+ * all L tokens):
+ *     k_t = C_k[h][k_codes[b][h][t][s]] concatenated over s, divided by the
+ *           smoothing factors k_scale[h] (keys stored smoothed, as written by
+ *           vq_encode_packed); v_t likewise from C_v without factors
+ *     out[b][hq] = sum_t softmax_t(softmax_scale * q[b][hq] . k_t) v_t
+ * (0 for a sequence with no attended token).  A code >= n_centroids decodes
+ * to a zero row.  Arithmetic: fp32 (q / f and the LUT in fp32, base-2
+ * softmax); the error bound the tests hold it to is stated with them.
+ *
+ *   q           device, [batch][n_q_heads][head_dim] of `dtype`, 2-aligned.
+ *   k_codes     device, [batch][n_kv_heads][max_kv_len][head_dim/k_sub_dim]
+ *               bytes (the 8-bit stream of vq_encode_packed over a
+ *               [batch][n_kv_heads][max_kv_len][head_dim] key cache), 4-aligned.
+ *   v_codes     device, [batch][n_kv_heads][max_kv_len][head_dim/v_sub_dim] bytes.
+ *   k_codebook  device, [n_kv_heads][n_centroids][k_sub_dim] of `dtype`.
+ *   v_codebook  device, [n_kv_heads][n_centroids][v_sub_dim] of `dtype`.
+ *   k_scale     device fp32 [n_kv_heads][head_dim] smoothing factors, or NULL.
+ *   kv_len      device int32 [batch] (clamped to [0, max_kv_len]) or NULL (all
+ *               max_kv_len).
+ *   k_sub_dim, v_sub_dim  4 or 8; head_dim <= VQ_ATTN_MAX_HEAD_DIM, a multiple
+ *               of 4*k_sub_dim and of v_sub_dim.
+ *   n_centroids 1 .. 256.  n_q_heads a multiple of n_kv_heads, at most
+ *               VQ_ATTN_MAX_GROUP query heads per kv head.
+ *   out         device fp32 [batch][n_q_heads][head_dim], 4-aligned.
+ *   workspace   device scratch of at least vq_attention_workspace_bytes(...)
+ *               bytes, 4-aligned, owned by the caller; its contents on entry do
+ *               not matter and on return are unspecified.  Calls that share a
+ *               workspace must be ordered on one stream.
+ */
+size_t vq_attention_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim,
+                                    int32_t max_kv_len);
+
+vq_status vq_attention_decode(const void *q, const uint8_t *k_codes, const uint8_t *v_codes,
+                              const void *k_codebook, const void *v_codebook,
+                              const float *k_scale, const int32_t *kv_len, int32_t batch,
+                              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                              int32_t max_kv_len, int32_t k_sub_dim, int32_t v_sub_dim,
+                              int32_t n_centroids, vq_dtype dtype, int32_t window,
+                              float softmax_scale, float *out, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * vq_decode -- gather used to check encode: row n of out_x is centroid idx[n]

@@ -22,6 +22,7 @@ oracle computes that attention from its plain definition, in float64:
       v_t = codebook_v[h][v_codes[b, h, t, s]] concatenated
       score_t = softmax_scale * (q[b, hq] . k_t)
       out[b, hq] = sum_t softmax(score)_t * v_t      (0 when no token)
+  (a code >= n_centroids decodes to a zero row)
 
 Every step is one library primitive (numpy gather, float64 matmul, exp) over
 the definition; no blocking, chunking or reordering.  ``tolerance_terms``
@@ -54,9 +55,14 @@ def _attended(L: int, window: int):
 
 
 def dequantize(codes: np.ndarray, codebook: np.ndarray, dtype: int) -> np.ndarray:
-    """[T, n_sub] codes -> [T, n_sub * sub_dim] float64 rows of `codebook` [n_c, sd]."""
+    """[T, n_sub] codes -> [T, n_sub * sub_dim] float64 rows of `codebook` [n_c, sd].
+    A code >= n_c decodes to a row of zeros (as the encode library's gather
+    does for an out-of-range index)."""
     cb = widen(codebook, dtype)
-    return cb[np.asarray(codes, dtype=np.int64)].reshape(codes.shape[0], -1)
+    codes = np.asarray(codes, dtype=np.int64)
+    if codes.size and codes.max() >= cb.shape[0]:
+        cb = np.vstack([cb, np.zeros((int(codes.max()) + 1 - cb.shape[0], cb.shape[1]))])
+    return cb[codes].reshape(codes.shape[0], -1)
 
 
 def decode_attention(q, k_codes, v_codes, k_codebook, v_codebook, dtype, *, k_scale=None,

@@ -10,6 +10,7 @@ is missing or cannot be loaded, importing this package raises.
     idx = vq.encode(keys_subvectors, codebook)          # uint32 [N]
     rec = vq.decode(idx, codebook)                      # gather, for checking
     codes = vq.encode_packed(keys, codebook, channel_scale=f, code_bits=8)  # uint8 stream
+    o = vq.attention_decode(q, k_codes, v_codes, k_cb, v_cb, k_scale=f)    # fp32 [B, Hq, D]
 
 ``encode`` follows the encode step of VecInfer product vector quantization as
 the VeloxQuant-MLX blog post "I Wrote a Metal Kernel to Stop My Mac From
@@ -25,8 +26,9 @@ from typing import Optional
 
 import torch  # loads the HIP runtime that libvq.so binds to (same soname)
 
-__all__ = ["encode", "decode", "encode_packed", "packed_bytes", "encode_raw", "decode_raw",
-           "encode_packed_raw", "VQError", "lib", "LIB_PATH", "F16", "BF16", "BAD_SLOT",
+__all__ = ["encode", "decode", "encode_packed", "packed_bytes", "attention_decode",
+           "attention_workspace_bytes", "encode_raw", "decode_raw", "encode_packed_raw",
+           "attention_decode_raw", "VQError", "lib", "LIB_PATH", "F16", "BF16", "BAD_SLOT",
            "MAX_CENTROIDS", "MAX_HEAD_DIM", "STATUS"]
 
 F16 = 0
@@ -53,6 +55,12 @@ lib.vq_encode.restype = _i32
 lib.vq_encode_packed.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _p, _i32,
                                  _i64, _i32, _p, _p]
 lib.vq_encode_packed.restype = _i32
+lib.vq_attention_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+lib.vq_attention_workspace_bytes.restype = ctypes.c_size_t
+lib.vq_attention_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _p,
+                                    ctypes.c_size_t, _p]
+lib.vq_attention_decode.restype = _i32
 lib.vq_decode.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _p, _p]
 lib.vq_decode.restype = _i32
 lib.vq_status_str.argtypes = [_i32]
@@ -258,4 +266,83 @@ def decode(idx: torch.Tensor, codebook: torch.Tensor, *, group_len: Optional[int
         raise ValueError("out must be a contiguous [N, sub_dim] tensor of the codebook dtype")
     decode_raw(idx.data_ptr(), codebook.data_ptr(), n, sd, n_c, dt, stride, k, group_len, gptr,
                out.data_ptr(), _stream_of(idx.device, stream))
+    return out
+
+
+def attention_workspace_bytes(batch: int, n_q_heads: int, head_dim: int, max_kv_len: int) -> int:
+    return int(lib.vq_attention_workspace_bytes(batch, n_q_heads, head_dim, max_kv_len))
+
+
+def attention_decode_raw(q_ptr, k_codes_ptr, v_codes_ptr, k_cb_ptr, v_cb_ptr, k_scale_ptr,
+                         kv_len_ptr, batch, n_q_heads, n_kv_heads, head_dim, max_kv_len,
+                         k_sub_dim, v_sub_dim, n_centroids, dtype, window, softmax_scale,
+                         out_ptr, ws_ptr, ws_bytes, stream) -> None:
+    """Direct call of ``vq_attention_decode`` with integer pointers (raises on error)."""
+    _check(lib.vq_attention_decode(q_ptr, k_codes_ptr, v_codes_ptr, k_cb_ptr, v_cb_ptr,
+                                   k_scale_ptr, kv_len_ptr, batch, n_q_heads, n_kv_heads,
+                                   head_dim, max_kv_len, k_sub_dim, v_sub_dim, n_centroids, dtype,
+                                   window, softmax_scale, out_ptr, ws_ptr, ws_bytes, stream),
+           "vq_attention_decode")
+
+
+def attention_decode(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor,
+                     k_codebook: torch.Tensor, v_codebook: torch.Tensor, *,
+                     k_scale: Optional[torch.Tensor] = None,
+                     kv_len: Optional[torch.Tensor] = None, window: int = 0,
+                     softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode attention from 8-bit VQ codes: fp32 [B, Hq, D].
+
+    q           fp16/bf16 [B, Hq, D]
+    k_codes     uint8 [B, Hkv, S, D / k_sub_dim]; v_codes uint8 [B, Hkv, S, D / v_sub_dim]
+    k_codebook  [Hkv, n_c, k_sub_dim] (same dtype as q); v_codebook [Hkv, n_c, v_sub_dim]
+    k_scale     fp32 [Hkv, D] smoothing factors the keys were encoded with, or None
+    kv_len      int32 [B] attended prefix per sequence (None: all S)
+    window      attend to the last `window` tokens only (0: all)
+    softmax_scale  default 1 / sqrt(D)
+    workspace   optional uint8 device tensor of attention_workspace_bytes(...) bytes
+    """
+    for t in (q, k_codes, v_codes, k_codebook, v_codebook):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous device tensors")
+    dt = _dtype_code(q.dtype)
+    if k_codebook.dtype != q.dtype or v_codebook.dtype != q.dtype:
+        raise TypeError("codebooks must have q's dtype")
+    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise TypeError("codes must be uint8")
+    B, Hq, D = q.shape
+    _, Hkv, S, nk = k_codes.shape
+    hkv2, n_c, sdk = k_codebook.shape
+    _, _, sdv = v_codebook.shape
+    if (k_codes.shape[:3] != (B, Hkv, S) or v_codes.shape[:3] != (B, Hkv, S)
+            or nk * sdk != D or v_codes.shape[3] * sdv != D or hkv2 != Hkv
+            or tuple(v_codebook.shape[:2]) != (Hkv, n_c)):
+        raise ValueError("inconsistent shapes")
+    sptr = None
+    if k_scale is not None:
+        if (k_scale.dtype != torch.float32 or not k_scale.is_cuda or not k_scale.is_contiguous()
+                or tuple(k_scale.shape) != (Hkv, D)):
+            raise ValueError("k_scale must be a contiguous fp32 device tensor [Hkv, D]")
+        sptr = k_scale.data_ptr()
+    lptr = None
+    if kv_len is not None:
+        if kv_len.dtype != torch.int32 or not kv_len.is_cuda or kv_len.numel() != B:
+            raise ValueError("kv_len must be an int32 device tensor [B]")
+        lptr = kv_len.data_ptr()
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor [B, Hq, D]")
+    need = attention_workspace_bytes(B, Hq, D, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    attention_decode_raw(q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
+                         k_codebook.data_ptr(), v_codebook.data_ptr(), sptr, lptr, B, Hq, Hkv, D,
+                         S, sdk, sdv, n_c, dt, window, softmax_scale, out.data_ptr(),
+                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                         _stream_of(q.device, stream))
     return out

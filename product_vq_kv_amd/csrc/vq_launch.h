@@ -50,4 +50,24 @@ hipError_t launch_encode_mfma(const void *x, const void *codebook, const int32_t
 hipError_t launch_decode(const uint32_t *idx, const void *codebook, const int32_t *group_map,
                          void *out_x, const Layout &l, hipStream_t stream);
 
+// Decode attention over VQ-coded caches (validated by the caller).
+struct AttnLayout {
+  const void *q;             // [B][Hq][D] fp16/bf16
+  const uint8_t *k_codes;    // [B][Hkv][S][D / k_sub_dim]
+  const uint8_t *v_codes;    // [B][Hkv][S][D / v_sub_dim]
+  const void *k_codebook;    // [Hkv][n_c][k_sub_dim]
+  const void *v_codebook;    // [Hkv][n_c][v_sub_dim]
+  const float *k_scale;      // [Hkv][D] or nullptr
+  const int32_t *kv_len;     // [B] or nullptr
+  float *out;                // [B][Hq][D]
+  float *workspace;          // attention_chunks(S) partials per (b, hq)
+  int32_t batch, n_q_heads, n_kv_heads, head_dim, max_kv_len;
+  int32_t k_sub_dim, v_sub_dim, n_centroids, bf16, window;
+  float softmax_scale;
+};
+
+int attention_chunks(int max_kv_len);
+size_t attention_lds_bytes(int k_sub_dim, int v_sub_dim, int head_dim, int group);
+hipError_t launch_attention(const AttnLayout &l, hipStream_t stream);
+
 }  // namespace vqk

@@ -1,0 +1,141 @@
+"""GPU parity of decode attention over VQ codes against the float64 oracle.
+
+``vq_attention_decode`` (through its C ABI) must match oracle/attention.py
+within an error bound derived from its fp32 arithmetic:
+
+  score error (natural-log units)  Delta <= 1.5 (sd_k + n_sub_k + 4) u A
+      A = scale * max_t sum_i |q_i k_ti|: the LUT entry is an sd_k-term fp32
+      dot product, the score a sum of n_sub_k entries, plus q / f, the
+      scale * log2(e) multiply and the base change (4 roundings);
+  |out - ref|  <=  (2 Delta + (3 T + 32) u) * M_d  (+ 1e-30)
+      M_d = sum_t p_t |v_td|; T attended tokens: exp2 and its input roundings,
+      the fp32 sums of weights and of weighted values, the chunk rescales.
+
+The bound is what the arithmetic guarantees in the worst case; the measured
+error is reported too and is typically ~1e-7 of M.  Cases cover both code
+sub-dims for keys and values, fp16 and bf16, smoothed and plain keys,
+grouped-query groups 1..8, head_dim 16..256, multi-chunk and ragged lengths
+(empty and one-token sequences), windows, codes past the codebook, a dirty
+workspace, and the Falcon3-7B decode workload at full size.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as A
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import product_vq_kv_amd as vq  # noqa: E402
+
+DEV = torch.device("cuda:0")
+U = 2.0 ** -24
+
+
+def to_dev(wl):
+    tdt = torch.float16 if wl.dtype == W.F16 else torch.bfloat16
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt).to(DEV)
+
+    return dict(q=bits(wl.q), k_codes=torch.from_numpy(wl.k_codes).to(DEV),
+                v_codes=torch.from_numpy(wl.v_codes).to(DEV), k_codebook=bits(wl.k_codebook),
+                v_codebook=bits(wl.v_codebook),
+                k_scale=None if wl.k_scale is None else torch.from_numpy(wl.k_scale).to(DEV),
+                kv_len=torch.from_numpy(wl.kv_len.astype(np.int32)).to(DEV))
+
+
+def gpu_attention(wl, dirty_workspace=True):
+    t = to_dev(wl)
+    B, Hq, Hkv, D, S = wl.shape
+    ws = None
+    if dirty_workspace:
+        n = vq.attention_workspace_bytes(B, Hq, D, S) // 4
+        ws = torch.full((max(n, 1),), float("nan"), dtype=torch.float32, device=DEV)
+    out = vq.attention_decode(t["q"], t["k_codes"], t["v_codes"], t["k_codebook"],
+                              t["v_codebook"], k_scale=t["k_scale"], kv_len=t["kv_len"],
+                              window=wl.window, softmax_scale=wl.softmax_scale, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def assert_attention_parity(wl):
+    B, Hq, Hkv, D, S = wl.shape
+    ref = A.decode_attention(wl.q, wl.k_codes, wl.v_codes, wl.k_codebook, wl.v_codebook,
+                             wl.dtype, **wl.kwargs())
+    Aq, T, M = A.tolerance_terms(wl.q, wl.k_codes, wl.v_codes, wl.k_codebook, wl.v_codebook,
+                                 wl.dtype, **wl.kwargs())
+    got = gpu_attention(wl)
+    sdk = D // wl.k_codes.shape[3]
+    n_sub_k = wl.k_codes.shape[3]
+    delta = 1.5 * (sdk + n_sub_k + 4) * U * Aq
+    rel = 2 * delta + (3 * T + 32) * U
+    bound = rel[:, :, None] * M + 1e-30
+    err = np.abs(got - ref)
+    worst = float(np.max(err / np.maximum(M, 1e-300))) if M.size else 0.0
+    print(f"[parity] {wl.name}: max |err| / M = {worst:.3e}, "
+          f"bound/M up to {float(rel.max()) if rel.size else 0:.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{len(bad)} outputs outside the bound; first {bad[:3].tolist()}: "
+                           f"got {got[tuple(bad[0])]} want {ref[tuple(bad[0])]}")
+    # empty sequences give exact zeros
+    assert np.all(got[wl.kv_len == 0] == 0)
+
+
+CASES = [
+    # (seed, B, Hq, Hkv, D, S, sdk, sdv, n_c, dtype, extras)
+    (1, 3, 6, 2, 32, 50, 4, 8, 64, W.F16, dict(lens="ragged")),
+    (2, 2, 4, 4, 64, 129, 8, 4, 256, W.BF16, dict(lens="mixed", smooth=False)),
+    (3, 2, 12, 4, 16, 40, 4, 4, 16, W.F16, dict(window=7)),
+    (4, 4, 8, 1, 32, 33, 8, 8, 200, W.F16, dict(lens="ragged", skew=1.2, window=100)),
+    (5, 3, 12, 4, 256, 1500, 4, 4, 256, W.F16, dict(lens="ragged")),
+    (6, 2, 32, 8, 128, 2049, 8, 8, 256, W.BF16, dict(lens="mixed")),
+    (7, 5, 8, 8, 128, 700, 8, 4, 256, W.F16, dict(lens="mixed", window=333)),
+    (8, 2, 16, 2, 64, 1100, 4, 8, 100, W.F16, dict(lens="ragged", skew=0.8)),
+    (9, 1, 1, 1, 256, 4096, 4, 4, 256, W.BF16, dict()),
+    (10, 6, 4, 1, 96, 520, 8, 8, 33, W.F16, dict(lens="ragged", window=513)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"t{c[0]}_D{c[4]}_S{c[5]}" for c in CASES])
+def test_attention_matches_oracle(case):
+    seed, B, Hq, Hkv, D, S, sdk, sdv, n_c, dt, extra = case
+    window = extra.pop("window", 0)
+    wl = W.attention_case(seed, B, Hq, Hkv, D, S, sdk, sdv, n_c, dt, window=window, **extra)
+    extra["window"] = window
+    print(f"[case] {wl.name}", flush=True)
+    assert_attention_parity(wl)
+
+
+def test_codes_past_the_codebook_read_zero_rows():
+    wl = W.attention_case(20, 2, 4, 2, 64, 300, 4, 8, 50, W.F16, lens="mixed")
+    r = np.random.default_rng(20)
+    wl.k_codes[r.random(wl.k_codes.shape) < 0.05] = 255
+    wl.v_codes[r.random(wl.v_codes.shape) < 0.05] = 200
+    assert_attention_parity(wl)
+
+
+def test_softmax_scale_and_identical_results_across_workspaces():
+    wl = W.attention_case(21, 2, 6, 3, 64, 900, 8, 8, 256, W.F16, lens="mixed")
+    wl.softmax_scale = 0.3
+    assert_attention_parity(wl)
+    a = gpu_attention(wl, dirty_workspace=True)
+    b = gpu_attention(wl, dirty_workspace=False)
+    assert np.array_equal(a, b)
+
+
+def test_all_sequences_empty():
+    wl = W.attention_case(22, 3, 4, 2, 32, 64, 4, 4, 64, W.F16)
+    wl.kv_len[:] = 0
+    assert np.all(gpu_attention(wl) == 0)
+
+
+def test_falcon_decode_workload_full_size():
+    wl = W.falcon_decode_attention()
+    print(f"[case] {wl.name}", flush=True)
+    assert_attention_parity(wl)

@@ -26,7 +26,8 @@ def declared_functions():
 
 
 def test_header_declares_the_expected_entry_points():
-    assert declared_functions() == ["vq_abi_version", "vq_decode", "vq_encode",
+    assert declared_functions() == ["vq_abi_version", "vq_attention_decode",
+                                    "vq_attention_workspace_bytes", "vq_decode", "vq_encode",
                                     "vq_encode_packed", "vq_last_hip_error", "vq_status_str"]
 
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert vq.lib.vq_abi_version() == 2
+    assert vq.lib.vq_abi_version() == 3
     for code in (0, -1, -2, -3, -4, 99):
         assert isinstance(vq.lib.vq_status_str(code), bytes)
     assert vq.lib.vq_status_str(-3) == b"misaligned pointer"
@@ -163,3 +164,40 @@ def test_encode_packed_word_aligned_groups_pass_validation(over):
     if torch.cuda.is_available():
         pytest.skip("would launch on the fake pointers")
     assert enc_packed(**over) == -4
+
+
+def attn(**over):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, kcb=FAKE, vcb=FAKE, ks=None, kl=None, B=2, Hq=12, Hkv=4,
+             D=256, S=100, sdk=4, sdv=4, n_c=256, dt=0, window=0, scale=0.0625, out=FAKE,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(over)
+    return vq.lib.vq_attention_decode(a["q"], a["kc"], a["vc"], a["kcb"], a["vcb"], a["ks"],
+                                      a["kl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["S"],
+                                      a["sdk"], a["sdv"], a["n_c"], a["dt"], a["window"],
+                                      a["scale"], a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_attention_workspace_size():
+    # one (D + 2)-float partial per (sequence, query head, 512-token chunk)
+    assert vq.lib.vq_attention_workspace_bytes(2, 12, 256, 100) == 2 * 12 * 1 * 258 * 4
+    assert vq.lib.vq_attention_workspace_bytes(2, 12, 256, 1025) == 2 * 12 * 3 * 258 * 4
+    assert vq.lib.vq_attention_workspace_bytes(-1, 12, 256, 100) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(sdk=2), UNSUPPORTED), (dict(sdv=16), UNSUPPORTED), (dict(dt=3), UNSUPPORTED),
+    (dict(n_c=257), UNSUPPORTED), (dict(n_c=0), UNSUPPORTED), (dict(D=512), UNSUPPORTED),
+    (dict(D=40, sdk=4), UNSUPPORTED), (dict(D=36, sdk=4, sdv=8), UNSUPPORTED),
+    (dict(Hq=13), INVALID), (dict(Hq=36, Hkv=4), UNSUPPORTED), (dict(Hkv=0), INVALID),
+    (dict(B=-1), INVALID), (dict(S=-1), INVALID), (dict(window=-1), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(kc=None), INVALID),
+    (dict(ws=None), INVALID), (dict(wsb=100), INVALID),
+    (dict(q=FAKE + 1), MISALIGNED), (dict(kc=FAKE + 2), MISALIGNED),
+    (dict(out=FAKE + 2), MISALIGNED), (dict(ws=FAKE + 2), MISALIGNED),
+    (dict(ks=FAKE + 2), MISALIGNED), (dict(kl=FAKE + 1), MISALIGNED),
+    (dict(B=70000), INVALID),
+    (dict(B=0), OK), (dict(B=0, q=None, out=None, ws=None), OK),
+])
+def test_attention_rejects_on_host(over, code):
+    assert attn(**over) == code

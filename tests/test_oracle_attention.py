@@ -113,6 +113,17 @@ def test_empty_sequence_gives_zero():
     assert np.all(got[0] == 0) and np.any(got[1] != 0)
 
 
+def test_codes_past_the_codebook_decode_to_zero_rows():
+    wl = W.attention_case(13, 1, 1, 1, 8, 3, 4, 4, 4)
+    wl.k_codes[0, 0] = np.array([[0, 1], [200, 2], [3, 255]], np.uint8)
+    wl.v_codes[0, 0] = np.array([[9, 0], [1, 2], [3, 4]], np.uint8)
+    K = A.dequantize(wl.k_codes[0, 0], wl.k_codebook[0], wl.dtype)
+    V = A.dequantize(wl.v_codes[0, 0], wl.v_codebook[0], wl.dtype)
+    assert np.all(K[1, :4] == 0) and np.all(K[2, 4:] == 0) and np.any(K[0] != 0)
+    assert np.all(V[0, :4] == 0) and np.all(V[2, 4:] == 0)
+    assert np.all(np.isfinite(run(wl)))
+
+
 def test_lookup_table_scores_equal_dense_scores():
     """The identity the kernels rely on: with q~ = q / f,
     sum_s LUT[s, code_s] = q . (k~ / f) for LUT[s, c] = q~_s . C_k[c]."""

@@ -22,6 +22,10 @@ host (``cpu_baseline``).  Other workloads (``--config``) are for exploration.
 its own synthetic workload and reported under ``"rows"`` in the same line:
   fused  ``vq_encode_packed``: per-channel smoothing + 8-bit packed codes on
          the smoothed Falcon3-7B-shape cache.
+  attention  ``vq_attention_decode``: one decode step of Falcon3-7B (32
+         sequences, 12 query / 4 KV heads, head_dim 256, lengths U[2048,
+         4096]) over 8-bit key/value codes; HBM roofline on the algorithmic
+         bytes (attended codes, queries, outputs, codebooks, factors).
 ``--only ROW`` runs just that row's leg (for profiling its kernel alone).
 """
 from __future__ import annotations
@@ -43,6 +47,7 @@ HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
 PAGES_FALCON_SUBVEC_PER_S = 1048576 / 7.98e-3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_falcon3_traffic.txt")
 FUSED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_fused_falcon3_traffic.txt")
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_falcon3_decode_traffic.txt")
 KERNEL_SOURCES = os.path.join(ROOT, "product_vq_kv_amd", "csrc")
 
 
@@ -158,7 +163,65 @@ def leg_fused(args, dev, stream):
     }
 
 
-ROW_LEGS = {"fused": leg_fused}
+def leg_attention(args, dev, stream):
+    """One decode-attention step over the VQ-coded Falcon3-7B cache."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import product_vq_kv_amd as vq
+    wl = W.falcon_decode_attention()
+    log(f"row attention: {wl.name}")
+    B, Hq, Hkv, D, S = wl.shape
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).to(dev)
+
+    q, kcb, vcb = bits(wl.q), bits(wl.k_codebook), bits(wl.v_codebook)
+    kc = torch.from_numpy(wl.k_codes).to(dev)
+    vc = torch.from_numpy(wl.v_codes).to(dev)
+    ks = torch.from_numpy(wl.k_scale).to(dev)
+    kl = torch.from_numpy(wl.kv_len).to(dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    wsb = vq.attention_workspace_bytes(B, Hq, D, S)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    sdk, sdv = D // wl.k_codes.shape[3], D // wl.v_codes.shape[3]
+    n_c = wl.k_codebook.shape[1]
+    scale = 1.0 / D ** 0.5
+    call = (q.data_ptr(), kc.data_ptr(), vc.data_ptr(), kcb.data_ptr(), vcb.data_ptr(),
+            ks.data_ptr(), kl.data_ptr(), B, Hq, Hkv, D, S, sdk, sdv, n_c, W.F16, 0, scale,
+            out.data_ptr(), ws.data_ptr(), wsb, stream.cuda_stream)
+    wall, launch_s = time_launches(lambda: vq.attention_decode_raw(*call), args.steps,
+                                   args.warmup, stream)
+    toks = int(np.sum(wl.kv_len)) * Hkv
+    algo_bytes = (toks * (D // sdk + D // sdv) + B * Hq * D * (2 + 4)
+                  + Hkv * n_c * (sdk + sdv) * 2 + Hkv * D * 4)
+    achieved = algo_bytes / launch_s / 1e9
+    parity = None
+    if args.cpu_sample > 0:
+        from oracle import attention as A
+        nb = 4
+        ref = A.decode_attention(wl.q[:nb], wl.k_codes[:nb], wl.v_codes[:nb], wl.k_codebook,
+                                 wl.v_codebook, wl.dtype, k_scale=wl.k_scale,
+                                 kv_len=wl.kv_len[:nb])
+        got = out.cpu().numpy()[:nb].astype(np.float64)
+        parity = dict(sequences=nb, max_abs_err=float(np.max(np.abs(got - ref))),
+                      max_abs_ref=float(np.max(np.abs(ref))))
+    return {
+        "workload": wl.name,
+        "value": B / wall,
+        "unit": "decode steps (sequences) / s",
+        "ms_per_call": wall * 1e3,
+        "kernel_ms_per_launch": launch_s * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_bytes_per_launch(ATTN_TRAFFIC_FILE)},
+        "algorithmic_bytes_per_launch": algo_bytes,
+        "tokens_attended_per_launch": int(np.sum(wl.kv_len)) * Hq,
+        "parity_sample": parity,
+    }
+
+
+ROW_LEGS = {"fused": leg_fused, "attention": leg_attention}
 
 
 def main() -> int:
@@ -171,7 +234,7 @@ def main() -> int:
                     help="rows the CPU oracle encodes for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter scaling)")
-    ap.add_argument("--rows", default="fused",
+    ap.add_argument("--rows", default="fused,attention",
                     help="comma-separated adjacent rows to time after the headline ('' = none)")
     ap.add_argument("--only", choices=sorted(ROW_LEGS), default=None,
                     help="run only this row's leg and print its object")

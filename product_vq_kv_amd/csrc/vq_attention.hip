@@ -17,9 +17,11 @@
 // an unnormalized partial (m, l, o) per head to the caller's workspace; a
 // second launch merges the chunks (flash-decoding split).  Within a chunk:
 //   * the codebooks are widened to fp32 in LDS once;
-//   * per query head the LUT [n_sub][n_c] (<= 64 KB) is built in LDS and each
-//     lane gathers the score of one token from it (one LDS read per
-//     sub-space); softmax runs in base 2 with scale * log2(e) folded into q~;
+//   * per query head the LUT is built in LDS, 16 sub-spaces x 256 codes at a
+//     time (16 KB, so several workgroups share a CU), and each lane gathers
+//     the scores of its tokens from it (one LDS read per sub-space, the key
+//     codes held in registers); softmax runs in base 2 with scale * log2(e)
+//     folded into q~;
 //   * the value sum maps lanes to (value sub-space, token group): a lane reads
 //     one value-codebook row per token and feeds all g heads with it.
 #include <hip/hip_runtime.h>
@@ -36,6 +38,11 @@ constexpr int kThreads = 256;
 constexpr int kChunk = 512;     // tokens per workgroup
 constexpr int kMaxGroup = 8;    // query heads per kv head
 constexpr int kRows = 256;      // every 8-bit code has a table row (zero past n_c)
+constexpr int kTokPerLane = kChunk / kThreads;  // score phase: tokens per lane
+constexpr int kMaxKeyWords = 16;                // 4-code words per key row (<= 64 codes)
+constexpr int kVPrefetch = 16;                  // value phase: code loads in flight per lane
+constexpr int kLutBlock = 16;                   // sub-spaces per LUT block in LDS
+constexpr int kVGroup = 4;                      // query heads per value pass
 constexpr float kNegInf = -__builtin_inff();
 
 template <bool BF16>
@@ -98,17 +105,18 @@ struct AttnArgs {
   float qmul;               // softmax_scale * log2(e)
 };
 
-// LDS: ck [256][SDK], cv [256][SDV], lut [n_sub_k][256], qt [D],
+// LDS: ck [256][SDK], cv [256][SDV], lut [kLutBlock][256], qt [D],
 // p [g][kChunk], red (reduction / partial sums) [max(64, NG * D)].  The
 // tables have a row for every byte value; rows past n_c are zero, so a code
-// >= n_c decodes to a zero row (as vq_decode does for a bad index).
+// >= n_c decodes to a zero row (as vq_decode does for a bad index).  The LUT
+// holds kLutBlock sub-spaces at a time (16 KB), so several workgroups share
+// a CU.
 template <int SDK, int SDV>
 size_t attn_lds_bytes(int D, int g) {
-  const int n_sub_k = D / SDK;
   const int n_sub_v = D / SDV;
   const int ng = kThreads / n_sub_v;
   return sizeof(float) * (static_cast<size_t>(kRows) * (SDK + SDV) +
-                          static_cast<size_t>(n_sub_k) * kRows + D +
+                          static_cast<size_t>(kLutBlock) * kRows + D +
                           static_cast<size_t>(g) * kChunk + std::max(64, ng * D));
 }
 
@@ -123,7 +131,7 @@ attn_partial(const AttnArgs a) {
   float *ck = lds;
   float *cv = ck + kRows * SDK;
   float *lut = cv + kRows * SDV;
-  float *qt = lut + n_sub_k * kRows;
+  float *qt = lut + kLutBlock * kRows;
   float *p = qt + D;
   float *red = p + g * kChunk;
 
@@ -148,65 +156,97 @@ attn_partial(const AttnArgs a) {
     return;
   }
 
-  // codebooks of kv head h, widened once
+  // codebooks of kv head h, widened once.  (Loads are unconditional from
+  // clamped in-bounds addresses: a load under a branch is waited for before
+  // the next one is issued.)
   const uint16_t *kcb = a.k_cb + static_cast<int64_t>(h) * n_c * SDK;
   const uint16_t *vcb = a.v_cb + static_cast<int64_t>(h) * n_c * SDV;
-  for (int e = tid; e < kRows * SDK; e += kThreads)
-    ck[e] = (e < n_c * SDK) ? widen<BF16>(kcb[e]) : 0.0f;
-  for (int e = tid; e < kRows * SDV; e += kThreads)
-    cv[e] = (e < n_c * SDV) ? widen<BF16>(vcb[e]) : 0.0f;
+  for (int e = tid; e < kRows * SDK; e += kThreads) {
+    const float v = widen<BF16>(kcb[min(e, n_c * SDK - 1)]);
+    ck[e] = (e < n_c * SDK) ? v : 0.0f;
+  }
+  for (int e = tid; e < kRows * SDV; e += kThreads) {
+    const float v = widen<BF16>(vcb[min(e, n_c * SDV - 1)]);
+    cv[e] = (e < n_c * SDV) ? v : 0.0f;
+  }
 
   const int64_t row0 = (static_cast<int64_t>(b) * a.Hkv + h) * a.S;
   const uint8_t *kc = a.k_codes + row0 * n_sub_k;
   const uint8_t *vc = a.v_codes + row0 * n_sub_v;
 
+  // this lane's key-code rows (tokens t0 + tid + kThreads*i), loaded once
+  // with every load in flight and reused by all g query heads
+  const int kwords = n_sub_k / 4;
+  uint32_t kw[kTokPerLane][kMaxKeyWords];
+#pragma unroll
+  for (int i = 0; i < kTokPerLane; ++i) {
+    const int t = min(max(t0 + tid + kThreads * i, lo), hi - 1);
+    const uint32_t *crow = reinterpret_cast<const uint32_t *>(kc + static_cast<int64_t>(t) * n_sub_k);
+#pragma unroll
+    for (int w = 0; w < kMaxKeyWords; ++w) kw[i][w] = crow[min(w, kwords - 1)];
+  }
+
   for (int j = 0; j < g; ++j) {
     const int hq = h * g + j;
     const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.Hq + hq) * D;
-    __syncthreads();  // previous head's LUT is no longer read
+    __syncthreads();  // the previous head is done with qt and the LUT
     for (int d = tid; d < D; d += kThreads) {
       float v = widen<BF16>(qrow[d]);
       if (a.k_scale) v = v / a.k_scale[static_cast<int64_t>(h) * D + d];
       qt[d] = v * a.qmul;
     }
-    __syncthreads();
-    // LUT[s][c] = sum_i qt[s*SDK + i] * ck[c][i], i ascending
-    for (int e = tid; e < n_sub_k * kRows; e += kThreads) {
-      const int s = e / kRows, c = e % kRows;
-      const float *qs = qt + s * SDK;
-      const float *cc = ck + c * SDK;
-      float acc = qs[0] * cc[0];
+    // scores (base-2 units): LUT gathers, sub-spaces in ascending order, the
+    // LUT built kLutBlock sub-spaces at a time
+    float acc[kTokPerLane];
 #pragma unroll
-      for (int i = 1; i < SDK; ++i) acc = __builtin_fmaf(qs[i], cc[i], acc);
-      lut[e] = acc;
-    }
-    __syncthreads();
-    // scores (base-2 units), one token per lane per pass
-    float mloc = kNegInf;
-    for (int t = lo + tid; t < t0 + kChunk; t += kThreads) {
-      float sc = kNegInf;
-      if (t < hi) {
-        const uint32_t *crow = reinterpret_cast<const uint32_t *>(kc + static_cast<int64_t>(t) * n_sub_k);
-        float acc = 0.0f;
-        for (int w = 0; w < n_sub_k / 4; ++w) {
-          const uint32_t cw = crow[w];
+    for (int i = 0; i < kTokPerLane; ++i) acc[i] = 0.0f;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int s = 4 * w + k;
-            const float l = lut[s * kRows + ((cw >> (8 * k)) & 0xFFu)];
-            acc = (s == 0) ? l : acc + l;
+    for (int sb = 0; sb < kMaxKeyWords * 4 / kLutBlock; ++sb) {
+      if (sb * kLutBlock < n_sub_k) {  // uniform
+        __syncthreads();  // qt is written; the previous block's LUT is no longer read
+        // LUT[s][c] = sum_i qt[s*SDK + i] * ck[c][i], i ascending
+        for (int e = tid; e < kLutBlock * kRows; e += kThreads) {
+          const int sl = e / kRows, c = e % kRows;
+          const int sg = min(sb * kLutBlock + sl, n_sub_k - 1);
+          const float *qs = qt + sg * SDK;
+          const float *cc = ck + c * SDK;
+          float x = qs[0] * cc[0];
+#pragma unroll
+          for (int i = 1; i < SDK; ++i) x = __builtin_fmaf(qs[i], cc[i], x);
+          lut[e] = x;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kTokPerLane; ++i) {
+#pragma unroll
+          for (int k4 = 0; k4 < kLutBlock / 4; ++k4) {
+            const int w = sb * (kLutBlock / 4) + k4;
+            if (w < kwords) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const int sl = 4 * k4 + k;
+                const float l = lut[sl * kRows + ((kw[i][w] >> (8 * k)) & 0xFFu)];
+                acc[i] = (w == 0 && k == 0) ? l : acc[i] + l;
+              }
+            }
           }
         }
-        sc = acc;
       }
-      p[j * kChunk + (t - t0)] = sc;
-      mloc = fmaxf(mloc, sc);
+    }
+    float sc[kTokPerLane];
+    float mloc = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kTokPerLane; ++i) {
+      const int t = t0 + tid + kThreads * i;
+      sc[i] = (t >= lo && t < hi) ? acc[i] : kNegInf;
+      mloc = fmaxf(mloc, sc[i]);
     }
     const float m = block_max(mloc, red);
     float lsum = 0.0f;
-    for (int t = lo + tid; t < t0 + kChunk; t += kThreads) {
-      const float e = exp2f(p[j * kChunk + (t - t0)] - m);  // masked: exp2(-inf) = 0
-      p[j * kChunk + (t - t0)] = e;
+#pragma unroll
+    for (int i = 0; i < kTokPerLane; ++i) {
+      const float e = exp2f(sc[i] - m);  // masked: exp2(-inf) = 0
+      p[j * kChunk + tid + kThreads * i] = e;
       lsum += e;
     }
     const float l = block_sum(lsum, red);
@@ -218,52 +258,66 @@ attn_partial(const AttnArgs a) {
   }
   __syncthreads();  // all weights are in p
 
-  // value sum: lane (s, grp) walks tokens lo + grp, lo + grp + ng, ...
+  // value sum, kVGroup heads per pass: lane (s, grp) walks tokens lo + grp,
+  // lo + grp + ng, ...; one value-codebook row read feeds every head
   const int ng = kThreads / n_sub_v;
   const int s = tid % n_sub_v, grp = tid / n_sub_v;
-  float acc[kMaxGroup][SDV];
+  for (int j0 = 0; j0 < g; j0 += kVGroup) {
+    float vacc[kVGroup][SDV];
 #pragma unroll
-  for (int j = 0; j < kMaxGroup; ++j)
+    for (int j = 0; j < kVGroup; ++j)
 #pragma unroll
-    for (int i = 0; i < SDV; ++i) acc[j][i] = 0.0f;
-  if (grp < ng) {
-    for (int t = lo + grp; t < hi; t += ng) {
-      const int c = vc[static_cast<int64_t>(t) * n_sub_v + s];
-      float v[SDV];
+      for (int i = 0; i < SDV; ++i) vacc[j][i] = 0.0f;
+    if (grp < ng) {
+      for (int tb = lo + grp; tb < hi; tb += ng * kVPrefetch) {
+        // the codes of the next kVPrefetch tokens, all loads in flight
+        int cs[kVPrefetch];
 #pragma unroll
-      for (int q4 = 0; q4 < SDV / 4; ++q4) {
-        const float4 w = *reinterpret_cast<const float4 *>(cv + c * SDV + 4 * q4);
-        v[4 * q4] = w.x;
-        v[4 * q4 + 1] = w.y;
-        v[4 * q4 + 2] = w.z;
-        v[4 * q4 + 3] = w.w;
-      }
+        for (int u = 0; u < kVPrefetch; ++u) {
+          const int t = min(tb + u * ng, hi - 1);
+          cs[u] = vc[static_cast<int64_t>(t) * n_sub_v + s];
+        }
 #pragma unroll
-      for (int j = 0; j < kMaxGroup; ++j) {
-        if (j < g) {
-          const float pw = p[j * kChunk + (t - t0)];
+        for (int u = 0; u < kVPrefetch; ++u) {
+          const int t = tb + u * ng;
+          if (t >= hi) break;
+          float v[SDV];
 #pragma unroll
-          for (int i = 0; i < SDV; ++i) acc[j][i] = __builtin_fmaf(pw, v[i], acc[j][i]);
+          for (int q4 = 0; q4 < SDV / 4; ++q4) {
+            const float4 w = *reinterpret_cast<const float4 *>(cv + cs[u] * SDV + 4 * q4);
+            v[4 * q4] = w.x;
+            v[4 * q4 + 1] = w.y;
+            v[4 * q4 + 2] = w.z;
+            v[4 * q4 + 3] = w.w;
+          }
+#pragma unroll
+          for (int j = 0; j < kVGroup; ++j) {
+            if (j0 + j < g) {
+              const float pw = p[(j0 + j) * kChunk + (t - t0)];
+#pragma unroll
+              for (int i = 0; i < SDV; ++i) vacc[j][i] = __builtin_fmaf(pw, v[i], vacc[j][i]);
+            }
+          }
         }
       }
     }
-  }
-  // sum the token groups, one head at a time
+    // sum the token groups, one head at a time
 #pragma unroll
-  for (int j = 0; j < kMaxGroup; ++j) {
-    if (j < g) {
-      if (grp < ng) {
+    for (int j = 0; j < kVGroup; ++j) {
+      if (j0 + j < g) {  // uniform
+        if (grp < ng) {
 #pragma unroll
-        for (int i = 0; i < SDV; ++i) red[grp * D + s * SDV + i] = acc[j][i];
+          for (int i = 0; i < SDV; ++i) red[grp * D + s * SDV + i] = vacc[j][i];
+        }
+        __syncthreads();
+        float *pj = part + static_cast<int64_t>(j0 + j) * a.n_chunks * part_stride;
+        for (int d = tid; d < D; d += kThreads) {
+          float o = red[d];
+          for (int r = 1; r < ng; ++r) o += red[r * D + d];
+          pj[d] = o;
+        }
+        __syncthreads();
       }
-      __syncthreads();
-      float *pj = part + static_cast<int64_t>(j) * a.n_chunks * part_stride;
-      for (int d = tid; d < D; d += kThreads) {
-        float o = red[d];
-        for (int r = 1; r < ng; ++r) o += red[r * D + d];
-        pj[d] = o;
-      }
-      __syncthreads();
     }
   }
 }

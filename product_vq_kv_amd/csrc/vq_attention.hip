@@ -269,13 +269,17 @@ attn_partial(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < SDV; ++i) vacc[j][i] = 0.0f;
     if (grp < ng) {
+      // codes of kVPrefetch tokens per batch; the next batch's loads are in
+      // flight while the current batch is summed
+      int cs[kVPrefetch], nx[kVPrefetch];
+#pragma unroll
+      for (int u = 0; u < kVPrefetch; ++u)
+        cs[u] = vc[static_cast<int64_t>(min(lo + grp + u * ng, hi - 1)) * n_sub_v + s];
       for (int tb = lo + grp; tb < hi; tb += ng * kVPrefetch) {
-        // the codes of the next kVPrefetch tokens, all loads in flight
-        int cs[kVPrefetch];
 #pragma unroll
         for (int u = 0; u < kVPrefetch; ++u) {
-          const int t = min(tb + u * ng, hi - 1);
-          cs[u] = vc[static_cast<int64_t>(t) * n_sub_v + s];
+          const int t = min(tb + (kVPrefetch + u) * ng, hi - 1);
+          nx[u] = vc[static_cast<int64_t>(t) * n_sub_v + s];
         }
 #pragma unroll
         for (int u = 0; u < kVPrefetch; ++u) {
@@ -299,6 +303,8 @@ attn_partial(const AttnArgs a) {
             }
           }
         }
+#pragma unroll
+        for (int u = 0; u < kVPrefetch; ++u) cs[u] = nx[u];
       }
     }
     // sum the token groups, one head at a time

@@ -20,7 +20,8 @@ little-endian packbits, the pages' worked packing examples, exact rational
 brute force).  ``tests/test_oracle_mutants.py`` checks that planted mistakes
 fail those pins.  ``oracle/attention.py`` (decode attention over VQ-coded
 caches, float64 numpy from its plain definition) is pinned by
-``tests/test_oracle_attention.py``.
+``tests/test_oracle_attention.py``; ``oracle/kmeans.py`` (Lloyd iterations
+with exact member means rounded once to fp16) by ``tests/test_oracle_kmeans.py``.
 """
 from __future__ import annotations
 

@@ -70,7 +70,8 @@ typedef enum {
 #define VQ_MAX_HEAD_DIM 4096
 #define VQ_ATTN_MAX_HEAD_DIM 256
 #define VQ_ATTN_MAX_GROUP 8
-#define VQ_ABI_VERSION 3
+#define VQ_KMEANS_MAX_SLOT_ROWS (1 << 23)
+#define VQ_ABI_VERSION 4
 
 /*
  * vq_encode -- nearest-centroid index of every sub-vector.
@@ -145,6 +146,42 @@ vq_status vq_encode_packed(const void *x, const void *codebook, int64_t n, int32
                            int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
                            const float *channel_scale, int32_t head_dim, int64_t scale_stride,
                            int32_t code_bits, void *out_codes, void *stream);
+
+/*
+ * vq_kmeans -- K-means calibration of the codebook slots on the device.
+ *
+ * The codebook of VecInfer product VQ is a set of K-means centroids trained
+ * on calibration data ("I Wrote a Metal Kernel to Stop My Mac From OOMing",
+ * section "What Even Is a KV Cache And Why Should You Care", step 2).  Runs
+ * `iterations` steps of Lloyd's algorithm from the codebook given, every slot
+ * trained on the sub-vectors of the groups mapped to it:
+ *     assignment: out_idx = vq_encode of every sub-vector (same arithmetic)
+ *     update:     every centroid with members becomes the exact mean of its
+ *                 members rounded once to fp16 (to nearest, ties to even);
+ *                 a centroid without members keeps its value.
+ * The codebook is updated in place; out_idx holds the assignment of the last
+ * iteration (made against the codebook before its last update).  Results
+ * are deterministic and identical to the CPU oracle's.
+ *
+ *   x, n, sub_dim, n_centroids, codebook_stride, n_codebooks, group_len,
+ *   group_map   as for vq_encode; dtype must be VQ_F16; x must be finite.
+ *   codebook    device, read and written.
+ *   iterations  >= 0 (0: nothing is done).
+ *   out_idx     device uint32 [n], 4-aligned.
+ *   workspace   device scratch of at least vq_kmeans_workspace_bytes(...)
+ *               bytes, 8-aligned, owned by the caller; contents on entry do
+ *               not matter.  Calls sharing a workspace must be ordered.
+ * A slot may receive at most VQ_KMEANS_MAX_SLOT_ROWS sub-vectors (n with a
+ * group_map, else min(group_len, n)), else VQ_ERR_UNSUPPORTED: the exact
+ * member sums are 64-bit integers.
+ */
+size_t vq_kmeans_workspace_bytes(int32_t sub_dim, int32_t n_centroids, int64_t n_codebooks);
+
+vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
+                    int32_t n_centroids, vq_dtype dtype, int64_t codebook_stride,
+                    int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
+                    int32_t iterations, uint32_t *out_idx, void *workspace,
+                    size_t workspace_bytes, void *stream);
 
 /*
  * vq_attention_decode -- attention of one new query per sequence over a key /

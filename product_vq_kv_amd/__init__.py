@@ -27,7 +27,7 @@ from typing import Optional
 import torch  # loads the HIP runtime that libvq.so binds to (same soname)
 
 __all__ = ["encode", "decode", "encode_packed", "packed_bytes", "attention_decode",
-           "attention_workspace_bytes", "encode_raw", "decode_raw", "encode_packed_raw",
+           "attention_workspace_bytes", "kmeans", "kmeans_workspace_bytes", "kmeans_raw", "encode_raw", "decode_raw", "encode_packed_raw",
            "attention_decode_raw", "VQError", "lib", "LIB_PATH", "F16", "BF16", "BAD_SLOT",
            "MAX_CENTROIDS", "MAX_HEAD_DIM", "STATUS"]
 
@@ -61,6 +61,11 @@ lib.vq_attention_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32
                                     _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _p,
                                     ctypes.c_size_t, _p]
 lib.vq_attention_decode.restype = _i32
+lib.vq_kmeans_workspace_bytes.argtypes = [_i32, _i32, _i64]
+lib.vq_kmeans_workspace_bytes.restype = ctypes.c_size_t
+lib.vq_kmeans.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _i32, _p, _p,
+                          ctypes.c_size_t, _p]
+lib.vq_kmeans.restype = _i32
 lib.vq_decode.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _p, _p]
 lib.vq_decode.restype = _i32
 lib.vq_status_str.argtypes = [_i32]
@@ -345,4 +350,42 @@ def attention_decode(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tens
                          S, sdk, sdv, n_c, dt, window, softmax_scale, out.data_ptr(),
                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                          _stream_of(q.device, stream))
+    return out
+
+
+def kmeans_workspace_bytes(sub_dim: int, n_centroids: int, n_codebooks: int = 1) -> int:
+    return int(lib.vq_kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks))
+
+
+def kmeans_raw(x_ptr, codebook_ptr, n, sub_dim, n_centroids, dtype, codebook_stride, n_codebooks,
+               group_len, group_map_ptr, iterations, out_ptr, ws_ptr, ws_bytes, stream) -> None:
+    """Direct call of ``vq_kmeans`` with integer pointers (raises on error)."""
+    _check(lib.vq_kmeans(x_ptr, codebook_ptr, n, sub_dim, n_centroids, dtype, codebook_stride,
+                         n_codebooks, group_len, group_map_ptr, iterations, out_ptr, ws_ptr,
+                         ws_bytes, stream), "vq_kmeans")
+
+
+def kmeans(x: torch.Tensor, codebook: torch.Tensor, iterations: int, *,
+           group_len: Optional[int] = None, group_map: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Lloyd K-means on the device: `codebook` (fp16, [n_c, sd] or
+    [slots, n_c, sd]) is updated in place; returns the last assignment
+    (uint32 [N])."""
+    dt, k, n_c, sd, stride, n = _keys(x, codebook)
+    if group_len is None:
+        group_len = max(n, 1)
+    gptr = _group_map_ptr(group_map, n, group_len)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint32, device=x.device)
+    elif out.dtype != torch.uint32 or out.numel() != n or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint32 tensor with one entry per sub-vector")
+    need = kmeans_workspace_bytes(sd, n_c, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=x.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    kmeans_raw(x.data_ptr(), codebook.data_ptr(), n, sd, n_c, dt, stride, k, group_len, gptr,
+               iterations, out.data_ptr(), workspace.data_ptr(),
+               workspace.numel() * workspace.element_size(), _stream_of(x.device, stream))
     return out

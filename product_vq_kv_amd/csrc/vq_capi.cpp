@@ -136,6 +136,43 @@ vq_status vq_decode(const uint32_t *idx, const void *codebook, int64_t n, int32_
       vqk::launch_decode(idx, codebook, group_map, out_x, l, static_cast<hipStream_t>(stream)));
 }
 
+size_t vq_kmeans_workspace_bytes(int32_t sub_dim, int32_t n_centroids, int64_t n_codebooks) {
+  if ((sub_dim != 4 && sub_dim != 8) || n_centroids < 1 || n_centroids > VQ_MAX_CENTROIDS ||
+      n_codebooks < 1)
+    return 0;
+  return vqk::kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks);
+}
+
+vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
+                    int32_t n_centroids, vq_dtype dtype, int64_t codebook_stride,
+                    int64_t n_codebooks, int64_t group_len, const int32_t *group_map,
+                    int32_t iterations, uint32_t *out_idx, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  vqk::Layout l;
+  vq_status st = check_common(codebook, n, sub_dim, n_centroids, dtype, codebook_stride,
+                              n_codebooks, group_len, group_map, &l);
+  if (st != VQ_OK) return st;
+  if (dtype != VQ_F16) return VQ_ERR_UNSUPPORTED;  // exact sums need fp16's fixed grid
+  if (iterations < 0) return VQ_ERR_INVALID_ARG;
+  // exact int64 member sums: at most 2^23 members of +-65504 per slot
+  const int64_t per_slot = group_map ? n : (group_len < n ? group_len : n);
+  if (per_slot > (int64_t(1) << 23)) return VQ_ERR_UNSUPPORTED;
+  if (n == 0 || iterations == 0) return VQ_OK;
+  if (!x || !out_idx || !workspace) return VQ_ERR_INVALID_ARG;
+  if (workspace_bytes < vqk::kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks))
+    return VQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(x) % (2 * sub_dim) != 0 ||
+      reinterpret_cast<uintptr_t>(out_idx) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
+    return VQ_ERR_MISALIGNED;
+  if (vqk::encode_grid(l) > kMaxGrid || vqk::encode_mfma_grid(l) > kMaxGrid ||
+      vqk::kmeans_grid(l) > kMaxGrid || n_codebooks * n_centroids / 256 + 1 > kMaxGrid)
+    return VQ_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return device_result(vqk::launch_kmeans(x, codebook, group_map, out_idx, l, iterations,
+                                          workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t vq_attention_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim,
                                     int32_t max_kv_len) {
   if (batch < 0 || n_q_heads < 0 || head_dim < 0 || max_kv_len < 0) return 0;

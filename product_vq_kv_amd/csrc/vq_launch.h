@@ -66,6 +66,13 @@ struct AttnLayout {
   float softmax_scale;
 };
 
+// K-means calibration (fp16): `iterations` Lloyd steps, codebook updated in
+// place, final assignment in out_idx; workspace = exact member sums + counts.
+size_t kmeans_workspace_bytes(int sub_dim, int n_centroids, int64_t n_codebooks);
+int64_t kmeans_grid(const Layout &l);
+hipError_t launch_kmeans(const void *x, void *codebook, const int32_t *group_map, uint32_t *out_idx,
+                         const Layout &l, int iterations, void *workspace, hipStream_t stream);
+
 int attention_chunks(int max_kv_len);
 size_t attention_lds_bytes(int k_sub_dim, int v_sub_dim, int head_dim, int group);
 hipError_t launch_attention(const AttnLayout &l, hipStream_t stream);

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == ["vq_abi_version", "vq_attention_decode",
                                     "vq_attention_workspace_bytes", "vq_decode", "vq_encode",
-                                    "vq_encode_packed", "vq_last_hip_error", "vq_status_str"]
+                                    "vq_encode_packed", "vq_kmeans", "vq_kmeans_workspace_bytes",
+                                    "vq_last_hip_error", "vq_status_str"]
 
 
 def test_library_exports_every_declared_function():
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert vq.lib.vq_abi_version() == 3
+    assert vq.lib.vq_abi_version() == 4
     for code in (0, -1, -2, -3, -4, 99):
         assert isinstance(vq.lib.vq_status_str(code), bytes)
     assert vq.lib.vq_status_str(-3) == b"misaligned pointer"
@@ -201,3 +202,31 @@ def test_attention_workspace_size():
 ])
 def test_attention_rejects_on_host(over, code):
     assert attn(**over) == code
+
+
+def km(**over):
+    a = dict(x=FAKE, cb=FAKE, n=1024, sd=8, n_c=256, dt=0, stride=0, k=1, glen=1024, gmap=None,
+             it=5, out=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(over)
+    return vq.lib.vq_kmeans(a["x"], a["cb"], a["n"], a["sd"], a["n_c"], a["dt"], a["stride"],
+                            a["k"], a["glen"], a["gmap"], a["it"], a["out"], a["ws"], a["wsb"],
+                            a["stream"])
+
+
+def test_kmeans_workspace_size():
+    assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4) == 4 * 256 * (8 * 8 + 4)
+    assert vq.lib.vq_kmeans_workspace_bytes(3, 256, 4) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dt=1), UNSUPPORTED), (dict(sd=2), UNSUPPORTED), (dict(n_c=0), INVALID),
+    (dict(it=-1), INVALID), (dict(x=None), INVALID), (dict(out=None), INVALID),
+    (dict(ws=None), INVALID), (dict(wsb=16), INVALID), (dict(x=FAKE + 8), MISALIGNED),
+    (dict(out=FAKE + 2), MISALIGNED), (dict(ws=FAKE + 4), MISALIGNED),
+    (dict(glen=512), INVALID),                            # two groups, one slot, no map
+    (dict(n=(1 << 23) + 1, glen=(1 << 23) + 1), UNSUPPORTED),
+    (dict(n=(1 << 24), glen=1 << 23, gmap=FAKE), UNSUPPORTED),
+    (dict(n=0), OK), (dict(it=0), OK), (dict(n=0, x=None, out=None, ws=None), OK),
+])
+def test_kmeans_rejects_on_host(over, code):
+    assert km(**over) == code

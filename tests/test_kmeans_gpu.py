@@ -1,0 +1,119 @@
+"""GPU parity of K-means calibration (vq_kmeans) against the CPU oracle.
+
+Every update is the exact member mean rounded once to fp16 on both sides, so
+the codebooks and assignments must be bit-identical after every iteration.
+Cases cover sub_dim 4 and 8, LDS and global accumulation (n_centroids above
+512), the matrix-core and direct assignment kernels (up to 5000 centroids),
+several slots with group maps and bad slots, exactly representable clusters,
+the Falcon3-7B keys at full size, and whole slots sampled from the 256-slot
+full cache trained in one call.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from oracle import kmeans as K
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import product_vq_kv_amd as vq  # noqa: E402
+
+from tests.test_parity_gpu import to_dev  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def gpu_kmeans(wl, iterations):
+    x, cb3, gmap = to_dev(wl)
+    cb = cb3[0] if wl.n_codebooks == 1 else cb3
+    idx = vq.kmeans(x, cb, iterations, group_len=wl.group_len, group_map=gmap)
+    torch.cuda.synchronize()
+    full = cb3.reshape(wl.n_codebooks, -1).cpu().numpy().view(np.uint16)
+    return full, idx.cpu().numpy().view(np.uint32)
+
+
+def slots_of(cb_flat, wl):
+    """[n_codebooks, n_c * sd] view of a flat codebook buffer."""
+    return np.stack([cb_flat[s * wl.codebook_stride: s * wl.codebook_stride
+                             + wl.n_centroids * wl.sub_dim] for s in range(wl.n_codebooks)])
+
+
+def assert_kmeans_parity(wl, iterations):
+    got_cb, got_idx = gpu_kmeans(wl, iterations)
+    want_cb, want_idx, counts = K.kmeans(wl.x, wl.codebook, wl.sub_dim, wl.n_centroids,
+                                         iterations, threads=16, **wl.kwargs())
+    want = slots_of(want_cb, wl)
+    moved = int(np.sum(want != slots_of(wl.codebook, wl)))
+    print(f"[parity] {wl.name} x{iterations}: {moved} codebook elements moved, "
+          f"{int(np.sum(counts == 0))} empty clusters at the end", flush=True)
+    np.testing.assert_array_equal(got_idx, want_idx)
+    np.testing.assert_array_equal(got_cb, want)
+
+
+CASES = [
+    # (seed, n, sd, n_c, iterations, extras)
+    (1, 3000, 8, 7, 3, {}),
+    (2, 5000, 4, 64, 4, {}),
+    (3, 20000, 8, 256, 5, dict(scale=3.0)),
+    (4, 9000, 4, 600, 2, {}),                 # global accumulation
+    (5, 6000, 8, 2000, 2, dict(dup_frac=0.1)),
+    (6, 3000, 8, 5000, 1, {}),                # direct assignment kernel
+    (7, 9000, 8, 32, 3, dict(n_codebooks=4, group_len=2048, use_map=True)),
+    (8, 7000, 4, 100, 3, dict(n_codebooks=7, group_len=1000, stride_pad=5)),
+    (9, 30000, 4, 16, 6, dict(scale=1e-3)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"k{c[0]}_n{c[1]}_sd{c[2]}_nc{c[3]}" for c in CASES])
+def test_kmeans_matches_oracle(case):
+    seed, n, sd, n_c, iters, extra = case
+    wl = W.random_case(300 + seed, n, sd, n_c, W.F16, **extra)
+    print(f"[case] {wl.name} {extra}", flush=True)
+    assert_kmeans_parity(wl, iters)
+
+
+def test_kmeans_bad_slots_are_left_alone():
+    wl = W.random_case(320, 6000, 8, 24, W.F16, n_codebooks=3, group_len=700, use_map=True)
+    wl.group_map = np.array([0, 2, -1, 1, 3, 2, 7, 0, 1], np.int32)
+    got_cb, got_idx = gpu_kmeans(wl, 2)
+    g = np.arange(wl.n) // 700
+    assert np.all(got_idx[np.isin(g, [2, 4, 6])] == vq.BAD_SLOT)
+    assert_kmeans_parity(wl, 2)
+
+
+def test_kmeans_exact_clusters():
+    pts = np.array([[0, 0, 0, 0], [2, 0, 0, 2], [0, 2, 2, 0], [2, 2, 2, 2],
+                    [10, 10, 10, 10], [12, 12, 12, 12],
+                    [-8, 4, -8, 4], [-6, 6, -6, 6], [-7, 5, -7, 5]], np.float64)
+    init = np.array([[0.5, 0.5, 0.5, 0.5], [10.5, 10, 10, 10], [-7, 4, -7, 4], [100] * 4])
+    wl = W.Workload("exact clusters", W.to_f16_bits(pts).reshape(-1, 4),
+                    W.to_f16_bits(init).reshape(-1), 4, 4, W.F16, 16, 1, 9)
+    got_cb, _ = gpu_kmeans(wl, 3)
+    f = got_cb.view(np.float16).astype(np.float64).reshape(4, 4)
+    assert f[0].tolist() == [1, 1, 1, 1] and f[1].tolist() == [11] * 4
+    assert f[2].tolist() == [-7, 5, -7, 5] and f[3].tolist() == [100] * 4
+    assert_kmeans_parity(wl, 3)
+
+
+def test_kmeans_falcon_keys_full_size():
+    wl = W.config(3)
+    assert_kmeans_parity(wl, 3)
+
+
+def test_kmeans_full_cache_sampled_slots():
+    wl = W.full_cache()
+    got_cb, got_idx = gpu_kmeans(wl, 2)
+    rng = np.random.default_rng(330)
+    for s in [0, 255] + list(rng.choice(np.arange(1, 255), size=4, replace=False)):
+        rows = slice(s * wl.group_len, (s + 1) * wl.group_len)
+        sub = wl.codebook[s * wl.codebook_stride:(s + 1) * wl.codebook_stride]
+        want_cb, want_idx, _ = K.kmeans(wl.x[rows], sub, wl.sub_dim, wl.n_centroids, 2,
+                                        threads=16)
+        np.testing.assert_array_equal(got_idx[rows], want_idx)
+        np.testing.assert_array_equal(got_cb[s], want_cb)
+        print(f"[parity] full cache slot {s}: identical", flush=True)

@@ -26,6 +26,9 @@ its own synthetic workload and reported under ``"rows"`` in the same line:
          sequences, 12 query / 4 KV heads, head_dim 256, lengths U[2048,
          4096]) over 8-bit key/value codes; HBM roofline on the algorithmic
          bytes (attended codes, queries, outputs, codebooks, factors).
+  kmeans  ``vq_kmeans``: 5 Lloyd iterations per call on the Falcon3-7B keys
+         (1,048,576 sub-vectors, 256 centroids, sub_dim 4); fp32 vector
+         roofline on the assignment's algorithmic flops.
 ``--only ROW`` runs just that row's leg (for profiling its kernel alone).
 """
 from __future__ import annotations
@@ -48,6 +51,7 @@ PAGES_FALCON_SUBVEC_PER_S = 1048576 / 7.98e-3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_falcon3_traffic.txt")
 FUSED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_fused_falcon3_traffic.txt")
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_falcon3_decode_traffic.txt")
+KMEANS_ITERATIONS = 5
 KERNEL_SOURCES = os.path.join(ROOT, "product_vq_kv_amd", "csrc")
 
 
@@ -221,7 +225,57 @@ def leg_attention(args, dev, stream):
     }
 
 
-ROW_LEGS = {"fused": leg_fused, "attention": leg_attention}
+def leg_kmeans(args, dev, stream):
+    """K-means calibration (Lloyd) on the Falcon3-7B keys."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import product_vq_kv_amd as vq
+    wl = W.config(3)
+    log(f"row kmeans: {wl.name}, {KMEANS_ITERATIONS} iterations per call")
+    x = torch.from_numpy(wl.x.view(np.int16)).view(torch.float16).to(dev)
+    cb0 = torch.from_numpy(wl.codebook.view(np.int16)).view(torch.float16).to(dev)
+    cb = cb0.clone()
+    idx = torch.empty(wl.n, dtype=torch.uint32, device=dev)
+    wsb = vq.kmeans_workspace_bytes(wl.sub_dim, wl.n_centroids, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    call = (x.data_ptr(), cb.data_ptr(), wl.n, wl.sub_dim, wl.n_centroids, wl.dtype,
+            wl.codebook_stride, 1, wl.group_len, None, KMEANS_ITERATIONS, idx.data_ptr(),
+            ws.data_ptr(), wsb, stream.cuda_stream)
+    steps = max(1, args.steps // 10)
+    wall, launch_s = time_launches(lambda: vq.kmeans_raw(*call), steps, min(args.warmup, 3),
+                                   stream)
+    it_s = launch_s / KMEANS_ITERATIONS
+    flops = 3.0 * wl.sub_dim * wl.n_centroids * wl.n
+    achieved = flops / it_s / 1e12
+    parity = None
+    if args.cpu_sample > 0:
+        # from the initial codebook, one call of the library against the oracle
+        from oracle import kmeans as K
+        cb.copy_(cb0)
+        vq.kmeans_raw(*call)
+        torch.cuda.synchronize()
+        want_cb, want_idx, _ = K.kmeans(wl.x, wl.codebook, wl.sub_dim, wl.n_centroids,
+                                        KMEANS_ITERATIONS, threads=16)
+        got_cb = cb.cpu().numpy().view(np.uint16)
+        parity = dict(iterations=KMEANS_ITERATIONS,
+                      codebook_equal=int(np.sum(got_cb == want_cb)), codebook_size=int(want_cb.size),
+                      assignment_equal=int(np.sum(idx.cpu().numpy().view(np.uint32) == want_idx)),
+                      rows=int(wl.n))
+    return {
+        "workload": wl.name + f", Lloyd x{KMEANS_ITERATIONS} per call",
+        "value": wl.n * KMEANS_ITERATIONS / wall,
+        "unit": "sub-vector-iterations/s",
+        "ms_per_call": wall * 1e3,
+        "ms_per_iteration": it_s * 1e3,
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
+                     "traffic": None},
+        "parity_sample": parity,
+    }
+
+
+ROW_LEGS = {"fused": leg_fused, "attention": leg_attention, "kmeans": leg_kmeans}
 
 
 def main() -> int:
@@ -234,7 +288,7 @@ def main() -> int:
                     help="rows the CPU oracle encodes for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter scaling)")
-    ap.add_argument("--rows", default="fused,attention",
+    ap.add_argument("--rows", default="fused,attention,kmeans",
                     help="comma-separated adjacent rows to time after the headline ('' = none)")
     ap.add_argument("--only", choices=sorted(ROW_LEGS), default=None,
                     help="run only this row's leg and print its object")

@@ -59,27 +59,34 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of every HIP/C++ source of the library (any change invalidates
-    counter figures taken on an earlier build)."""
+# The sources each profiled kernel is built from: a counter summary stays
+# valid while these files are unchanged.
+ENCODE_SOURCES = ("vq_encode_mfma.hip", "vq_codes.h")
+ATTENTION_SOURCES = ("vq_attention.hip",)
+
+
+def kernel_source_hash(names=ENCODE_SOURCES) -> str:
+    """Hash of the named library sources (a change invalidates counter
+    figures taken on an earlier build of that kernel)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_SOURCES)):
-        if name.endswith((".hip", ".cpp", ".h")):
-            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(names):
+        with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
 def traffic_bytes_per_launch(path: str = TRAFFIC_FILE):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
+    None when there is none or the kernel's sources changed since it was
+    taken."""
     try:
         with open(path) as f:
             rows = [ln for ln in f if ln.strip() and not ln.startswith("#")]
         t = json.loads(rows[-1])
-    except (OSError, ValueError, IndexError):
+        names = tuple(t["kernel_sources"])
+    except (OSError, ValueError, IndexError, KeyError, TypeError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(names):
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -84,6 +84,21 @@ struct Consts {
   static constexpr float kGamma2 = 2.0f * (SD + 2) * kU * 1.01f;  // >= 1/(1-gamma) - 1
 };
 
+// Plain sub_dim 4 leaves K slots 4..7 of the matrix-core dot empty; they
+// carry C instead ("folded"): A = [-c, C_hi, C_lo, 0, 0], B = [x, 1, 1, 0, 0],
+// so the accumulator input is zero and C need not be loaded per block.
+template <int SD, bool SCALED>
+constexpr bool kFold = (SD == 4 && !SCALED);
+
+// Products per matrix-core dot for the error bound.
+template <int SD, bool SCALED>
+constexpr int kTerms = SCALED ? 2 * SD : (kFold<SD, SCALED> ? SD + 1 : SD);
+
+template <bool BF16>
+constexpr uint16_t kInfBits = BF16 ? 0x7F80 : 0x7C00;
+template <bool BF16>
+constexpr uint32_t kOnePair = BF16 ? 0x3F803F80u : 0x3C003C00u;  // (1, 1)
+
 // Matrix-core operands: 4 halves per lane (K = 8), or 8 (K = 16) for the
 // smoothed sub_dim 8 path.
 template <int SD, bool SCALED>
@@ -107,6 +122,34 @@ __device__ __forceinline__ uint16_t narrow(float v) {
   } else {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
   }
+}
+
+// C = hi + lo with hi = rn(C) and lo = C - hi rounded toward -inf (C - hi is
+// exact), so hi + lo <= C and the folded bound stays a lower bound.  False
+// when hi overflows the element type.
+template <bool BF16>
+__device__ __forceinline__ bool split_down(float c, uint16_t &hi, uint16_t &lo) {
+  if (c == __builtin_inff()) {
+    hi = kInfBits<BF16>;
+    lo = 0;
+    return true;
+  }
+  hi = narrow<BF16>(c);
+  const float hf = widen<BF16>(hi);
+  if (!(__builtin_fabsf(hf) <= kFltMax)) return false;
+  const float r = c - hf;
+  uint16_t l = narrow<BF16>(r);
+  if (widen<BF16>(l) > r) {  // one step toward -inf
+    if ((l & 0x7FFFu) == 0) {
+      l = 0x8001u;            // -(smallest subnormal)
+    } else if (l & 0x8000u) {
+      l = static_cast<uint16_t>(l + 1u);
+    } else {
+      l = static_cast<uint16_t>(l - 1u);
+    }
+  }
+  lo = l;
+  return true;
 }
 
 template <int SD>
@@ -186,6 +229,35 @@ __device__ __forceinline__ float min16(const f32x16 &v) {
   return fminf(fminf(a, v[14]), v[15]);
 }
 
+// The two lanes of a pair are l and l + 32 (h = 0, 1): they sit in the two
+// 32-lane halves of the wave.  v_permlane32_swap trades the upper half of one
+// register with the lower half of another on the VALU; with both operands
+// equal to v it gives, in every lane, v of the pair's lane 0 (first) and v
+// of its lane 1 (second), without the LDS round trip of a ds_bpermute.
+struct PairVals {
+  uint32_t first, second;
+};
+__device__ __forceinline__ PairVals pair_vals(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return {static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1])};
+}
+// v of the other lane of the pair
+__device__ __forceinline__ uint32_t pair_other(uint32_t v, int h) {
+  const PairVals p = pair_vals(v);
+  return h ? p.first : p.second;
+}
+__device__ __forceinline__ float pair_other(float v, int h) {
+  return __builtin_bit_cast(float, pair_other(__builtin_bit_cast(uint32_t, v), h));
+}
+__device__ __forceinline__ int pair_other(int v, int h) {
+  return static_cast<int>(pair_other(static_cast<uint32_t>(v), h));
+}
+// v(lane 0) + v(lane 1), the same value in both lanes
+__device__ __forceinline__ float pair_sum(float v) {
+  const PairVals p = pair_vals(__builtin_bit_cast(uint32_t, v));
+  return __builtin_bit_cast(float, p.first) + __builtin_bit_cast(float, p.second);
+}
+
 // Per-workgroup LDS (dynamic) for one codebook slot of n_c centroids, padded
 // to n_cpad = roundup(n_c, 32):
 //   rows [n_cpad] uint4     A operand: halves 0..7 = -c_0 .. -c_{SD-1}, zero
@@ -246,17 +318,17 @@ __device__ __forceinline__ void centroid(const Lds<SD, ROWS32> &s, int c, float 
 // Stage one codebook slot (and, for smoothed keys, its channel factors).
 // Returns true when some centroid has a non-finite or huge norm: then every
 // sub-vector of the slot takes the full exact scan.
-template <int SD, int NT, bool BF16, bool ROWS32, int BLOCK>
+template <int SD, int NT, bool BF16, bool ROWS32, int BLOCK, bool FOLD>
 __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_cpad,
                                const Lds<SD, ROWS32> &s, int hash_slots,
-                               const float *__restrict__ scale, int scale_len) {
+                               const float *__restrict__ scale, int scale_len, bool &fold_ok) {
   using K = Consts<SD, NT>;
   const int tid = threadIdx.x;
   for (int i = tid; i < hash_slots; i += BLOCK) s.hash[i] = -1;
   for (int i = tid; i < n_cpad / 16; i += BLOCK) s.gan[i] = 0.0f;
   for (int i = tid; i < scale_len; i += BLOCK) s.scale[i] = scale ? scale[i] : 1.0f;
   __syncthreads();
-  int flag = 0;
+  int flag = 0, nofold = 0;
   for (int r = tid; r < n_cpad; r += BLOCK) {
     uint16_t k8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float v[SD];
@@ -284,6 +356,9 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
         atomicMax(reinterpret_cast<int *>(&s.gan[group_of(r)]), __float_as_int(an));
       }
     }
+    if constexpr (FOLD) {  // halves 4, 5 carry C (SD == 4)
+      if (!split_down<BF16>(cv, k8[4], k8[5])) nofold = 1;
+    }
     s.rows[r] = make_uint4(k8[0] | (static_cast<uint32_t>(k8[1]) << 16),
                            k8[2] | (static_cast<uint32_t>(k8[3]) << 16),
                            k8[4] | (static_cast<uint32_t>(k8[5]) << 16),
@@ -297,6 +372,7 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
     }
   }
   const bool exact = __syncthreads_or(flag) != 0;
+  fold_ok = FOLD && __syncthreads_or(nofold) == 0;
   if (!exact) {
     // A row bit-identical to an earlier row can never win the strict-< scan.
     // Open addressing, at most half full: each distinct row value keeps the
@@ -329,7 +405,10 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
         }
         slot = (slot + 1) & mask;
       }
-      if (first < r) s.cval[r] = __builtin_inff();
+      if (first < r) {
+        s.cval[r] = __builtin_inff();
+        if constexpr (FOLD) s.rows[r].z = kInfBits<BF16>;  // C_hi = +inf, C_lo = 0
+      }
     }
     __syncthreads();
   }
@@ -357,9 +436,9 @@ __device__ __forceinline__ void exact4(const Lds<SD, ROWS32> &s, const float (&x
 
 // Combine (distance, index) over the two lanes of a pair: smaller distance,
 // then lower index.
-__device__ __forceinline__ void pair_min(float &best, int &bi) {
-  const float ob = __shfl_xor(best, 32);
-  const int oi = __shfl_xor(bi, 32);
+__device__ __forceinline__ void pair_min(float &best, int &bi, int h) {
+  const float ob = pair_other(best, h);
+  const int oi = pair_other(bi, h);
   const bool take = ob < best || (ob == best && oi < bi);
   best = take ? ob : best;
   bi = take ? oi : bi;
@@ -368,7 +447,7 @@ __device__ __forceinline__ void pair_min(float &best, int &bi) {
 // The full sub-vector of a column from the two halves held by the pair.
 template <int SD, bool BF16>
 __device__ __forceinline__ void column_x(const uint2 &own, int h, float (&xv)[SD]) {
-  const uint2 o = make_uint2(__shfl_xor(own.x, 32), __shfl_xor(own.y, 32));
+  const uint2 o = make_uint2(pair_other(own.x, h), pair_other(own.y, h));
   uint32_t w[4];
   const uint2 lo = (h == 0) ? own : o;
   w[0] = lo.x;
@@ -405,9 +484,9 @@ struct Smooth {
 // One tile: every wave encodes T columns of 32 sub-vectors.
 template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
 __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64_t gend, int n_c,
-                            int n_cpad, const Lds<SD, ROWS32> &s, bool exact_tile,
+                            int n_cpad, const Lds<SD, ROWS32> &s, bool exact_tile, bool fold,
                             const Smooth sm, int code_bits, uint8_t *__restrict__ out) {
-  using K = Consts<SD, SCALED ? 2 * SD : SD>;
+  using K = Consts<SD, kTerms<SD, SCALED>>;
   using OpT = Op<SD, SCALED>;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -493,11 +572,11 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
 #pragma unroll
       for (int q = 0; q < E / 2; ++q) {
         keep[q] = (h == 0) ? hw[q] : lw[q];
-        got[q] = static_cast<uint32_t>(__shfl_xor(static_cast<int>((h == 0) ? lw[q] : hw[q]), 32));
+        got[q] = pair_other((h == 0) ? lw[q] : hw[q], h);
       }
-      nv2 = nv2 + __shfl_xor(nv2, 32);
-      esum = esum + __shfl_xor(esum, 32);
-      fin = fin && (__shfl_xor(fin ? 1 : 0, 32) != 0);
+      nv2 = pair_sum(nv2);
+      esum = pair_sum(esum);
+      fin = fin && (pair_other(fin ? 1u : 0u, h) != 0u);
       const bool ex = !fin || !(nv2 <= kNormCap) || exact_tile;
       full_bits |= (ex ? 1u : 0u) << t;
       bn[t] = ex ? 0.0f
@@ -522,7 +601,9 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
       full_bits |= (ex ? 1u : 0u) << t;
       bn[t] = ex ? 0.0f : __builtin_sqrtf(n2x) * kNormUp;
       if constexpr (SD == 4) {
-        bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(0, 0);
+        // folded slots: the h = 1 half multiplies C_hi, C_lo by (1, 1)
+        bop[t] = (h == 0) ? make_uint2(w[0], w[1])
+                          : make_uint2(fold ? kOnePair<BF16> : 0u, 0u);
       } else {
         bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(w[2], w[3]);
       }
@@ -556,11 +637,15 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
     return cop;
   };
 
+  // accumulator input of block blk: C from LDS, or zero when C is folded
+  const f32x16 zero16 = {};
+
   // ---- stage 1: group lower bounds on the matrix cores ---------------------
-  if (!exact_tile) {
+  auto stage1 = [&](auto folded) {
+    constexpr bool F = decltype(folded)::value;
     for (int blk = 0; blk < nblk; ++blk) {
       const OpT aop = a_operand(blk);
-      const f32x16 cop = c_operand(blk);
+      const f32x16 cop = F ? zero16 : c_operand(blk);
       const float an = s.gan[2 * blk + h];
       const int grp = 2 * blk + h;
 #pragma unroll
@@ -570,6 +655,13 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
         g1[t] = (mb < m1[t]) ? grp : g1[t];
         m1[t] = __builtin_amdgcn_fmed3f(m1[t], mb, kNegMax);
       }
+    }
+  };
+  if (!exact_tile) {
+    if (kFold<SD, SCALED> && fold) {
+      stage1(std::true_type{});
+    } else {
+      stage1(std::false_type{});
     }
   }
 
@@ -592,9 +684,9 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
     } else {
       column_x<SD, BF16>(bop[t], h, xv);
     }
-    const float om1 = __shfl_xor(m1[t], 32);
-    const float om2 = __shfl_xor(m2[t], 32);
-    const int og1 = __shfl_xor(g1[t], 32);
+    const float om1 = pair_other(m1[t], h);
+    const float om2 = pair_other(m2[t], h);
+    const int og1 = pair_other(g1[t], h);
     const bool mine = m1[t] < om1;
     const bool theirs = om1 < m1[t];
     const int cg1 = mine ? g1[t] : (theirs ? og1 : min(g1[t], og1));
@@ -611,7 +703,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
       exact4<SD, BF16, ROWS32, false>(s, xv, c0, n_c, best, bi);
       exact4<SD, BF16, ROWS32, false>(s, xv, c0 + 8, n_c, best, bi);
     }
-    pair_min(best, bi);
+    pair_min(best, bi, h);
     float n2x;
     if constexpr (SCALED) {
       n2x = xv[0] * xv[0];
@@ -635,7 +727,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
       int fi = 0x7fffffff;
       for (int blk = 0; blk < nblk; ++blk) {
         const OpT aop = a_operand(blk);
-        const f32x16 cop = c_operand(blk);
+        const f32x16 cop = (kFold<SD, SCALED> && fold) ? zero16 : c_operand(blk);
         const float an = s.gan[2 * blk + h];
         const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
         if (amb && mb <= U) {
@@ -644,7 +736,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
           for (int j = 0; j < 4; ++j) exact4<SD, BF16, ROWS32>(s, xv, r0 + 8 * j, n_c, fb, fi);
         }
       }
-      pair_min(fb, fi);
+      pair_min(fb, fi, h);
       best = amb ? fb : best;
       bi = amb ? fi : bi;
     }
@@ -663,7 +755,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
         fb = lt ? d : fb;
         fi = lt ? c : fi;
       }
-      pair_min(fb, fi);
+      pair_min(fb, fi, h);
       best = full ? fb : best;
       bi = full ? fi : bi;
     }
@@ -722,7 +814,7 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
   const int64_t first = static_cast<int64_t>(blockIdx.x) * tiles_per_wg;
   const int64_t last = min(first + tiles_per_wg, total_tiles);
   int64_t staged = -1;
-  bool exact_tile = false;
+  bool exact_tile = false, fold = false;
   for (int64_t tile = first; tile < last; ++tile) {
     const int64_t g = tile / tiles_per_group;
     const int64_t gstart = g * group_len;
@@ -745,13 +837,13 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     }
     if (slot != staged) {
       __syncthreads();  // every wave is done with the previous slot
-      exact_tile = stage_codebook<SD, SCALED ? 2 * SD : SD, BF16, ROWS32, BLOCK>(
+      exact_tile = stage_codebook<SD, kTerms<SD, SCALED>, BF16, ROWS32, BLOCK, kFold<SD, SCALED>>(
           codebook + slot * cb_stride, n_c, n_cpad, s, hash_slots,
-          (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len);
+          (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len, fold);
       staged = slot;
     }
     encode_tile<SD, T, BLOCK, BF16, ROWS32, SCALED>(x, tbase, gend, n_c, n_cpad, s, exact_tile,
-                                                    sm, code_bits, out);
+                                                    fold, sm, code_bits, out);
   }
 }
 

@@ -200,8 +200,12 @@ vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
  *           vq_encode_packed); v_t likewise from C_v without factors
  *     out[b][hq] = sum_t softmax_t(softmax_scale * q[b][hq] . k_t) v_t
  * (0 for a sequence with no attended token).  A code >= n_centroids decodes
- * to a zero row.  Arithmetic: fp32 (q / f and the LUT in fp32, base-2
- * softmax); the error bound the tests hold it to is stated with them.
+ * to a zero row.  Arithmetic: q / f in fp32, base-2 softmax in fp32.  For
+ * head_dim 64, 128 or 256 with at least 16 codes per key and value row and
+ * 16-byte aligned code arrays, scores and the value sum run on the matrix
+ * cores with the fp32 query and weights split exactly into element-type parts
+ * (products exact, fp32 accumulation); other shapes build a per-query fp32
+ * lookup table.  The error bound the tests hold both to is stated with them.
  *
  *   q           device, [batch][n_q_heads][head_dim] of `dtype`, 2-aligned.
  *   k_codes     device, [batch][n_kv_heads][max_kv_len][head_dim/k_sub_dim]

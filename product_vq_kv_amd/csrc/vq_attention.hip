@@ -328,7 +328,503 @@ attn_partial(const AttnArgs a) {
   }
 }
 
-// Merge the chunk partials of one (sequence, query head): thread d.
+// ---------------------------------------------------------------------------
+// Matrix-core form (head_dim 128 or 256, 16-byte aligned code rows): the
+// scores of 16 tokens for up to 16 rows of query parts are one
+// v_mfma_f32_16x16x32 per 32 elements of the head dimension:
+//   rows     (query head, part): the query q~ = q / f * scale * log2(e),
+//            multiplied by 2^E (E per head, max |q~| 2^E in [2^13, 2^14)),
+//            is split exactly into element-type parts, q~ 2^E = sum of parts
+//            + e with |e| <= 2^-22 |q~ 2^E| + 2^-25 (fp16: hi, lo; bf16: four
+//            parts, |e| <= 2^-32 |q~ 2^E|);
+//   columns  16 tokens; the B operand of lane (token, quarter) is the key
+//            codebook rows of its codes, gathered from LDS;
+//   score    = 2^-E (sum of the head's part rows).
+// Products of element-type values are exact in fp32 and the instruction's
+// accumulation errs by less than 4 u (sum |terms| + |C|) (measured), so the
+// score error stays below (4 head_dim/32 + 3) u sum_i |q_i k_i| -- inside the
+// bound of the LUT form.  Each wave scores 64 tokens of the 256-token chunk;
+// after one barrier the chunk maximum is known and the weights go to LDS;
+// for the value sum every wave takes a quarter of the value sub-spaces over
+// all 256 tokens, so its results go straight to the partial with no
+// reduction across waves.
+constexpr int kWaveTok = 64;
+constexpr int kMChunk = kWaveTok * (kThreads / 64);  // 256 tokens per workgroup
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16(const uint4 &a, const uint4 &b, const f32x4 &c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Round a finite fp32 value to the element type (nearest, ties to even).
+template <bool BF16>
+__device__ __forceinline__ uint16_t narrow_rn(float v) {
+  if constexpr (BF16) {
+    const uint32_t u = __float_as_uint(v);
+    if (!(__builtin_fabsf(v) <= 3.4028234663852886e38f))
+      return static_cast<uint16_t>((u >> 16) | ((v != v) ? 0x40u : 0u));
+    return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  } else {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Max / sum over the 16 lanes of a DPP row (xor 1, xor 2, half mirror,
+// mirror); every lane of the row ends with the same value.
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  return fmaxf(v, dpp_f<0x140>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v = v + dpp_f<0xB1>(v);
+  v = v + dpp_f<0x4E>(v);
+  v = v + dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
+
+template <int SDK, int SDV, bool BF16, int D>
+struct MLayout {
+  static constexpr int kNSK = D / SDK, kNSV = D / SDV;
+  static constexpr int kParts = BF16 ? 4 : 2;  // element-type parts of a split fp32 value
+  static constexpr int kHeadsPerBlock = 16 / kParts;
+  static constexpr size_t kKTab = 256 * SDK * 2;  // key codebook, element bits
+  static constexpr size_t kVTab = 256 * SDV * 2;  // value codebook, element bits
+  static constexpr size_t kCodes = static_cast<size_t>(kMChunk) * kNSV;  // value codes
+  // value sums of the token groups > 0 (head_dim < 4 * 16 * SDV), after the codes
+  static constexpr int kTokGroups = 4 / (kNSV / 16);
+  __host__ __device__ static size_t region(int g) {
+    const size_t red = static_cast<size_t>(kTokGroups - 1) * g * D * 4;
+    return red > kCodes ? red : kCodes;
+  }
+  // ktab | vtab | qp [g * kParts][D] u16 | codes / reduction | pp [g * kParts][256] u16
+  // | qexp [8] i32 | chunk maxima [8] | wave maxima [4][8] | wave sums [4][8]
+  __host__ __device__ static size_t qp_off() { return kKTab + kVTab; }
+  __host__ __device__ static size_t codes_off(int g) {
+    return qp_off() + static_cast<size_t>(g) * kParts * D * 2;
+  }
+  __host__ __device__ static size_t pp_off(int g) { return codes_off(g) + region(g); }
+  __host__ __device__ static size_t small_off(int g) {
+    return pp_off(g) + static_cast<size_t>(g) * kParts * kMChunk * 2;
+  }
+  __host__ __device__ static size_t bytes(int g) {
+    return small_off(g) + 4 * (2 * kMaxGroup + 2 * 4 * kMaxGroup);
+  }
+};
+
+// Elements e of the rows r[0..7] (each row SDV element-type values in SDV/2
+// words) as the 8 K values of a B operand: word m = (r[2m][e], r[2m+1][e]).
+template <int SDV>
+__device__ __forceinline__ uint4 column_of(const uint32_t (&r)[8][SDV / 2], int e) {
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+  uint32_t o[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    o[m] = __builtin_amdgcn_perm(r[2 * m + 1][e >> 1], r[2 * m][e >> 1], sel);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <int SDK, int SDV, bool BF16, int D>
+__global__ void __launch_bounds__(kThreads)
+attn_mfma_partial(const AttnArgs a) {
+  using LY = MLayout<SDK, SDV, BF16, D>;
+  constexpr int NSK = LY::kNSK, NSV = LY::kNSV;
+  constexpr int QB = NSK / 4;          // key-code bytes per lane quarter (4, 8 or 16)
+  constexpr int NQW = QB / 4;          // their 32-bit words
+  constexpr int NI = D / 32;           // score instructions per 16 tokens
+  constexpr int P = LY::kParts;
+  constexpr int GB = LY::kHeadsPerBlock;
+  constexpr int HPL = 4 / P;           // heads per lane in the output layout
+  constexpr int VP = NSV / 16;         // 16-byte value-code pieces per thread
+  constexpr int WG = NSV / 16;         // waves covering all value sub-spaces (16 each)
+  constexpr int TG = LY::kTokGroups;   // token groups of the value sum
+  constexpr int TOKW = kMChunk / TG;   // tokens per wave in the value sum
+  static_assert(QB % 4 == 0 && NSV % 16 == 0 && WG * TG == 4, "shape");
+  constexpr float kPScale = 16384.0f;  // weights in (0, 1] are split as p 2^14
+
+  extern __shared__ float4 lds4[];
+  uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
+  const int g = a.Hq / a.Hkv;
+  const int nb = (g + GB - 1) / GB;
+  const int nrows = g * P;             // rows (head, part) in use
+  uint16_t *ktab = reinterpret_cast<uint16_t *>(lds);
+  uint16_t *vtab = reinterpret_cast<uint16_t *>(lds + LY::kKTab);
+  uint16_t *qp = reinterpret_cast<uint16_t *>(lds + LY::qp_off());
+  uint8_t *codes = lds + LY::codes_off(g);
+  float *red = reinterpret_cast<float *>(codes);  // after the value sum
+  uint16_t *pp = reinterpret_cast<uint16_t *>(lds + LY::pp_off(g));
+  int *qexp = reinterpret_cast<int *>(lds + LY::small_off(g));  // E of each head
+  float *cmax = reinterpret_cast<float *>(qexp + kMaxGroup);      // chunk maximum per head
+  float *wmax = cmax + kMaxGroup;                                  // [4][kMaxGroup]
+  float *wsum = wmax + 4 * kMaxGroup;                              // [4][kMaxGroup]
+
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int L = a.kv_len ? a.kv_len[b] : a.S;
+  L = min(max(L, 0), a.S);
+  const int first = a.window > 0 ? max(0, L - a.window) : 0;
+  const int t0 = chunk * kMChunk;
+  const int lo = max(first, t0), hi = min(L, t0 + kMChunk);
+  const int64_t part_stride = D + 2;
+  const int64_t head_stride = static_cast<int64_t>(a.n_chunks) * part_stride;
+  float *part = a.ws + ((static_cast<int64_t>(b) * a.Hq + h * g) * a.n_chunks + chunk) * part_stride;
+  if (lo >= hi) {  // nothing attended here (uniform)
+    for (int j = 0; j < g; ++j) {
+      float *pj = part + j * head_stride;
+      for (int d = tid; d < D; d += kThreads) pj[d] = 0.0f;
+      if (tid == 0) {
+        pj[D] = kNegInf;
+        pj[D + 1] = 0.0f;
+      }
+    }
+    return;
+  }
+
+  // ---- every global load is issued here, in the order it is needed: the
+  // codebooks, the query rows, then the codes (clamped token indices) --------
+  const int n_c = a.n_c;
+  const uint16_t *kcb = a.k_cb + static_cast<int64_t>(h) * n_c * SDK;
+  const uint16_t *vcb = a.v_cb + static_cast<int64_t>(h) * n_c * SDV;
+  uint16_t kv[SDK], vv[SDV];
+#pragma unroll
+  for (int k = 0; k < SDK; ++k) kv[k] = kcb[min(tid + kThreads * k, n_c * SDK - 1)];
+#pragma unroll
+  for (int k = 0; k < SDV; ++k) vv[k] = vcb[min(tid + kThreads * k, n_c * SDV - 1)];
+  // query head slots w and w + 4 of this wave (slot < g), elements lane + 64 k
+  uint16_t qv[2][D / 64];
+  float ks[D / 64];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int hq = h * g + min(w + 4 * j, g - 1);
+    const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.Hq + hq) * D;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) qv[j][k] = qrow[lane + 64 * k];
+  }
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k)
+    ks[k] = a.k_scale ? a.k_scale[static_cast<int64_t>(h) * D + lane + 64 * k] : 1.0f;
+
+  const int64_t row0 = (static_cast<int64_t>(b) * a.Hkv + h) * a.S;
+  const uint8_t *kc = a.k_codes + row0 * NSK;
+  const uint8_t *vc = a.v_codes + row0 * NSV;
+  const int col = lane & 15, kg = lane >> 4;
+  uint32_t kw[4][NQW];  // key codes: quarter kg of token t0 + 64 w + 16 G + col
+#pragma unroll
+  for (int G = 0; G < 4; ++G) {
+    const int t = min(max(t0 + w * kWaveTok + 16 * G + col, lo), hi - 1);
+    const uint8_t *src = kc + static_cast<int64_t>(t) * NSK + kg * QB;
+    if constexpr (NQW == 4) {
+      const uint4 q = *reinterpret_cast<const uint4 *>(src);
+      kw[G][0] = q.x;
+      kw[G][1] = q.y;
+      kw[G][2] = q.z;
+      kw[G][3] = q.w;
+    } else if constexpr (NQW == 2) {
+      const uint2 q = *reinterpret_cast<const uint2 *>(src);
+      kw[G][0] = q.x;
+      kw[G][1] = q.y;
+    } else {
+      kw[G][0] = *reinterpret_cast<const uint32_t *>(src);
+    }
+  }
+  uint4 vw[VP];  // value codes of the chunk, 16-byte pieces
+#pragma unroll
+  for (int k = 0; k < VP; ++k) {
+    const int e = tid + kThreads * k;
+    const int tc = e / VP, pc = e % VP;
+    const int t = min(max(t0 + tc, lo), hi - 1);
+    vw[k] = *reinterpret_cast<const uint4 *>(vc + static_cast<int64_t>(t) * NSV + 16 * pc);
+  }
+
+  // ---- codebooks of kv head h into LDS (rows past n_c are zero) -------------
+#pragma unroll
+  for (int k = 0; k < SDK; ++k) {
+    const int e = tid + kThreads * k;
+    ktab[e] = (e < n_c * SDK) ? kv[k] : static_cast<uint16_t>(0);
+  }
+#pragma unroll
+  for (int k = 0; k < SDV; ++k) {
+    const int e = tid + kThreads * k;
+    vtab[e] = (e < n_c * SDV) ? vv[k] : static_cast<uint16_t>(0);
+  }
+  // value codes to LDS
+#pragma unroll
+  for (int k = 0; k < VP; ++k) {
+    const int e = tid + kThreads * k;
+    *reinterpret_cast<uint4 *>(codes + 16 * e) = vw[k];
+  }
+
+  // ---- query parts: wave w splits heads w and w + 4 into rows h P + part ----
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int hs = w + 4 * j;
+    if (hs < g) {  // uniform per wave
+      uint16_t *rows = qp + static_cast<int64_t>(hs) * P * D;
+      float x[D / 64];
+      float mx = 0.0f;
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) {
+        float v = widen<BF16>(qv[j][k]);
+        if (a.k_scale) v = v / ks[k];
+        v = v * a.qmul;
+        x[k] = v;
+        mx = fmaxf(mx, __builtin_fabsf(v));
+      }
+      mx = row_max16(mx);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      int E = 0;
+      if (mx > 0.0f && mx <= 3.4028234663852886e38f) {
+        int ex;
+        (void)frexpf(mx, &ex);  // mx = f 2^ex, f in [0.5, 1)
+        E = 14 - ex;            // max |q~| 2^E in [2^13, 2^14)
+      }
+      if (lane == 0) qexp[hs] = E;
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) {
+        const int d = lane + 64 * k;
+        float r = ldexpf(x[k], E);
+#pragma unroll
+        for (int q = 0; q < P; ++q) {  // r - part is exact in fp32
+          const uint16_t pb = narrow_rn<BF16>(r);
+          rows[q * D + d] = pb;
+          r = r - widen<BF16>(pb);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- scores on the matrix cores: wave w, tokens t0 + 64 w + 16 G + col ----
+  // lane (col, kg): A = row col of a block at elements kg D/4 + 8 i .. + 7
+  // (rows past g P are zero); B = the key rows of its codes for the same
+  // elements; the result rows 4 kg .. 4 kg + 3 are (head, part) rows
+  float sreg[2][4][HPL];  // blocks x groups x heads of the lane (bf16: 2 blocks)
+  const uint2 *ktab2 = reinterpret_cast<const uint2 *>(ktab);
+  const uint4 *ktab4 = reinterpret_cast<const uint4 *>(ktab);
+#pragma unroll
+  for (int hb = 0; hb < (BF16 ? 2 : 1); ++hb) {
+    if (hb < nb) {  // uniform
+      const int ar = hb * 16 + col;
+      const uint16_t *arow = qp + static_cast<int64_t>(min(ar, nrows - 1)) * D + kg * (D / 4);
+      uint4 areg[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(arow + 8 * i);
+        areg[i] = ar < nrows ? v : make_uint4(0, 0, 0, 0);
+      }
+      int ex[HPL];
+#pragma unroll
+      for (int j = 0; j < HPL; ++j) ex[j] = qexp[min(hb * GB + kg * HPL + j, kMaxGroup - 1)];
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          uint4 bop;
+          if constexpr (SDK == 4) {
+            const uint32_t wd = kw[G][i >> 1];
+            const uint32_t c0 = (wd >> (16 * (i & 1))) & 0xFFu;
+            const uint32_t c1 = (wd >> (16 * (i & 1) + 8)) & 0xFFu;
+            const uint2 r0 = ktab2[c0], r1 = ktab2[c1];
+            bop = make_uint4(r0.x, r0.y, r1.x, r1.y);
+          } else {
+            const uint32_t c = (kw[G][i >> 2] >> (8 * (i & 3))) & 0xFFu;
+            bop = ktab4[c];
+          }
+          acc = mfma16<BF16>(areg[i], bop, acc);
+        }
+        const int t = t0 + w * kWaveTok + 16 * G + col;
+        const bool valid = t >= lo && t < hi;
+        if constexpr (P == 2) {
+          sreg[hb][G][0] = valid ? ldexpf(acc[0] + acc[1], -ex[0]) : kNegInf;
+          sreg[hb][G][1] = valid ? ldexpf(acc[2] + acc[3], -ex[1]) : kNegInf;
+        } else {
+          sreg[hb][G][0] = valid ? ldexpf(((acc[3] + acc[2]) + acc[1]) + acc[0], -ex[0]) : kNegInf;
+        }
+      }
+      // this wave's maximum per head
+#pragma unroll
+      for (int j = 0; j < HPL; ++j) {
+        float m = kNegInf;
+#pragma unroll
+        for (int G = 0; G < 4; ++G) m = fmaxf(m, sreg[hb][G][j]);
+        m = row_max16(m);
+        const int hh = hb * GB + kg * HPL + j;
+        if (col == 0 && hh < g) wmax[w * kMaxGroup + hh] = m;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- weights against the chunk maximum, stored split: rows h P + part of
+  // pp hold the element-type parts of p 2^14 -----------------------------------
+#pragma unroll
+  for (int hb = 0; hb < (BF16 ? 2 : 1); ++hb) {
+    if (hb < nb) {
+#pragma unroll
+      for (int j = 0; j < HPL; ++j) {
+        const int hh = hb * GB + kg * HPL + j;
+        const int hc = min(hh, g - 1);
+        float M = wmax[hc];
+#pragma unroll
+        for (int v = 1; v < 4; ++v) M = fmaxf(M, wmax[v * kMaxGroup + hc]);
+        float lsum = 0.0f;
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+          const float sv = sreg[hb][G][j];
+          const float pv = (sv == kNegInf) ? 0.0f : exp2f(sv - M);
+          lsum += pv;
+          if (hh < g) {
+            const int tc = w * kWaveTok + 16 * G + col;
+            float r = pv * kPScale;
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+              const uint16_t pb = narrow_rn<BF16>(r);
+              pp[(hh * P + q) * kMChunk + tc] = pb;
+              r = r - widen<BF16>(pb);
+            }
+          }
+        }
+        lsum = row_sum16(lsum);
+        if (col == 0 && hh < g) wsum[w * kMaxGroup + hh] = lsum;
+        if (w == 0 && col == 0 && hh < g) cmax[hh] = M;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- value sum on the matrix cores: wave w takes sub-spaces 16 (w % WG)
+  // .. + 15 (columns) over tokens (w / WG) TOKW .. + TOKW - 1 (K), one
+  // instruction per value element; lane (col, kg) gathers the rows of its
+  // sub-space for 8 tokens and regroups them by element --------------------
+  const int sb = w % WG, tg = w / WG;
+  const int sv = sb * 16 + col;
+  f32x4 vacc[2][SDV];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int e = 0; e < SDV; ++e) vacc[hb][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+  for (int blk = 0; blk < TOKW / 32; ++blk) {
+    const int tk = tg * TOKW + blk * 32 + kg * 8;  // this lane's 8 tokens
+    uint32_t rw[8][SDV / 2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t c = codes[(tk + j) * NSV + sv];
+      if constexpr (SDV == 4) {
+        const uint2 r = reinterpret_cast<const uint2 *>(vtab)[c];
+        rw[j][0] = r.x;
+        rw[j][1] = r.y;
+      } else {
+        const uint4 r = reinterpret_cast<const uint4 *>(vtab)[c];
+        rw[j][0] = r.x;
+        rw[j][1] = r.y;
+        rw[j][2] = r.z;
+        rw[j][3] = r.w;
+      }
+    }
+#pragma unroll
+    for (int hb = 0; hb < (BF16 ? 2 : 1); ++hb) {
+      if (hb < nb) {
+        const int ar = hb * 16 + col;
+        const uint4 av = *reinterpret_cast<const uint4 *>(pp + min(ar, nrows - 1) * kMChunk + tk);
+        const uint4 aop = ar < nrows ? av : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < SDV; ++e)
+          vacc[hb][e] = mfma16<BF16>(aop, column_of<SDV>(rw, e), vacc[hb][e]);
+      }
+    }
+  }
+  // rows 4 kg .. 4 kg + 3 of column col: the (head, part) rows of heads
+  // hb GB + kg HPL + j, element e of sub-space sv
+  float o[2][HPL][SDV];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int e = 0; e < SDV; ++e) {
+      const f32x4 v = vacc[hb][e];
+      if constexpr (P == 2) {
+        o[hb][0][e] = (v[0] + v[1]) * (1.0f / kPScale);
+        o[hb][1][e] = (v[2] + v[3]) * (1.0f / kPScale);
+      } else {
+        o[hb][0][e] = (((v[3] + v[2]) + v[1]) + v[0]) * (1.0f / kPScale);
+      }
+    }
+  if constexpr (TG > 1) {
+    // token groups 1 .. TG-1 hand their sums to group 0 through LDS
+    __syncthreads();  // every wave is done with the codes
+    if (tg > 0) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < HPL; ++j) {
+          const int hh = hb * GB + kg * HPL + j;
+          if (hb < nb && hh < g) {
+#pragma unroll
+            for (int e = 0; e < SDV; ++e) red[((tg - 1) * g + hh) * D + sv * SDV + e] = o[hb][j][e];
+          }
+        }
+    }
+    __syncthreads();
+    if (tg == 0) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < HPL; ++j) {
+          const int hh = hb * GB + kg * HPL + j;
+          if (hb < nb && hh < g) {
+#pragma unroll
+            for (int e = 0; e < SDV; ++e)
+              for (int q = 1; q < TG; ++q) o[hb][j][e] += red[((q - 1) * g + hh) * D + sv * SDV + e];
+          }
+        }
+    }
+  }
+  if (tg == 0) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int j = 0; j < HPL; ++j) {
+        const int hh = hb * GB + kg * HPL + j;
+        if (hb < nb && hh < g) {
+          float *dst = part + hh * head_stride + sv * SDV;
+#pragma unroll
+          for (int q4 = 0; q4 < SDV / 4; ++q4)
+            reinterpret_cast<float4 *>(dst)[q4] =
+                make_float4(o[hb][j][4 * q4], o[hb][j][4 * q4 + 1], o[hb][j][4 * q4 + 2],
+                            o[hb][j][4 * q4 + 3]);
+        }
+      }
+  }
+  if (tid < g) {
+    float *pj = part + tid * head_stride;
+    const float l = ((wsum[tid] + wsum[kMaxGroup + tid]) + wsum[2 * kMaxGroup + tid]) +
+                    wsum[3 * kMaxGroup + tid];
+    pj[D] = cmax[tid];
+    pj[D + 1] = l;
+  }
+}
+
+// Merge the chunk partials of one (sequence, query head): thread d.  The
+// chunk loop is unrolled so the loads of several chunks are in flight.
 __global__ void __launch_bounds__(kThreads)
 attn_combine(const AttnArgs a) {
   const int bh = blockIdx.x;
@@ -336,15 +832,16 @@ attn_combine(const AttnArgs a) {
   const int64_t part_stride = D + 2;
   const float *part = a.ws + static_cast<int64_t>(bh) * a.n_chunks * part_stride;
   float M = kNegInf;
+#pragma unroll 8
   for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, part[c * part_stride + D]);
   for (int d = threadIdx.x; d < D; d += kThreads) {
     float o = 0.0f;
     if (M != kNegInf) {
+      // an empty chunk has m = -inf (weight 0), l = 0 and o = 0
       float l = 0.0f, acc = 0.0f;
+#pragma unroll 8
       for (int c = 0; c < a.n_chunks; ++c) {
-        const float mc = part[c * part_stride + D];
-        if (mc == kNegInf) continue;
-        const float w = exp2f(mc - M);
+        const float w = exp2f(part[c * part_stride + D] - M);
         l = __builtin_fmaf(part[c * part_stride + D + 1], w, l);
         acc = __builtin_fmaf(part[c * part_stride + d], w, acc);
       }
@@ -355,7 +852,7 @@ attn_combine(const AttnArgs a) {
 }
 
 template <int SDK, int SDV, bool BF16>
-hipError_t launch_attn_t(const AttnArgs &a, hipStream_t stream) {
+hipError_t launch_attn_t(AttnArgs a, hipStream_t stream) {
   const int g = a.Hq / a.Hkv;
   const size_t lds = attn_lds_bytes<SDK, SDV>(a.D, g);
   auto kern = attn_partial<SDK, SDV, BF16>;
@@ -365,6 +862,7 @@ hipError_t launch_attn_t(const AttnArgs &a, hipStream_t stream) {
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
+  a.n_chunks = std::max(1, (a.S + kChunk - 1) / kChunk);
   hipLaunchKernelGGL(kern, dim3(a.n_chunks, a.Hkv, a.B), dim3(kThreads), lds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -372,17 +870,58 @@ hipError_t launch_attn_t(const AttnArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool BF16>
-hipError_t launch_attn_dt(const AttnArgs &a, int sdk, int sdv, hipStream_t stream) {
-  if (sdk == 4) {
-    return sdv == 4 ? launch_attn_t<4, 4, BF16>(a, stream) : launch_attn_t<4, 8, BF16>(a, stream);
+// The matrix-core form takes head_dim 64, 128 or 256 with 16 or more codes
+// per key and per value row.
+constexpr bool mfma_shape(int sdk, int sdv, int d) {
+  return (d == 64 || d == 128 || d == 256) && (d / sdk) % 16 == 0 && (d / sdv) % 16 == 0;
+}
+
+template <int SDK, int SDV, bool BF16, int D>
+hipError_t launch_attn_m(AttnArgs a, hipStream_t stream) {
+  if constexpr (!mfma_shape(SDK, SDV, D)) {
+    return hipErrorInvalidValue;
+  } else {
+    const int g = a.Hq / a.Hkv;
+    const size_t lds = MLayout<SDK, SDV, BF16, D>::bytes(g);
+    auto kern = attn_mfma_partial<SDK, SDV, BF16, D>;
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    a.n_chunks = std::max(1, (a.S + kMChunk - 1) / kMChunk);
+    hipLaunchKernelGGL(kern, dim3(a.n_chunks, a.Hkv, a.B), dim3(kThreads), lds, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_combine, dim3(a.B * a.Hq), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
   }
-  return sdv == 4 ? launch_attn_t<8, 4, BF16>(a, stream) : launch_attn_t<8, 8, BF16>(a, stream);
+}
+
+template <int SDK, int SDV, bool BF16>
+hipError_t launch_attn_d(const AttnArgs &a, bool mfma, hipStream_t stream) {
+  if (mfma) {
+    if (a.D == 256) return launch_attn_m<SDK, SDV, BF16, 256>(a, stream);
+    if (a.D == 128) return launch_attn_m<SDK, SDV, BF16, 128>(a, stream);
+    return launch_attn_m<SDK, SDV, BF16, 64>(a, stream);
+  }
+  return launch_attn_t<SDK, SDV, BF16>(a, stream);
+}
+
+template <bool BF16>
+hipError_t launch_attn_dt(const AttnArgs &a, int sdk, int sdv, bool mfma, hipStream_t stream) {
+  if (sdk == 4) {
+    return sdv == 4 ? launch_attn_d<4, 4, BF16>(a, mfma, stream)
+                    : launch_attn_d<4, 8, BF16>(a, mfma, stream);
+  }
+  return sdv == 4 ? launch_attn_d<8, 4, BF16>(a, mfma, stream)
+                  : launch_attn_d<8, 8, BF16>(a, mfma, stream);
 }
 
 }  // namespace
 
-int attention_chunks(int max_kv_len) { return std::max(1, (max_kv_len + kChunk - 1) / kChunk); }
+int attention_chunks(int max_kv_len) { return std::max(1, (max_kv_len + kMChunk - 1) / kMChunk); }
 
 size_t attention_lds_bytes(int sdk, int sdv, int D, int g) {
   if (sdk == 4) return sdv == 4 ? attn_lds_bytes<4, 4>(D, g) : attn_lds_bytes<4, 8>(D, g);
@@ -407,10 +946,13 @@ hipError_t launch_attention(const AttnLayout &l, hipStream_t stream) {
   a.S = l.max_kv_len;
   a.n_c = l.n_centroids;
   a.window = l.window;
-  a.n_chunks = attention_chunks(l.max_kv_len);
+  a.n_chunks = 0;
   a.qmul = l.softmax_scale * 1.4426950408889634f;
-  return l.bf16 ? launch_attn_dt<true>(a, l.k_sub_dim, l.v_sub_dim, stream)
-                : launch_attn_dt<false>(a, l.k_sub_dim, l.v_sub_dim, stream);
+  const bool mfma = mfma_shape(l.k_sub_dim, l.v_sub_dim, l.head_dim) &&
+                    reinterpret_cast<uintptr_t>(l.k_codes) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(l.v_codes) % 16 == 0;
+  return l.bf16 ? launch_attn_dt<true>(a, l.k_sub_dim, l.v_sub_dim, mfma, stream)
+                : launch_attn_dt<false>(a, l.k_sub_dim, l.v_sub_dim, mfma, stream);
 }
 
 }  // namespace vqk

@@ -400,33 +400,25 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v + dpp_f<0x140>(v);
 }
 
-template <int SDK, int SDV, bool BF16, int D>
+// LDS of the matrix-core kernel for up to GC query heads per kv head.  All
+// of it is static: the value codes are the target of asynchronous copies, and
+// the compiler tells them apart from the other LDS objects only then.
+template <int SDK, int SDV, bool BF16, int D, int GC>
 struct MLayout {
   static constexpr int kNSK = D / SDK, kNSV = D / SDV;
   static constexpr int kParts = BF16 ? 4 : 2;  // element-type parts of a split fp32 value
   static constexpr int kHeadsPerBlock = 16 / kParts;
-  static constexpr size_t kKTab = 256 * SDK * 2;  // key codebook, element bits
-  static constexpr size_t kVTab = 256 * SDV * 2;  // value codebook, element bits
-  static constexpr size_t kCodes = static_cast<size_t>(kMChunk) * kNSV;  // value codes
-  // value sums of the token groups > 0 (head_dim < 4 * 16 * SDV), after the codes
-  static constexpr int kTokGroups = 4 / (kNSV / 16);
-  __host__ __device__ static size_t region(int g) {
-    const size_t red = static_cast<size_t>(kTokGroups - 1) * g * D * 4;
-    return red > kCodes ? red : kCodes;
-  }
-  // ktab | vtab | qp [g * kParts][D] u16 | codes / reduction | pp [g * kParts][256] u16
-  // | qexp [8] i32 | chunk maxima [8] | wave maxima [4][8] | wave sums [4][8]
-  __host__ __device__ static size_t qp_off() { return kKTab + kVTab; }
-  __host__ __device__ static size_t codes_off(int g) {
-    return qp_off() + static_cast<size_t>(g) * kParts * D * 2;
-  }
-  __host__ __device__ static size_t pp_off(int g) { return codes_off(g) + region(g); }
-  __host__ __device__ static size_t small_off(int g) {
-    return pp_off(g) + static_cast<size_t>(g) * kParts * kMChunk * 2;
-  }
-  __host__ __device__ static size_t bytes(int g) {
-    return small_off(g) + 4 * (2 * kMaxGroup + 2 * 4 * kMaxGroup);
-  }
+  static constexpr int kPieces = kNSV / 16;    // 16-byte pieces per value-code row
+  static constexpr int kTokGroups = 4 / kPieces;
+  // the value codes of the chunk, later the value sums of token groups > 0
+  // (head_dim < 4 * 16 * SDV)
+  static constexpr int kCodes = kMChunk * kNSV;
+  static constexpr int kRed = (kTokGroups - 1) * GC * D * 4;
+  static constexpr int kCodeBytes = kCodes > kRed ? kCodes : kRed;
+  // query parts [GC * kParts][D] (scores), then the weights [GC * kParts][256]
+  static constexpr int kRowElems = GC * kParts * (D > kMChunk ? D : kMChunk);
+  static constexpr size_t kBytes = 2 * 256 * (SDK + SDV) + 2 * kRowElems + kCodeBytes +
+                                   4 * (2 * kMaxGroup + 2 * 4 * kMaxGroup);
 };
 
 // Elements e of the rows r[0..7] (each row SDV element-type values in SDV/2
@@ -441,10 +433,36 @@ __device__ __forceinline__ uint4 column_of(const uint32_t (&r)[8][SDV / 2], int 
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-template <int SDK, int SDV, bool BF16, int D>
-__global__ void __launch_bounds__(kThreads)
+// Asynchronous copy of 16 bytes per lane from global memory to LDS
+// (global_load_lds_dwordx4): lane l of the wave writes lds + 16 l; `lds` is
+// the same for every lane.  The target is an LDS object of its own, so the
+// compiler does not make accesses to other LDS objects wait for the copy.
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// Waits until every vector memory operation of the wave has completed.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Value codes of a chunk in LDS, token-major; piece p (16 bytes) of token t
+// sits at position p ^ ((t / 8) mod VP) of its row, so that the rows of
+// tokens 8 apart, read together by the value sum, start on different banks.
+// Byte offset of the code of (token tc, sub-space s):
+template <int VP, int NSV>
+__device__ __forceinline__ int code_at(int tc, int s) {
+  return tc * NSV + (((s >> 4) ^ ((tc >> 3) & (VP - 1))) << 4) + (s & 15);
+}
+
+// Waves per SIMD the register budget is set for (6 fit the LDS of the common
+// fp16 shapes; the wider forms need more registers).
+template <int SDV_, bool BF16_, int GC_>
+constexpr int kMfmaWaves = BF16_ ? (SDV_ == 8 ? 3 : 4) : (SDV_ == 8 || GC_ == 8 ? 5 : 6);
+
+template <int SDK, int SDV, bool BF16, int D, int GC>
+__global__ void __launch_bounds__(kThreads, (kMfmaWaves<SDV, BF16, GC>))
 attn_mfma_partial(const AttnArgs a) {
-  using LY = MLayout<SDK, SDV, BF16, D>;
+  using LY = MLayout<SDK, SDV, BF16, D, GC>;
   constexpr int NSK = LY::kNSK, NSV = LY::kNSV;
   constexpr int QB = NSK / 4;          // key-code bytes per lane quarter (4, 8 or 16)
   constexpr int NQW = QB / 4;          // their 32-bit words
@@ -452,28 +470,29 @@ attn_mfma_partial(const AttnArgs a) {
   constexpr int P = LY::kParts;
   constexpr int GB = LY::kHeadsPerBlock;
   constexpr int HPL = 4 / P;           // heads per lane in the output layout
-  constexpr int VP = NSV / 16;         // 16-byte value-code pieces per thread
+  constexpr int VP = LY::kPieces;      // 16-byte value-code pieces per thread and per row
   constexpr int WG = NSV / 16;         // waves covering all value sub-spaces (16 each)
   constexpr int TG = LY::kTokGroups;   // token groups of the value sum
-  constexpr int TOKW = kMChunk / TG;   // tokens per wave in the value sum
   static_assert(QB % 4 == 0 && NSV % 16 == 0 && WG * TG == 4, "shape");
   constexpr float kPScale = 16384.0f;  // weights in (0, 1] are split as p 2^14
 
-  extern __shared__ float4 lds4[];
-  uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
+  __shared__ uint4 ktab_s[256 * SDK / 8];       // key codebook, element bits
+  __shared__ uint4 vtab4[256 * SDV / 8];        // value codebook, element bits
+  __shared__ uint4 rows4[LY::kRowElems / 8];    // query parts, then weights
+  __shared__ uint4 codes4[LY::kCodeBytes / 16];  // value codes, then value sums
+  __shared__ int qexp[kMaxGroup];               // E of each head
+  __shared__ float cmax[kMaxGroup];             // chunk maximum per head
+  __shared__ float wmax[4 * kMaxGroup];         // per wave and head
+  __shared__ float wsum[4 * kMaxGroup];
   const int g = a.Hq / a.Hkv;
   const int nb = (g + GB - 1) / GB;
   const int nrows = g * P;             // rows (head, part) in use
-  uint16_t *ktab = reinterpret_cast<uint16_t *>(lds);
-  uint16_t *vtab = reinterpret_cast<uint16_t *>(lds + LY::kKTab);
-  uint16_t *qp = reinterpret_cast<uint16_t *>(lds + LY::qp_off());
-  uint8_t *codes = lds + LY::codes_off(g);
-  float *red = reinterpret_cast<float *>(codes);  // after the value sum
-  uint16_t *pp = reinterpret_cast<uint16_t *>(lds + LY::pp_off(g));
-  int *qexp = reinterpret_cast<int *>(lds + LY::small_off(g));  // E of each head
-  float *cmax = reinterpret_cast<float *>(qexp + kMaxGroup);      // chunk maximum per head
-  float *wmax = cmax + kMaxGroup;                                  // [4][kMaxGroup]
-  float *wsum = wmax + 4 * kMaxGroup;                              // [4][kMaxGroup]
+  uint16_t *ktab = reinterpret_cast<uint16_t *>(ktab_s);
+  uint16_t *vtab = reinterpret_cast<uint16_t *>(vtab4);
+  uint16_t *qp = reinterpret_cast<uint16_t *>(rows4);
+  uint16_t *pp = reinterpret_cast<uint16_t *>(rows4);  // after the scores
+  uint8_t *codes = reinterpret_cast<uint8_t *>(codes4);
+  float *red = reinterpret_cast<float *>(codes4);  // after the value sum
 
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -544,15 +563,6 @@ attn_mfma_partial(const AttnArgs a) {
       kw[G][0] = *reinterpret_cast<const uint32_t *>(src);
     }
   }
-  uint4 vw[VP];  // value codes of the chunk, 16-byte pieces
-#pragma unroll
-  for (int k = 0; k < VP; ++k) {
-    const int e = tid + kThreads * k;
-    const int tc = e / VP, pc = e % VP;
-    const int t = min(max(t0 + tc, lo), hi - 1);
-    vw[k] = *reinterpret_cast<const uint4 *>(vc + static_cast<int64_t>(t) * NSV + 16 * pc);
-  }
-
   // ---- codebooks of kv head h into LDS (rows past n_c are zero) -------------
 #pragma unroll
   for (int k = 0; k < SDK; ++k) {
@@ -563,12 +573,6 @@ attn_mfma_partial(const AttnArgs a) {
   for (int k = 0; k < SDV; ++k) {
     const int e = tid + kThreads * k;
     vtab[e] = (e < n_c * SDV) ? vv[k] : static_cast<uint16_t>(0);
-  }
-  // value codes to LDS
-#pragma unroll
-  for (int k = 0; k < VP; ++k) {
-    const int e = tid + kThreads * k;
-    *reinterpret_cast<uint4 *>(codes + 16 * e) = vw[k];
   }
 
   // ---- query parts: wave w splits heads w and w + 4 into rows h P + part ----
@@ -611,6 +615,20 @@ attn_mfma_partial(const AttnArgs a) {
     }
   }
   __syncthreads();
+
+  // value codes of the chunk straight to LDS, in flight during the scores
+  // (the key codes have landed first, so that their uses do not wait for
+  // the copies): wave w fills pieces
+  // 64 VP w .. 64 VP (w + 1) - 1 (slot e: token e / VP, position e % VP)
+  wait_vm_all();
+#pragma unroll
+  for (int q = 0; q < VP; ++q) {
+    const int e0 = 64 * VP * w + 64 * q, e = e0 + lane;
+    const int tc = e / VP, pos = e % VP;
+    const int t = min(max(t0 + tc, lo), hi - 1);
+    copy16_to_lds(vc + static_cast<int64_t>(t) * NSV + 16 * (pos ^ ((tc >> 3) & (VP - 1))),
+                  codes4 + e0);
+  }
 
   // ---- scores on the matrix cores: wave w, tokens t0 + 64 w + 16 G + col ----
   // lane (col, kg): A = row col of a block at elements kg D/4 + 8 i .. + 7
@@ -712,7 +730,7 @@ attn_mfma_partial(const AttnArgs a) {
   __syncthreads();
 
   // ---- value sum on the matrix cores: wave w takes sub-spaces 16 (w % WG)
-  // .. + 15 (columns) over tokens (w / WG) TOKW .. + TOKW - 1 (K), one
+  // .. + 15 (columns) over the 32-token blocks tg, tg + TG, ... (K), one
   // instruction per value element; lane (col, kg) gathers the rows of its
   // sub-space for 8 tokens and regroups them by element --------------------
   const int sb = w % WG, tg = w / WG;
@@ -722,13 +740,14 @@ attn_mfma_partial(const AttnArgs a) {
   for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
     for (int e = 0; e < SDV; ++e) vacc[hb][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int kBlocks = kMChunk / 32 / TG;  // 32-token blocks per wave
 #pragma unroll 2
-  for (int blk = 0; blk < TOKW / 32; ++blk) {
-    const int tk = tg * TOKW + blk * 32 + kg * 8;  // this lane's 8 tokens
+  for (int m = 0; m < kBlocks; ++m) {
+    const int tk = (tg + TG * m) * 32 + kg * 8;  // this lane's 8 tokens
     uint32_t rw[8][SDV / 2];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t c = codes[(tk + j) * NSV + sv];
+      const uint32_t c = codes[code_at<VP, NSV>(tk + j, sv)];
       if constexpr (SDV == 4) {
         const uint2 r = reinterpret_cast<const uint2 *>(vtab)[c];
         rw[j][0] = r.x;
@@ -745,7 +764,8 @@ attn_mfma_partial(const AttnArgs a) {
     for (int hb = 0; hb < (BF16 ? 2 : 1); ++hb) {
       if (hb < nb) {
         const int ar = hb * 16 + col;
-        const uint4 av = *reinterpret_cast<const uint4 *>(pp + min(ar, nrows - 1) * kMChunk + tk);
+        const uint4 av =
+            *reinterpret_cast<const uint4 *>(pp + min(ar, nrows - 1) * kMChunk + tk);
         const uint4 aop = ar < nrows ? av : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < SDV; ++e)
@@ -823,32 +843,55 @@ attn_mfma_partial(const AttnArgs a) {
   }
 }
 
-// Merge the chunk partials of one (sequence, query head): thread d.  The
-// chunk loop is unrolled so the loads of several chunks are in flight.
+// Merge the chunk partials of one (sequence, query head): thread d.  Chunks
+// are taken 16 at a time: lanes 0..15 load their (m, l) pairs and the
+// threads their 16 o values, every load in flight (clamped indices); each
+// batch is merged against the running maximum.  An empty chunk has m = -inf
+// (weight 0), l = 0 and o = 0.
 __global__ void __launch_bounds__(kThreads)
 attn_combine(const AttnArgs a) {
+  constexpr int kBatch = 16;
+  __shared__ float bm[kBatch], bl[kBatch];
   const int bh = blockIdx.x;
-  const int D = a.D;
+  const int D = a.D, d = threadIdx.x, dc = min(d, D - 1);
   const int64_t part_stride = D + 2;
   const float *part = a.ws + static_cast<int64_t>(bh) * a.n_chunks * part_stride;
-  float M = kNegInf;
-#pragma unroll 8
-  for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, part[c * part_stride + D]);
-  for (int d = threadIdx.x; d < D; d += kThreads) {
-    float o = 0.0f;
-    if (M != kNegInf) {
-      // an empty chunk has m = -inf (weight 0), l = 0 and o = 0
-      float l = 0.0f, acc = 0.0f;
-#pragma unroll 8
-      for (int c = 0; c < a.n_chunks; ++c) {
-        const float w = exp2f(part[c * part_stride + D] - M);
-        l = __builtin_fmaf(part[c * part_stride + D + 1], w, l);
-        acc = __builtin_fmaf(part[c * part_stride + d], w, acc);
-      }
-      o = acc / l;
+  float M = kNegInf, l = 0.0f, acc = 0.0f;
+  for (int c0 = 0; c0 < a.n_chunks; c0 += kBatch) {  // uniform
+    float oc[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) oc[j] = part[min(c0 + j, a.n_chunks - 1) * part_stride + dc];
+    if (d < kBatch) {
+      const float *pc = part + min(c0 + d, a.n_chunks - 1) * part_stride;
+      const float mj = pc[D], lj = pc[D + 1];
+      bm[d] = c0 + d < a.n_chunks ? mj : kNegInf;
+      bl[d] = lj;
     }
-    a.out[static_cast<int64_t>(bh) * D + d] = o;
+    __syncthreads();
+    float m[kBatch], lc[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      m[j] = bm[j];
+      lc[j] = bl[j];
+    }
+    __syncthreads();  // bm, bl are refilled by the next batch
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) Mb = fmaxf(Mb, m[j]);
+    if (Mb != kNegInf) {
+      const float r = exp2f(M - Mb);  // 0 while nothing is merged yet
+      l *= r;
+      acc *= r;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float wj = exp2f(m[j] - Mb);
+        l = __builtin_fmaf(lc[j], wj, l);
+        acc = __builtin_fmaf(oc[j], wj, acc);
+      }
+      M = Mb;
+    }
   }
+  if (d < D) a.out[static_cast<int64_t>(bh) * D + d] = M == kNegInf ? 0.0f : acc / l;
 }
 
 template <int SDK, int SDV, bool BF16>
@@ -882,16 +925,10 @@ hipError_t launch_attn_m(AttnArgs a, hipStream_t stream) {
     return hipErrorInvalidValue;
   } else {
     const int g = a.Hq / a.Hkv;
-    const size_t lds = MLayout<SDK, SDV, BF16, D>::bytes(g);
-    auto kern = attn_mfma_partial<SDK, SDV, BF16, D>;
-    if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(lds));
-      if (e != hipSuccess) return e;
-    }
+    auto kern = g <= 4 ? attn_mfma_partial<SDK, SDV, BF16, D, 4>
+                       : attn_mfma_partial<SDK, SDV, BF16, D, kMaxGroup>;
     a.n_chunks = std::max(1, (a.S + kMChunk - 1) / kMChunk);
-    hipLaunchKernelGGL(kern, dim3(a.n_chunks, a.Hkv, a.B), dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3(a.n_chunks, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine, dim3(a.B * a.Hq), dim3(kThreads), 0, stream, a);

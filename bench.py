@@ -194,7 +194,7 @@ def leg_attention(args, dev, stream):
     kl = torch.from_numpy(wl.kv_len).to(dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     wsb = vq.attention_workspace_bytes(B, Hq, D, S)
-    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)  # zeroed counter area
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     sdk, sdv = D // wl.k_codes.shape[3], D // wl.v_codes.shape[3]
     n_c = wl.k_codebook.shape[1]
     scale = 1.0 / D ** 0.5

@@ -70,9 +70,6 @@ typedef enum {
 #define VQ_MAX_HEAD_DIM 4096
 #define VQ_ATTN_MAX_HEAD_DIM 256
 #define VQ_ATTN_MAX_GROUP 8
-/* Leading bytes of an attention workspace that hold arrival counters: zero
- * before the first call, left zero by every call. */
-#define VQ_ATTN_WORKSPACE_ZERO_BYTES 65536
 #define VQ_KMEANS_MAX_SLOT_ROWS (1 << 23)
 #define VQ_ABI_VERSION 4
 
@@ -226,16 +223,9 @@ vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
  *               VQ_ATTN_MAX_GROUP query heads per kv head.
  *   out         device fp32 [batch][n_q_heads][head_dim], 4-aligned.
  *   workspace   device scratch of at least vq_attention_workspace_bytes(...)
- *               bytes, 4-aligned, owned by the caller.  Its first
- *               VQ_ATTN_WORKSPACE_ZERO_BYTES bytes count the chunk workgroups
- *               of each (sequence, kv head) as they finish, so that the last
- *               one merges the chunk results: they must be zero on entry (zero
- *               the workspace once when allocating it; every call leaves them
- *               zero, also for a later call of another shape).  A workspace
- *               that served anything else must be zeroed again.  The rest is
- *               scratch whose contents on entry do not matter.  Calls that
- *               share a workspace must be ordered on one stream; a non-zero
- *               counter area gives wrong (not faulting) results.
+ *               bytes, 4-aligned, owned by the caller; its contents on entry do
+ *               not matter and on return are unspecified.  Calls that share a
+ *               workspace must be ordered on one stream.
  */
 size_t vq_attention_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim,
                                     int32_t max_kv_len);

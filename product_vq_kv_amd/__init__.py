@@ -274,11 +274,6 @@ def decode(idx: torch.Tensor, codebook: torch.Tensor, *, group_len: Optional[int
     return out
 
 
-# leading bytes of an attention workspace that must be zero on entry (arrival
-# counters of the chunk merge; every call leaves them zero)
-ATTN_WORKSPACE_ZERO_BYTES = 65536
-
-
 def attention_workspace_bytes(batch: int, n_q_heads: int, head_dim: int, max_kv_len: int) -> int:
     return int(lib.vq_attention_workspace_bytes(batch, n_q_heads, head_dim, max_kv_len))
 
@@ -310,9 +305,7 @@ def attention_decode(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tens
     kv_len      int32 [B] attended prefix per sequence (None: all S)
     window      attend to the last `window` tokens only (0: all)
     softmax_scale  default 1 / sqrt(D)
-    workspace   optional uint8 device tensor of attention_workspace_bytes(...) bytes whose
-                first ATTN_WORKSPACE_ZERO_BYTES are zero (torch.zeros once; every call
-                leaves them zero); None allocates a zeroed one
+    workspace   optional uint8 device tensor of attention_workspace_bytes(...) bytes
     """
     for t in (q, k_codes, v_codes, k_codebook, v_codebook):
         if not t.is_cuda or not t.is_contiguous():
@@ -349,7 +342,7 @@ def attention_decode(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tens
         raise ValueError("out must be a contiguous fp32 tensor [B, Hq, D]")
     need = attention_workspace_bytes(B, Hq, D, S)
     if workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace needs {need} bytes")
     attention_decode_raw(q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),

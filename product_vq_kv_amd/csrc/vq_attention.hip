@@ -14,10 +14,8 @@
 // Design (MI355X): the sequence is split into chunks of kChunk tokens so a
 // batch of decode queries fills the chip; each workgroup handles one
 // (sequence, kv head, chunk) for all g query heads of that kv head and writes
-// an unnormalized partial (m, l, o) per head to the caller's workspace
-// (flash-decoding split).  The matrix-core form counts the finished chunks of
-// each (sequence, kv head) in the workspace and the last one to finish merges
-// them; the lookup-table form merges in a second launch.  Within a chunk:
+// an unnormalized partial (m, l, o) per head to the caller's workspace; a
+// second launch merges the chunks (flash-decoding split).  Within a chunk:
 //   * the codebooks are widened to fp32 in LDS once;
 //   * per query head the LUT is built in LDS, 16 sub-spaces x 256 codes at a
 //     time (16 KB, so several workgroups share a CU), and each lane gathers
@@ -46,9 +44,6 @@ constexpr int kVPrefetch = 16;                  // value phase: code loads in fl
 constexpr int kLutBlock = 16;                   // sub-spaces per LUT block in LDS
 constexpr int kVGroup = 4;                      // query heads per value pass
 constexpr float kNegInf = -__builtin_inff();
-// the workspace starts with one arrival counter per (sequence, kv head)
-constexpr size_t kArriveBytes = 65536;
-constexpr int64_t kArriveSlots = kArriveBytes / sizeof(unsigned);
 
 template <bool BF16>
 __device__ __forceinline__ float widen(uint16_t v) {
@@ -105,7 +100,6 @@ struct AttnArgs {
   const float *k_scale;     // [Hkv][D] or null
   const int32_t *kv_len;    // [B] or null
   float *ws;                // [B][Hq][n_chunks][D + 2]
-  unsigned *arrive;         // [B][Hkv] finished chunks, zero at rest; null: second launch
   float *out;               // [B][Hq][D]
   int B, Hq, Hkv, D, S, n_c, window, n_chunks;
   float qmul;               // softmax_scale * log2(e)
@@ -464,84 +458,6 @@ __device__ __forceinline__ int code_at(int tc, int s) {
   return tc * NSV + (((s >> 4) ^ ((tc >> 3) & (VP - 1))) << 4) + (s & 15);
 }
 
-// The chunk partials of the matrix-core form are written and read back by
-// workgroups on different XCDs within one launch.  They go through
-// device-coherent accesses (agent-scope relaxed atomics: write-through
-// stores, loads that miss stale L2 lines), so the finish count needs no L2
-// write-back and the merge no L2 invalidate: stores are complete (vmcnt 0)
-// before the count is raised, and the merging workgroup loads only after it
-// has read the count.
-__device__ __forceinline__ void store_coherent(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float *p) {
-  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Merges the partials of chunks cf .. cl of the g query heads of one
-// (sequence, kv head) into `out` (head j at out + j D): thread d takes
-// dimension d of every head.  Chunks are taken kB at a time with every load
-// in flight; the (m, l) pairs go through LDS (bm, bl: GC kB floats each).
-// Each batch is merged against the running maximum of its head.  All
-// threads of the workgroup call it (it holds barriers).
-template <int GC, int D>
-__device__ __forceinline__ void merge_chunks(const float *part, int64_t head_stride, int cf,
-                                             int cl, int g, float *out, float *bm, float *bl) {
-  constexpr int kB = 32 / GC;
-  constexpr int64_t kStride = D + 2;
-  const int d = threadIdx.x, dc = min(d, D - 1);
-  float M[GC], l[GC], acc[GC];
-#pragma unroll
-  for (int j = 0; j < GC; ++j) {
-    M[j] = kNegInf;
-    l[j] = 0.0f;
-    acc[j] = 0.0f;
-  }
-  for (int c0 = cf; c0 <= cl; c0 += kB) {  // uniform
-    float oc[GC][kB];
-#pragma unroll
-    for (int j = 0; j < GC; ++j)
-#pragma unroll
-      for (int i = 0; i < kB; ++i)
-        oc[j][i] = load_coherent(part + min(j, g - 1) * head_stride + min(c0 + i, cl) * kStride + dc);
-    if (d < GC * kB) {
-      const int j = d / kB, c = c0 + d % kB;
-      const float *pc = part + min(j, g - 1) * head_stride + min(c, cl) * kStride;
-      const float mj = load_coherent(pc + D), lj = load_coherent(pc + D + 1);
-      const bool ok = j < g && c <= cl;
-      bm[d] = ok ? mj : kNegInf;
-      bl[d] = ok ? lj : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < GC; ++j) {
-      if (j < g) {
-        float Mb = M[j];
-#pragma unroll
-        for (int i = 0; i < kB; ++i) Mb = fmaxf(Mb, bm[j * kB + i]);
-        if (Mb != kNegInf) {
-          const float r = exp2f(M[j] - Mb);  // 0 while nothing is merged yet
-          l[j] *= r;
-          acc[j] *= r;
-#pragma unroll
-          for (int i = 0; i < kB; ++i) {
-            const float wi = exp2f(bm[j * kB + i] - Mb);
-            l[j] = __builtin_fmaf(bl[j * kB + i], wi, l[j]);
-            acc[j] = __builtin_fmaf(oc[j][i], wi, acc[j]);
-          }
-          M[j] = Mb;
-        }
-      }
-    }
-    __syncthreads();  // bm, bl are refilled by the next batch
-  }
-  if (d < D) {
-#pragma unroll
-    for (int j = 0; j < GC; ++j)
-      if (j < g) out[j * D + d] = M[j] == kNegInf ? 0.0f : acc[j] / l[j];
-  }
-}
-
 // Waves per SIMD the register budget is set for (6 fit the LDS of the common
 // fp16 shapes; the wider forms need more registers).
 template <int SDV_, bool BF16_, int GC_>
@@ -572,7 +488,6 @@ attn_mfma_partial(const AttnArgs a) {
   __shared__ float cmax[kMaxGroup];             // chunk maximum per head
   __shared__ float wmax[4 * kMaxGroup];         // per wave and head
   __shared__ float wsum[4 * kMaxGroup];
-  __shared__ int merge_here;                    // this workgroup finished last
   const int g = a.Hq / a.Hkv;
   const int nb = (g + GB - 1) / GB;
   const int nrows = g * P;             // rows (head, part) in use
@@ -598,12 +513,6 @@ attn_mfma_partial(const AttnArgs a) {
   const int64_t head_stride = static_cast<int64_t>(a.n_chunks) * part_stride;
   float *part = a.ws + ((static_cast<int64_t>(b) * a.Hq + h * g) * a.n_chunks + chunk) * part_stride;
   if (lo >= hi) {  // nothing attended here (uniform)
-    if (a.arrive) {  // only attended chunks are merged; with none, chunk 0 writes zeros
-      if (L == 0 && chunk == 0)
-        for (int e = tid; e < g * D; e += kThreads)
-          a.out[(static_cast<int64_t>(b) * a.Hq + h * g) * D + e] = 0.0f;
-      return;
-    }
     for (int j = 0; j < g; ++j) {
       float *pj = part + j * head_stride;
       for (int d = tid; d < D; d += kThreads) pj[d] = 0.0f;
@@ -926,7 +835,10 @@ attn_mfma_partial(const AttnArgs a) {
         if (hb < nb && hh < g) {
           float *dst = part + hh * head_stride + sv * SDV;
 #pragma unroll
-          for (int e = 0; e < SDV; ++e) store_coherent(dst + e, o[hb][j][e]);
+          for (int q4 = 0; q4 < SDV / 4; ++q4)
+            reinterpret_cast<float4 *>(dst)[q4] =
+                make_float4(o[hb][j][4 * q4], o[hb][j][4 * q4 + 1], o[hb][j][4 * q4 + 2],
+                            o[hb][j][4 * q4 + 3]);
         }
       }
   }
@@ -934,28 +846,9 @@ attn_mfma_partial(const AttnArgs a) {
     float *pj = part + tid * head_stride;
     const float l = ((wsum[tid] + wsum[kMaxGroup + tid]) + wsum[2 * kMaxGroup + tid]) +
                     wsum[3 * kMaxGroup + tid];
-    store_coherent(pj + D, cmax[tid]);
-    store_coherent(pj + D + 1, l);
+    pj[D] = cmax[tid];
+    pj[D + 1] = l;
   }
-  if (!a.arrive) return;  // merged by attn_combine (uniform)
-
-  // ---- the last of the attended chunks of (b, h) to finish merges them
-  wait_vm_all();  // this thread's partial stores are complete
-  __syncthreads();
-  const int cf = first / kMChunk, cl = (L - 1) / kMChunk;
-  if (tid == 0) {
-    unsigned *ctr = a.arrive + static_cast<int64_t>(b) * a.Hkv + h;
-    const unsigned n =
-        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    const bool last = n == static_cast<unsigned>(cl - cf + 1);
-    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    merge_here = last;
-  }
-  __syncthreads();
-  if (!merge_here) return;  // uniform
-  const float *part0 = a.ws + (static_cast<int64_t>(b) * a.Hq + h * g) * a.n_chunks * part_stride;
-  merge_chunks<GC, D>(part0, head_stride, cf, cl, g,
-                      a.out + (static_cast<int64_t>(b) * a.Hq + h * g) * D, red, red + 64);
 }
 
 // Merge the chunk partials of one (sequence, query head): thread d.  Chunks
@@ -1043,12 +936,9 @@ hipError_t launch_attn_m(AttnArgs a, hipStream_t stream) {
     auto kern = g <= 4 ? attn_mfma_partial<SDK, SDV, BF16, D, 4>
                        : attn_mfma_partial<SDK, SDV, BF16, D, kMaxGroup>;
     a.n_chunks = std::max(1, (a.S + kMChunk - 1) / kMChunk);
-    // one counter per (sequence, kv head) in the zeroed head of the workspace;
-    // past its size a second launch merges
-    if (static_cast<int64_t>(a.B) * a.Hkv > kArriveSlots) a.arrive = nullptr;
     hipLaunchKernelGGL(kern, dim3(a.n_chunks, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.arrive) return e;
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine, dim3(a.B * a.Hq), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
   }
@@ -1078,11 +968,6 @@ hipError_t launch_attn_dt(const AttnArgs &a, int sdk, int sdv, bool mfma, hipStr
 
 int attention_chunks(int max_kv_len) { return std::max(1, (max_kv_len + kMChunk - 1) / kMChunk); }
 
-size_t attention_workspace_bytes(int batch, int n_q_heads, int head_dim, int max_kv_len) {
-  return kArriveBytes + static_cast<size_t>(batch) * n_q_heads * attention_chunks(max_kv_len) *
-                            (static_cast<size_t>(head_dim) + 2) * sizeof(float);
-}
-
 size_t attention_lds_bytes(int sdk, int sdv, int D, int g) {
   if (sdk == 4) return sdv == 4 ? attn_lds_bytes<4, 4>(D, g) : attn_lds_bytes<4, 8>(D, g);
   return sdv == 4 ? attn_lds_bytes<8, 4>(D, g) : attn_lds_bytes<8, 8>(D, g);
@@ -1097,8 +982,7 @@ hipError_t launch_attention(const AttnLayout &l, hipStream_t stream) {
   a.v_cb = static_cast<const uint16_t *>(l.v_codebook);
   a.k_scale = l.k_scale;
   a.kv_len = l.kv_len;
-  a.arrive = static_cast<unsigned *>(l.workspace);
-  a.ws = reinterpret_cast<float *>(static_cast<char *>(l.workspace) + kArriveBytes);
+  a.ws = l.workspace;
   a.out = l.out;
   a.B = l.batch;
   a.Hq = l.n_q_heads;

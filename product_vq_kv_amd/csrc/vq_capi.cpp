@@ -176,7 +176,8 @@ vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
 size_t vq_attention_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim,
                                     int32_t max_kv_len) {
   if (batch < 0 || n_q_heads < 0 || head_dim < 0 || max_kv_len < 0) return 0;
-  return vqk::attention_workspace_bytes(batch, n_q_heads, head_dim, max_kv_len);
+  return static_cast<size_t>(batch) * n_q_heads * vqk::attention_chunks(max_kv_len) *
+         (static_cast<size_t>(head_dim) + 2) * sizeof(float);
 }
 
 vq_status vq_attention_decode(const void *q, const uint8_t *k_codes, const uint8_t *v_codes,
@@ -222,7 +223,7 @@ vq_status vq_attention_decode(const void *q, const uint8_t *k_codes, const uint8
   l.k_scale = k_scale;
   l.kv_len = kv_len;
   l.out = out;
-  l.workspace = workspace;
+  l.workspace = static_cast<float *>(workspace);
   l.batch = batch;
   l.n_q_heads = n_q_heads;
   l.n_kv_heads = n_kv_heads;

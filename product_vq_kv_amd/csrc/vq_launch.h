@@ -60,7 +60,7 @@ struct AttnLayout {
   const float *k_scale;      // [Hkv][D] or nullptr
   const int32_t *kv_len;     // [B] or nullptr
   float *out;                // [B][Hq][D]
-  void *workspace;           // counters, then attention_chunks(S) partials per (b, hq)
+  float *workspace;          // attention_chunks(S) partials per (b, hq)
   int32_t batch, n_q_heads, n_kv_heads, head_dim, max_kv_len;
   int32_t k_sub_dim, v_sub_dim, n_centroids, bf16, window;
   float softmax_scale;
@@ -74,8 +74,6 @@ hipError_t launch_kmeans(const void *x, void *codebook, const int32_t *group_map
                          const Layout &l, int iterations, void *workspace, hipStream_t stream);
 
 int attention_chunks(int max_kv_len);
-// bytes of the workspace: the zeroed arrival counters, then the partials
-size_t attention_workspace_bytes(int batch, int n_q_heads, int head_dim, int max_kv_len);
 size_t attention_lds_bytes(int k_sub_dim, int v_sub_dim, int head_dim, int group);
 hipError_t launch_attention(const AttnLayout &l, hipStream_t stream);
 

@@ -180,9 +180,8 @@ def attn(**over):
 
 def test_attention_workspace_size():
     # one (D + 2)-float partial per (sequence, query head, 256-token chunk)
-    z = vq.ATTN_WORKSPACE_ZERO_BYTES
-    assert vq.lib.vq_attention_workspace_bytes(2, 12, 256, 100) == z + 2 * 12 * 1 * 258 * 4
-    assert vq.lib.vq_attention_workspace_bytes(2, 12, 256, 1025) == z + 2 * 12 * 5 * 258 * 4
+    assert vq.lib.vq_attention_workspace_bytes(2, 12, 256, 100) == 2 * 12 * 1 * 258 * 4
+    assert vq.lib.vq_attention_workspace_bytes(2, 12, 256, 1025) == 2 * 12 * 5 * 258 * 4
     assert vq.lib.vq_attention_workspace_bytes(-1, 12, 256, 100) == 0
 
 

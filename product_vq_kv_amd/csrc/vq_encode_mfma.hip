@@ -50,6 +50,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "vq_codes.h"
 #include "vq_launch.h"
@@ -164,6 +165,18 @@ __device__ __forceinline__ float sqdist(const float (&xv)[SD], const float (&c)[
   return acc;
 }
 
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>): the body
+// is instantiated once per index, so per-column arrays are indexed by
+// constants (never moved to scratch) however large the body is.
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F &&f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 // Element j of the 16-bit values packed in w (two per word).
 __device__ __forceinline__ uint16_t half_of(const uint32_t *w, int j) {
   return static_cast<uint16_t>((j & 1) ? (w[j >> 1] >> 16) : w[j >> 1]);
@@ -265,76 +278,118 @@ __device__ __forceinline__ float pair_sum(float v) {
 //   cval [n_cpad] float     C operand: shrunk |c|^2/2, +inf for padding and
 //                           duplicate rows;
 //   gan  [n_cpad/16] float  per 16-row group: kappa max |c| (rounded up);
-//   c32  [n_cpad][SD] float the centroids in fp32 (ROWS32 only);
-//   hash [hash_slots] int   duplicate detection while staging;
+//   c32                     the centroids in fp32 (ROWS32 only), row r at
+//                           c32_offset(r): 16 bytes of padding after every
+//                           4 rows and after every 32, so that the rows the
+//                           lanes of a wave read together in the exact stage
+//                           (same position in different groups) fall on
+//                           different LDS banks;
+//   hash [hash_slots] uint  duplicate detection while staging;
+//   flags [16] int          per-wave staging flags;
 //   scale [head_dim] float  the slot's channel factors (smoothed keys only).
 // gan is padded to a multiple of 4 floats so every region is 16-byte aligned.
 template <int SD, bool ROWS32>
 struct Lds {
+  static constexpr int kFlags = 16;  // one per wave, at most 1024 threads
   uint4 *rows;
   float *cval;
   float *gan;
   float *c32;
-  int *hash;
+  uint32_t *hash;
+  int *flags;
   float *scale;
   static constexpr int gan_len(int n_cpad) { return (n_cpad / 16 + 3) & ~3; }
+  // floats of the c32 region, and the float offset of row r in it
+  static constexpr int c32_len(int n_cpad) {
+    return ROWS32 ? SD * n_cpad + 4 * (n_cpad / 4 + n_cpad / 32 + 1) : 0;
+  }
+  static __device__ __forceinline__ int c32_offset(int r) { return SD * r + 4 * ((r >> 2) + (r >> 5)); }
   __device__ Lds(uint4 *base, int n_cpad, int hash_slots) {
     rows = base;
     cval = reinterpret_cast<float *>(rows + n_cpad);
     gan = cval + n_cpad;
     c32 = gan + gan_len(n_cpad);
-    hash = reinterpret_cast<int *>(c32 + (ROWS32 ? n_cpad * SD : 0));
-    scale = reinterpret_cast<float *>(hash + hash_slots);
+    hash = reinterpret_cast<uint32_t *>(c32 + c32_len(n_cpad));
+    flags = reinterpret_cast<int *>(hash + hash_slots);
+    scale = reinterpret_cast<float *>(flags + kFlags);
   }
   static size_t bytes(int n_cpad, int hash_slots, int scale_len) {
-    return static_cast<size_t>(n_cpad) * (16 + 4 + (ROWS32 ? 4 * SD : 0)) +
+    return static_cast<size_t>(n_cpad) * (16 + 4) + static_cast<size_t>(c32_len(n_cpad)) * 4 +
            static_cast<size_t>(gan_len(n_cpad)) * 4 + static_cast<size_t>(hash_slots) * 4 +
-           static_cast<size_t>(scale_len) * 4;
+           kFlags * 4 + static_cast<size_t>(scale_len) * 4;
   }
 };
 
 // Group (16 rows) of row r: block r/32, half ((r%32)/4)%2.
 __device__ __forceinline__ int group_of(int r) { return 2 * (r >> 5) + ((r >> 2) & 1); }
 
-// Centroid c as fp32, from the fp32 copy or widened from the staged -c bits.
+// Row i (0..3) of the 4-row set starting at c0 (a multiple of 4) as fp32,
+// from the fp32 copy (the set is contiguous there) or widened from the
+// staged -c bits.
 template <int SD, bool BF16, bool ROWS32>
-__device__ __forceinline__ void centroid(const Lds<SD, ROWS32> &s, int c, float (&v)[SD]) {
+__device__ __forceinline__ void centroid_in_set(const Lds<SD, ROWS32> &s, int c0, int i,
+                                                float (&v)[SD]) {
   if constexpr (ROWS32) {
+    const float *base = s.c32 + s.c32_offset(c0) + SD * i;
 #pragma unroll
     for (int q = 0; q < SD / 4; ++q) {
-      const float4 w = *reinterpret_cast<const float4 *>(s.c32 + c * SD + 4 * q);
+      const float4 w = *reinterpret_cast<const float4 *>(base + 4 * q);
       v[4 * q] = w.x;
       v[4 * q + 1] = w.y;
       v[4 * q + 2] = w.z;
       v[4 * q + 3] = w.w;
     }
   } else {
-    const uint4 q = s.rows[c];
+    const uint4 q = s.rows[c0 + i];
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     widen_words<SD, BF16>(w, 0x8000u, v);
   }
 }
 
+// Centroid c as fp32.
+template <int SD, bool BF16, bool ROWS32>
+__device__ __forceinline__ void centroid(const Lds<SD, ROWS32> &s, int c, float (&v)[SD]) {
+  centroid_in_set<SD, BF16, ROWS32>(s, c & ~3, c & 3, v);
+}
+
+// Maximum over the 16 lanes that hold the rows of one group (lanes that agree
+// on bits 2 and 5 of the lane index: rows b*32 + 8j + 4hh + i, i, j = 0..3).
+// Non-negative floats order like their bit patterns.
+__device__ __forceinline__ float group_max(float v) {
+  int b = __float_as_int(v);
+  b = max(b, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false));  // lane ^ 8
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);     // lane ^ 16
+  return __int_as_float(max(static_cast<int>(r[0]), static_cast<int>(r[1])));
+}
+
 // Stage one codebook slot (and, for smoothed keys, its channel factors).
 // Returns true when some centroid has a non-finite or huge norm: then every
-// sub-vector of the slot takes the full exact scan.
+// sub-vector of the slot takes the full exact scan.  Two barriers: one after
+// the rows are written, one after duplicate rows are marked.
 template <int SD, int NT, bool BF16, bool ROWS32, int BLOCK, bool FOLD>
 __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_cpad,
                                const Lds<SD, ROWS32> &s, int hash_slots,
                                const float *__restrict__ scale, int scale_len, bool &fold_ok) {
   using K = Consts<SD, NT>;
+  constexpr uint32_t kEmpty = 0xFFFFFFFFu;
   const int tid = threadIdx.x;
-  for (int i = tid; i < hash_slots; i += BLOCK) s.hash[i] = -1;
-  for (int i = tid; i < n_cpad / 16; i += BLOCK) s.gan[i] = 0.0f;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < hash_slots; i += BLOCK) s.hash[i] = kEmpty;
   for (int i = tid; i < scale_len; i += BLOCK) s.scale[i] = scale ? scale[i] : 1.0f;
-  __syncthreads();
   int flag = 0, nofold = 0;
-  for (int r = tid; r < n_cpad; r += BLOCK) {
+  // whole waves per pass (n_cpad is a multiple of 32, so a group never
+  // straddles the end), which keeps the group maximum's lane exchanges uniform
+  for (int base = wave * 64; base < n_cpad; base += BLOCK) {
+    const int r = base + lane;
     uint16_t k8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float v[SD];
 #pragma unroll
     for (int i = 0; i < SD; ++i) v[i] = 0.0f;
     float cv = __builtin_inff();
+    float an = 0.0f;
     if (r < n_c) {
       // element loads: a slot only has to be 2-byte aligned
       const uint16_t *p = cb + static_cast<int64_t>(r) * SD;
@@ -351,63 +406,61 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
         flag = 1;
       } else {
         cv = n2c * K::kHalfShrink - 2.0f * kTau;
-        const float an = __builtin_sqrtf(n2c) * kNormUp * K::kKappa;
-        // non-negative floats order like their bit patterns
-        atomicMax(reinterpret_cast<int *>(&s.gan[group_of(r)]), __float_as_int(an));
+        an = __builtin_sqrtf(n2c) * kNormUp * K::kKappa;
       }
     }
-    if constexpr (FOLD) {  // halves 4, 5 carry C (SD == 4)
-      if (!split_down<BF16>(cv, k8[4], k8[5])) nofold = 1;
-    }
-    s.rows[r] = make_uint4(k8[0] | (static_cast<uint32_t>(k8[1]) << 16),
-                           k8[2] | (static_cast<uint32_t>(k8[3]) << 16),
-                           k8[4] | (static_cast<uint32_t>(k8[5]) << 16),
-                           k8[6] | (static_cast<uint32_t>(k8[7]) << 16));
-    s.cval[r] = cv;
-    if constexpr (ROWS32) {
+    an = group_max(an);
+    if (r < n_cpad) {
+      if ((lane & 0x1B) == 0) s.gan[group_of(r)] = an;
+      if constexpr (FOLD) {  // halves 4, 5 carry C (SD == 4)
+        if (!split_down<BF16>(cv, k8[4], k8[5])) nofold = 1;
+      }
+      s.rows[r] = make_uint4(k8[0] | (static_cast<uint32_t>(k8[1]) << 16),
+                             k8[2] | (static_cast<uint32_t>(k8[3]) << 16),
+                             k8[4] | (static_cast<uint32_t>(k8[5]) << 16),
+                             k8[6] | (static_cast<uint32_t>(k8[7]) << 16));
+      s.cval[r] = cv;
+      if constexpr (ROWS32) {
 #pragma unroll
-      for (int q = 0; q < SD / 4; ++q)
-        *reinterpret_cast<float4 *>(s.c32 + r * SD + 4 * q) =
-            make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        for (int q = 0; q < SD / 4; ++q)
+          *reinterpret_cast<float4 *>(s.c32 + s.c32_offset(r) + 4 * q) =
+              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      }
     }
   }
-  const bool exact = __syncthreads_or(flag) != 0;
-  fold_ok = FOLD && __syncthreads_or(nofold) == 0;
+  const int wflags = (__any(flag) ? 1 : 0) | (__any(nofold) ? 2 : 0);
+  if (lane == 0) s.flags[wave] = wflags;
+  __syncthreads();
+  int all = 0;
+#pragma unroll
+  for (int w = 0; w < BLOCK / 64; ++w) all |= s.flags[w];
+  const bool exact = (all & 1) != 0;
+  fold_ok = FOLD && (all & 2) == 0;
   if (!exact) {
     // A row bit-identical to an earlier row can never win the strict-< scan.
-    // Open addressing, at most half full: each distinct row value keeps the
-    // smallest index that has it.
-    const int mask = hash_slots - 1;
+    // Open addressing, at most half full; an entry is (tag << 12) | row with
+    // the tag taken from hash bits the slot does not use (n_c <= 4096).  All
+    // copies of one row value meet in one entry: the first to arrive claims
+    // it, every later one lowers it to the smaller index with an atomic min,
+    // and whichever of the two indices is larger is a duplicate.  So every
+    // copy but the first is marked, and never the first.
+    const uint32_t mask = static_cast<uint32_t>(hash_slots - 1);
     for (int r = tid; r < n_c; r += BLOCK) {
       const uint4 q = s.rows[r];
-      int slot = static_cast<int>(hash_row<SD>(q)) & mask;
+      const uint32_t hv = hash_row<SD>(q);
+      const uint32_t key = ((hv >> 13) << 12) | static_cast<uint32_t>(r);
+      uint32_t slot = hv & mask;
       for (int probe = 0; probe < hash_slots; ++probe) {
-        const int old = atomicCAS(&s.hash[slot], -1, r);
-        if (old == -1) break;
-        if (same_row<SD>(s.rows[old], q)) {
-          atomicMin(&s.hash[slot], r);
+        const uint32_t old = atomicCAS(&s.hash[slot], kEmpty, key);
+        if (old == kEmpty) break;
+        if ((old >> 12) == (key >> 12) && same_row<SD>(s.rows[old & 0xFFFu], q)) {
+          const uint32_t prev = atomicMin(&s.hash[slot], key);
+          const int dup = max(static_cast<int>(prev & 0xFFFu), r);
+          s.cval[dup] = __builtin_inff();
+          if constexpr (FOLD) s.rows[dup].z = kInfBits<BF16>;  // C_hi = +inf, C_lo = 0
           break;
         }
         slot = (slot + 1) & mask;
-      }
-    }
-    __syncthreads();
-    for (int r = tid; r < n_c; r += BLOCK) {
-      const uint4 q = s.rows[r];
-      int slot = static_cast<int>(hash_row<SD>(q)) & mask;
-      int first = r;
-      for (int probe = 0; probe < hash_slots; ++probe) {
-        const int v = s.hash[slot];
-        if (v < 0) break;
-        if (same_row<SD>(s.rows[v], q)) {
-          first = v;
-          break;
-        }
-        slot = (slot + 1) & mask;
-      }
-      if (first < r) {
-        s.cval[r] = __builtin_inff();
-        if constexpr (FOLD) s.rows[r].z = kInfBits<BF16>;  // C_hi = +inf, C_lo = 0
       }
     }
     __syncthreads();
@@ -415,23 +468,35 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
   return exact;
 }
 
-// Lowest-index strict-< minimum of the exact distance over 4 consecutive rows
-// from c0; rows are visited in ascending order.  With MASK, rows >= n_c (the
-// padding of the last block) are excluded; without it every row is < n_c.
-template <int SD, bool BF16, bool ROWS32, bool MASK = true>
+// Strict-< minimum of the exact distance over the 4 consecutive rows c0 ..
+// c0 + 3 (c0 a multiple of 4, c0 + 3 < n_cpad: padding rows are staged too),
+// visited in ascending order; the index recorded for row c0 + i is k0 + i.
+// With MASK, rows >= n_c (the padding of the last block) are excluded;
+// without it every row is < n_c.
+template <int SD, bool BF16, bool ROWS32, bool MASK>
 __device__ __forceinline__ void exact4(const Lds<SD, ROWS32> &s, const float (&xv)[SD], int c0,
-                                       int n_c, float &best, int &bi) {
+                                       int k0, int n_c, float &best, int &bk) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = c0 + i;
     float cv[SD];
-    centroid<SD, BF16, ROWS32>(s, MASK ? min(c, n_c - 1) : c, cv);
+    centroid_in_set<SD, BF16, ROWS32>(s, c0, i, cv);
     float d = sqdist<SD>(xv, cv);
     if (MASK) d = (c < n_c) ? d : __builtin_inff();
     const bool lt = d < best;
     best = lt ? d : best;
-    bi = lt ? c : bi;
+    bk = lt ? k0 + i : bk;
   }
+}
+
+// All 16 rows of group grp (rows b*32 + 8j + 4hh + i, grp = 2b + hh), in
+// ascending order, into (best, bi) by strict <.
+template <int SD, bool BF16, bool ROWS32>
+__device__ __forceinline__ void exact_group(const Lds<SD, ROWS32> &s, const float (&xv)[SD],
+                                            int grp, int n_c, float &best, int &bi) {
+  const int r0 = (grp >> 1) * 32 + 4 * (grp & 1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) exact4<SD, BF16, ROWS32, true>(s, xv, r0 + 8 * j, r0 + 8 * j, n_c, best, bi);
 }
 
 // Combine (distance, index) over the two lanes of a pair: smaller distance,
@@ -444,21 +509,13 @@ __device__ __forceinline__ void pair_min(float &best, int &bi, int h) {
   bi = take ? oi : bi;
 }
 
-// The full sub-vector of a column from the two halves held by the pair.
+// The full sub-vector of a column: lane 0 of the pair holds words 0, 1 and
+// lane 1 words 2, 3 (sub_dim 8; at sub_dim 4 only lane 0's words are used).
 template <int SD, bool BF16>
-__device__ __forceinline__ void column_x(const uint2 &own, int h, float (&xv)[SD]) {
-  const uint2 o = make_uint2(pair_other(own.x, h), pair_other(own.y, h));
-  uint32_t w[4];
-  const uint2 lo = (h == 0) ? own : o;
-  w[0] = lo.x;
-  w[1] = lo.y;
-  if constexpr (SD == 4) {
-    w[2] = w[3] = 0;
-  } else {
-    const uint2 hi = (h == 0) ? o : own;
-    w[2] = hi.x;
-    w[3] = hi.y;
-  }
+__device__ __forceinline__ void column_x(const uint2 &own, float (&xv)[SD]) {
+  const PairVals p0 = pair_vals(own.x);
+  const PairVals p1 = pair_vals(own.y);
+  const uint32_t w[4] = {p0.first, p1.first, p0.second, p1.second};
   widen_words<SD, BF16>(w, 0, xv);
 }
 
@@ -481,9 +538,37 @@ struct Smooth {
   float inv_n_sub;
 };
 
-// One tile: every wave encodes T columns of 32 sub-vectors.
+// Raw words of the T sub-vectors this lane loads for a tile: column t, row
+// tbase + (wave T + t) 32 + lane mod 32 (zero past the group's end).
+template <int SD, int T>
+__device__ __forceinline__ void load_tile_x(const uint16_t *__restrict__ x, int64_t tbase,
+                                            int64_t gend, uint32_t (&w)[T][4]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t row = tbase + (wave * T + t) * 32 + (lane & 31);
+    w[t][0] = w[t][1] = w[t][2] = w[t][3] = 0;
+    if (row < gend) {
+      if constexpr (SD == 4) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(x + row * 4);
+        w[t][0] = q.x;
+        w[t][1] = q.y;
+      } else {
+        const uint4 q = *reinterpret_cast<const uint4 *>(x + row * 8);
+        w[t][0] = q.x;
+        w[t][1] = q.y;
+        w[t][2] = q.z;
+        w[t][3] = q.w;
+      }
+    }
+  }
+}
+
+// One tile: every wave encodes T columns of 32 sub-vectors (raw words from
+// load_tile_x).
 template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
-__device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64_t gend, int n_c,
+__device__ void encode_tile(const uint32_t (&xin)[T][4], int64_t tbase, int64_t gend, int n_c,
                             int n_cpad, const Lds<SD, ROWS32> &s, bool exact_tile, bool fold,
                             const Smooth sm, int code_bits, uint8_t *__restrict__ out) {
   using K = Consts<SD, kTerms<SD, SCALED>>;
@@ -510,21 +595,7 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
   uint32_t full_bits = 0;  // bit t: column t takes the full exact scan
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int64_t row = tbase + (wave * T + t) * 32 + col;
-    uint32_t w[4] = {0, 0, 0, 0};
-    if (row < gend) {
-      if constexpr (SD == 4) {
-        const uint2 q = *reinterpret_cast<const uint2 *>(x + row * 4);
-        w[0] = q.x;
-        w[1] = q.y;
-      } else {
-        const uint4 q = *reinterpret_cast<const uint4 *>(x + row * 8);
-        w[0] = q.x;
-        w[1] = q.y;
-        w[2] = q.z;
-        w[3] = q.w;
-      }
-    }
+    const uint32_t w[4] = {xin[t][0], xin[t][1], xin[t][2], xin[t][3]};
     if constexpr (SCALED) {
       // the pair splits the components: lane h smooths and splits components
       // h*E .. h*E + E - 1 (x~ = hi + lo + e exactly), then each lane trades
@@ -665,45 +736,63 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
     }
   }
 
-  // ---- stage 2: exact resolution, one column at a time (lanes col and
-  // col+32 share a column) ---------------------------------------------------
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    float xv[SD];
+  // the fp32 sub-vector of column t (smoothed keys: times the factors)
+  auto column_value = [&](int t, float (&xv)[SD]) {
     if constexpr (SCALED) {
       if constexpr (SD == 4) {
         const uint32_t w[4] = {xw[t].x, xw[t].y, 0, 0};
         widen_words<SD, BF16>(w, 0, xv);
       } else {
-        column_x<SD, BF16>(xw[t], h, xv);
+        column_x<SD, BF16>(xw[t], xv);
       }
       float f[SD];
       factors<SD, ROWS32>(s, mod_small(m0 + 32 * t, sm.n_sub, sm.inv_n_sub), f);
 #pragma unroll
       for (int i = 0; i < SD; ++i) xv[i] = xv[i] * f[i];
     } else {
-      column_x<SD, BF16>(bop[t], h, xv);
+      column_x<SD, BF16>(bop[t], xv);
     }
-    const float om1 = pair_other(m1[t], h);
-    const float om2 = pair_other(m2[t], h);
-    const int og1 = pair_other(g1[t], h);
-    const bool mine = m1[t] < om1;
-    const bool theirs = om1 < m1[t];
-    const int cg1 = mine ? g1[t] : (theirs ? og1 : min(g1[t], og1));
-    const float cm2 = mine ? fminf(m2[t], om1) : (theirs ? fminf(om2, m1[t]) : m1[t]);
+  };
+
+  // ---- stage 2: exact resolution, one column at a time (lanes col and
+  // col+32 share a column) ---------------------------------------------------
+  unroll<T>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    float xv[SD];
+    column_value(t, xv);
+    // the pair's combined smallest group bound (lower group on equal bounds)
+    // and second smallest bound: with a0 <= b0 and a1 <= b1 the second
+    // smallest of {a0, b0, a1, b1} is med3(a0, a1, min(b0, b1))
+    const PairVals pa = pair_vals(__float_as_uint(m1[t]));
+    const PairVals pb = pair_vals(__float_as_uint(m2[t]));
+    const PairVals pg = pair_vals(static_cast<uint32_t>(g1[t]));
+    const float a0 = __uint_as_float(pa.first), a1 = __uint_as_float(pa.second);
+    const bool take1 = a1 < a0 || (a1 == a0 && static_cast<int>(pg.second) < static_cast<int>(pg.first));
+    const int cg1 = static_cast<int>(take1 ? pg.second : pg.first);
+    const float cm2 = __builtin_amdgcn_fmed3f(
+        a0, a1,
+        __builtin_amdgcn_fmed3f(__uint_as_float(pb.first), __uint_as_float(pb.second), kNegMax));
     // rows of group cg1 (block b, half hh): b*32 + 8j + 4hh + i; this lane
-    // takes j = 2h and 2h + 1, in ascending row order
+    // takes j = 2h and 2h + 1 in ascending order, so every row of lane 0
+    // precedes every row of lane 1
     const int c0 = (cg1 >> 1) * 32 + 16 * h + 4 * (cg1 & 1);
     float best = __builtin_inff();
-    int bi = 0x7fffffff;
+    int bk = 0;
     if (n_c & 31) {  // uniform: the last block has padding rows
-      exact4<SD, BF16, ROWS32, true>(s, xv, c0, n_c, best, bi);
-      exact4<SD, BF16, ROWS32, true>(s, xv, c0 + 8, n_c, best, bi);
+      exact4<SD, BF16, ROWS32, true>(s, xv, c0, 0, n_c, best, bk);
+      exact4<SD, BF16, ROWS32, true>(s, xv, c0 + 8, 4, n_c, best, bk);
     } else {
-      exact4<SD, BF16, ROWS32, false>(s, xv, c0, n_c, best, bi);
-      exact4<SD, BF16, ROWS32, false>(s, xv, c0 + 8, n_c, best, bi);
+      exact4<SD, BF16, ROWS32, false>(s, xv, c0, 0, n_c, best, bk);
+      exact4<SD, BF16, ROWS32, false>(s, xv, c0 + 8, 4, n_c, best, bk);
     }
-    pair_min(best, bi, h);
+    int bi = c0 + (bk & 3) + ((bk & 4) << 1);
+    {
+      const PairVals pd = pair_vals(__float_as_uint(best));
+      const PairVals pi = pair_vals(static_cast<uint32_t>(bi));
+      const bool t1 = __uint_as_float(pd.second) < __uint_as_float(pd.first);
+      best = __uint_as_float(t1 ? pd.second : pd.first);
+      bi = static_cast<int>(t1 ? pi.second : pi.first);
+    }
     float n2x;
     if constexpr (SCALED) {
       n2x = xv[0] * xv[0];
@@ -719,28 +808,50 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
     U = U + (best + xl) * (2.0f * kU) + kTau;
     const bool full = ((full_bits >> t) & 1u) || !(best < __builtin_inff());
     const bool amb = !full && !(cm2 > U);
+    codes[t] = static_cast<uint32_t>(bi);
 
     // ambiguous: every group whose bound can reach U contains the oracle's
-    // winner if any does; those groups are recomputed exactly
+    // winner if any does; those groups are recomputed exactly.  The bounds
+    // are recomputed on the matrix cores and each lane keeps the first two
+    // of its groups (its half of every block) that qualify; lanes evaluate
+    // their own kept groups side by side.  A lane with more than two takes a
+    // second pass over all of its qualifying groups, which come after the
+    // kept two.
     if (__any(amb)) {
-      float fb = __builtin_inff();
-      int fi = 0x7fffffff;
+      int q0 = -1, q1 = -1;
+      bool over = false;
       for (int blk = 0; blk < nblk; ++blk) {
         const OpT aop = a_operand(blk);
         const f32x16 cop = (kFold<SD, SCALED> && fold) ? zero16 : c_operand(blk);
         const float an = s.gan[2 * blk + h];
         const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
+        const int grp = 2 * blk + h;
         if (amb && mb <= U) {
-          const int r0 = blk * 32 + 4 * h;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) exact4<SD, BF16, ROWS32>(s, xv, r0 + 8 * j, n_c, fb, fi);
+          over = over || q1 >= 0;
+          q1 = (q0 >= 0 && q1 < 0) ? grp : q1;
+          q0 = (q0 < 0) ? grp : q0;
+        }
+      }
+      float fb = __builtin_inff();
+      int fi = 0x7fffffff;
+      if (q0 >= 0) exact_group<SD, BF16, ROWS32>(s, xv, q0, n_c, fb, fi);
+      if (__any(q1 >= 0)) {
+        if (q1 >= 0) exact_group<SD, BF16, ROWS32>(s, xv, q1, n_c, fb, fi);
+      }
+      if (__any(over)) {
+        for (int blk = 0; blk < nblk; ++blk) {
+          const OpT aop = a_operand(blk);
+          const f32x16 cop = (kFold<SD, SCALED> && fold) ? zero16 : c_operand(blk);
+          const float an = s.gan[2 * blk + h];
+          const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
+          if (over && mb <= U) exact_group<SD, BF16, ROWS32>(s, xv, 2 * blk + h, n_c, fb, fi);
         }
       }
       pair_min(fb, fi, h);
-      best = amb ? fb : best;
-      bi = amb ? fi : bi;
+      codes[t] = amb ? static_cast<uint32_t>(fi) : codes[t];
     }
-    // non-finite or huge values: full exact strict-< scan, split by parity
+    // non-finite or huge values (or no distance below +inf): full exact
+    // strict-< scan, split by parity; index 0 when nothing beats +inf
     if (__any(full)) {
       float fb = __builtin_inff();
       int fi = 0x7fffffff;
@@ -756,11 +867,9 @@ __device__ void encode_tile(const uint16_t *__restrict__ x, int64_t tbase, int64
         fi = lt ? c : fi;
       }
       pair_min(fb, fi, h);
-      best = full ? fb : best;
-      bi = full ? fi : bi;
+      codes[t] = full ? ((fi == 0x7fffffff) ? 0u : static_cast<uint32_t>(fi)) : codes[t];
     }
-    codes[t] = (bi == 0x7fffffff) ? 0u : static_cast<uint32_t>(bi);
-  }
+  });
 
   // ---- store: outside the column loop, one width branch ---------------------
   if constexpr (SCALED) {
@@ -835,14 +944,17 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
       }
       continue;  // uniform
     }
+    // the tile's loads are issued first, so that they overlap the staging
+    uint32_t xw[T][4];
+    load_tile_x<SD, T>(x, tbase, gend, xw);
     if (slot != staged) {
-      __syncthreads();  // every wave is done with the previous slot
+      if (staged >= 0) __syncthreads();  // every wave is done with the previous slot
       exact_tile = stage_codebook<SD, kTerms<SD, SCALED>, BF16, ROWS32, BLOCK, kFold<SD, SCALED>>(
           codebook + slot * cb_stride, n_c, n_cpad, s, hash_slots,
           (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len, fold);
       staged = slot;
     }
-    encode_tile<SD, T, BLOCK, BF16, ROWS32, SCALED>(x, tbase, gend, n_c, n_cpad, s, exact_tile,
+    encode_tile<SD, T, BLOCK, BF16, ROWS32, SCALED>(xw, tbase, gend, n_c, n_cpad, s, exact_tile,
                                                     fold, sm, code_bits, out);
   }
 }

@@ -532,6 +532,24 @@ __device__ __forceinline__ void factors(const Lds<SD, ROWS32> &s, int m, float (
   }
 }
 
+// Wave priority from progress: the waves of a CU share its SIMDs, and the
+// issue arbiter prefers the oldest wave among equals, so without this the
+// first workgroup of a CU finishes far ahead of the last and the CU runs its
+// tail with few waves.  A wave that has done phase p of n (two phases per
+// tile) drops to level 3 - 4p/n, so waves that fall behind are preferred.
+__device__ __forceinline__ void set_progress_priority(int64_t phase, int64_t n_phases) {
+  const int64_t lvl = 3 - (4 * phase) / n_phases;
+  if (lvl >= 3) {
+    __builtin_amdgcn_s_setprio(3);
+  } else if (lvl == 2) {
+    __builtin_amdgcn_s_setprio(2);
+  } else if (lvl == 1) {
+    __builtin_amdgcn_s_setprio(1);
+  } else {
+    __builtin_amdgcn_s_setprio(0);
+  }
+}
+
 // Channel layout of smoothed keys: row r is sub-slot r mod n_sub of its key.
 struct Smooth {
   int n_sub;
@@ -570,7 +588,8 @@ __device__ __forceinline__ void load_tile_x(const uint16_t *__restrict__ x, int6
 template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
 __device__ void encode_tile(const uint32_t (&xin)[T][4], int64_t tbase, int64_t gend, int n_c,
                             int n_cpad, const Lds<SD, ROWS32> &s, bool exact_tile, bool fold,
-                            const Smooth sm, int code_bits, uint8_t *__restrict__ out) {
+                            const Smooth sm, int code_bits, uint8_t *__restrict__ out,
+                            int64_t phase, int64_t n_phases) {
   using K = Consts<SD, kTerms<SD, SCALED>>;
   using OpT = Op<SD, SCALED>;
   const int lane = threadIdx.x & 63;
@@ -735,6 +754,8 @@ __device__ void encode_tile(const uint32_t (&xin)[T][4], int64_t tbase, int64_t 
       stage1(std::false_type{});
     }
   }
+
+  set_progress_priority(phase + 1, n_phases);
 
   // the fp32 sub-vector of column t (smoothed keys: times the factors)
   auto column_value = [&](int t, float (&xv)[SD]) {
@@ -954,8 +975,10 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
           (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len, fold);
       staged = slot;
     }
+    set_progress_priority(2 * (tile - first), 2 * (last - first));
     encode_tile<SD, T, BLOCK, BF16, ROWS32, SCALED>(xw, tbase, gend, n_c, n_cpad, s, exact_tile,
-                                                    fold, sm, code_bits, out);
+                                                    fold, sm, code_bits, out, 2 * (tile - first),
+                                                    2 * (last - first));
   }
 }
 

@@ -285,12 +285,13 @@ __device__ __forceinline__ float pair_sum(float v) {
 //                           (same position in different groups) fall on
 //                           different LDS banks;
 //   hash [hash_slots] uint  duplicate detection while staging;
-//   flags [16] int          per-wave staging flags;
+//   flags [16] int          per-wave staging flags, then the unit counter;
 //   scale [head_dim] float  the slot's channel factors (smoothed keys only).
 // gan is padded to a multiple of 4 floats so every region is 16-byte aligned.
 template <int SD, bool ROWS32>
 struct Lds {
   static constexpr int kFlags = 16;  // one per wave, at most 1024 threads
+  static constexpr int kCounter = kFlags;  // flags[kCounter]: next unit of the segment
   uint4 *rows;
   float *cval;
   float *gan;
@@ -311,12 +312,12 @@ struct Lds {
     c32 = gan + gan_len(n_cpad);
     hash = reinterpret_cast<uint32_t *>(c32 + c32_len(n_cpad));
     flags = reinterpret_cast<int *>(hash + hash_slots);
-    scale = reinterpret_cast<float *>(flags + kFlags);
+    scale = reinterpret_cast<float *>(flags + kFlags + 4);
   }
   static size_t bytes(int n_cpad, int hash_slots, int scale_len) {
     return static_cast<size_t>(n_cpad) * (16 + 4) + static_cast<size_t>(c32_len(n_cpad)) * 4 +
            static_cast<size_t>(gan_len(n_cpad)) * 4 + static_cast<size_t>(hash_slots) * 4 +
-           kFlags * 4 + static_cast<size_t>(scale_len) * 4;
+           (kFlags + 4) * 4 + static_cast<size_t>(scale_len) * 4;
   }
 };
 
@@ -366,8 +367,8 @@ __device__ __forceinline__ float group_max(float v) {
 
 // Stage one codebook slot (and, for smoothed keys, its channel factors).
 // Returns true when some centroid has a non-finite or huge norm: then every
-// sub-vector of the slot takes the full exact scan.  Two barriers: one after
-// the rows are written, one after duplicate rows are marked.
+// sub-vector of the slot takes the full exact scan.  One barrier, after the
+// rows are written; duplicate rows are marked after it.
 template <int SD, int NT, bool BF16, bool ROWS32, int BLOCK, bool FOLD>
 __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_cpad,
                                const Lds<SD, ROWS32> &s, int hash_slots,
@@ -444,6 +445,12 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
     // it, every later one lowers it to the smaller index with an atomic min,
     // and whichever of the two indices is larger is a duplicate.  So every
     // copy but the first is marked, and never the first.
+    // No barrier follows: the marks may land while other waves already run
+    // stage 1.  Either value of a marked word is valid there (a duplicate's
+    // own C, or +inf, which drops a row that can never win), and every mark
+    // is one 32-bit store; marks only make fewer sub-vectors ambiguous.  The
+    // rows' x, y words (all the comparisons read at sub_dim 4) are never
+    // written.
     const uint32_t mask = static_cast<uint32_t>(hash_slots - 1);
     for (int r = tid; r < n_c; r += BLOCK) {
       const uint4 q = s.rows[r];
@@ -463,7 +470,6 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
         slot = (slot + 1) & mask;
       }
     }
-    __syncthreads();
   }
   return exact;
 }
@@ -532,40 +538,21 @@ __device__ __forceinline__ void factors(const Lds<SD, ROWS32> &s, int m, float (
   }
 }
 
-// Wave priority from progress: the waves of a CU share its SIMDs, and the
-// issue arbiter prefers the oldest wave among equals, so without this the
-// first workgroup of a CU finishes far ahead of the last and the CU runs its
-// tail with few waves.  A wave that has done phase p of n (two phases per
-// tile) drops to level 3 - 4p/n, so waves that fall behind are preferred.
-__device__ __forceinline__ void set_progress_priority(int64_t phase, int64_t n_phases) {
-  const int64_t lvl = 3 - (4 * phase) / n_phases;
-  if (lvl >= 3) {
-    __builtin_amdgcn_s_setprio(3);
-  } else if (lvl == 2) {
-    __builtin_amdgcn_s_setprio(2);
-  } else if (lvl == 1) {
-    __builtin_amdgcn_s_setprio(1);
-  } else {
-    __builtin_amdgcn_s_setprio(0);
-  }
-}
-
 // Channel layout of smoothed keys: row r is sub-slot r mod n_sub of its key.
 struct Smooth {
   int n_sub;
   float inv_n_sub;
 };
 
-// Raw words of the T sub-vectors this lane loads for a tile: column t, row
-// tbase + (wave T + t) 32 + lane mod 32 (zero past the group's end).
+// Raw words of the T sub-vectors this lane loads for a unit: column t, row
+// ubase + 32 t + lane mod 32 (zero past the group's end).
 template <int SD, int T>
-__device__ __forceinline__ void load_tile_x(const uint16_t *__restrict__ x, int64_t tbase,
+__device__ __forceinline__ void load_unit_x(const uint16_t *__restrict__ x, int64_t ubase,
                                             int64_t gend, uint32_t (&w)[T][4]) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int64_t row = tbase + (wave * T + t) * 32 + (lane & 31);
+    const int64_t row = ubase + t * 32 + (lane & 31);
     w[t][0] = w[t][1] = w[t][2] = w[t][3] = 0;
     if (row < gend) {
       if constexpr (SD == 4) {
@@ -583,17 +570,16 @@ __device__ __forceinline__ void load_tile_x(const uint16_t *__restrict__ x, int6
   }
 }
 
-// One tile: every wave encodes T columns of 32 sub-vectors (raw words from
-// load_tile_x).
-template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
-__device__ void encode_tile(const uint32_t (&xin)[T][4], int64_t tbase, int64_t gend, int n_c,
+// One unit: the wave encodes T columns of 32 sub-vectors, rows ubase ..
+// ubase + 32 T - 1 (raw words from load_unit_x).
+template <int SD, int T, bool BF16, bool ROWS32, bool SCALED>
+__device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t gend, int n_c,
                             int n_cpad, const Lds<SD, ROWS32> &s, bool exact_tile, bool fold,
-                            const Smooth sm, int code_bits, uint8_t *__restrict__ out,
-                            int64_t phase, int64_t n_phases) {
+                            const Smooth sm, int sub0, int code_bits,
+                            uint8_t *__restrict__ out) {
   using K = Consts<SD, kTerms<SD, SCALED>>;
   using OpT = Op<SD, SCALED>;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;  // half of the block's rows / K slots this lane holds
   const int col = lane & 31;
   const int nblk = n_cpad / 32;
@@ -605,12 +591,8 @@ __device__ void encode_tile(const uint32_t (&xin)[T][4], int64_t tbase, int64_t 
   float m1[T], m2[T];
   int g1[T];
   uint32_t codes[T];
-  int m0 = 0;    // smoothed keys: sub-slot of this lane's column 0
-  if constexpr (SCALED) {
-    const int64_t first = tbase + wave * T * 32 + col;
-    m0 = mod_small(static_cast<int>(tbase % sm.n_sub) + static_cast<int>(first - tbase), sm.n_sub,
-                   sm.inv_n_sub);
-  }
+  // smoothed keys: sub-slot of this lane's column 0 (sub0 = ubase mod n_sub)
+  const int m0 = SCALED ? mod_small(sub0 + col, sm.n_sub, sm.inv_n_sub) : 0;
   uint32_t full_bits = 0;  // bit t: column t takes the full exact scan
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -731,19 +713,47 @@ __device__ void encode_tile(const uint32_t (&xin)[T][4], int64_t tbase, int64_t 
   const f32x16 zero16 = {};
 
   // ---- stage 1: group lower bounds on the matrix cores ---------------------
+  // With C folded into the product (no accumulator input) there are
+  // registers for two accumulators: the matrix cores compute column t + 1
+  // while the VALU reduces column t, and the next block's A operand and norm
+  // bound are loaded one block ahead.  Otherwise one accumulator is reused.
   auto stage1 = [&](auto folded) {
     constexpr bool F = decltype(folded)::value;
+    OpT aop = a_operand(0);
+    float an = s.gan[h];
     for (int blk = 0; blk < nblk; ++blk) {
-      const OpT aop = a_operand(blk);
+      const OpT a_cur = aop;
+      const float an_cur = an;
       const f32x16 cop = F ? zero16 : c_operand(blk);
-      const float an = s.gan[2 * blk + h];
+      if constexpr (F) {
+        const int nxt = min(blk + 1, nblk - 1);
+        aop = a_operand(nxt);
+        an = s.gan[2 * nxt + h];
+      } else if (blk + 1 < nblk) {
+        aop = a_operand(blk + 1);
+        an = s.gan[2 * blk + 2 + h];
+      }
       const int grp = 2 * blk + h;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
+      auto track = [&](int t, float mb) {
         m2[t] = __builtin_amdgcn_fmed3f(m1[t], m2[t], mb);
         g1[t] = (mb < m1[t]) ? grp : g1[t];
         m1[t] = __builtin_amdgcn_fmed3f(m1[t], mb, kNegMax);
+      };
+      if constexpr (F && T > 1) {
+        f32x16 acc[2];
+        acc[0] = mfma<BF16>(a_cur, bop[0], cop);
+        acc[1] = mfma<BF16>(a_cur, bop[1], cop);
+        unroll<T>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          const float mb = __builtin_fmaf(-an_cur, bn[t], min16(acc[t & 1]));
+          if constexpr (t + 2 < T) acc[t & 1] = mfma<BF16>(a_cur, bop[t + 2], cop);
+          track(t, mb);
+        });
+      } else {
+        unroll<T>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          track(t, __builtin_fmaf(-an_cur, bn[t], min16(mfma<BF16>(a_cur, bop[t], cop))));
+        });
       }
     }
   };
@@ -754,8 +764,6 @@ __device__ void encode_tile(const uint32_t (&xin)[T][4], int64_t tbase, int64_t 
       stage1(std::false_type{});
     }
   }
-
-  set_progress_priority(phase + 1, n_phases);
 
   // the fp32 sub-vector of column t (smoothed keys: times the factors)
   auto column_value = [&](int t, float (&xv)[SD]) {
@@ -896,9 +904,9 @@ __device__ void encode_tile(const uint32_t (&xin)[T][4], int64_t tbase, int64_t 
   if constexpr (SCALED) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
-      store_codes32(codes[t], tbase + (wave * T + t) * 32, gend, code_bits, h == 0, out);
+      store_codes32(codes[t], ubase + t * 32, gend, code_bits, h == 0, out);
   } else if (h == 0) {
-    const int64_t row0 = tbase + wave * T * 32 + col;
+    const int64_t row0 = ubase + col;
     if (code_bits == 32) {
 #pragma unroll
       for (int t = 0; t < T; ++t)
@@ -916,19 +924,23 @@ __device__ void encode_tile(const uint32_t (&xin)[T][4], int64_t tbase, int64_t 
   }
 }
 
-// Persistent workgroups: workgroup w encodes tiles [w*k, (w+1)*k) of the
-// group-major tile sequence and stages a codebook slot only when it changes.
-// At least 4 waves per SIMD (at most 128 VGPRs): the matrix-core stream and
-// the VALU stream of different waves overlap only with that many.
+// One workgroup of BLOCK threads per CU.  Workgroup w owns units [w k,
+// (w + 1) k) of the group-major unit sequence (a unit = 32 T consecutive
+// sub-vectors of one group, encoded by one wave), split into segments of one
+// group each.  Per segment the codebook slot is staged once, then the waves
+// take units from a counter in LDS: a wave that runs ahead takes more units,
+// so all waves of the CU finish close together (the issue arbiter favours
+// the oldest waves, which would otherwise finish far ahead of the others).
 template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
-__global__ void __launch_bounds__(BLOCK, 4)
+__global__ void __launch_bounds__(BLOCK, 1)
 encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ codebook,
                    int64_t n, int n_c, int64_t cb_stride, int64_t n_codebooks, int64_t group_len,
-                   int64_t tiles_per_group, int64_t total_tiles, int64_t tiles_per_wg,
+                   int64_t units_per_group, int64_t total_units, int64_t units_per_wg,
                    const int32_t *__restrict__ group_map, uint8_t *__restrict__ out,
                    int hash_slots, const float *__restrict__ scale, int64_t scale_stride,
                    int head_dim, int code_bits) {
-  constexpr int kTile = (BLOCK / 64) * T * 32;
+  constexpr int kWaves = BLOCK / 64;
+  constexpr int kUnit = T * 32;
   extern __shared__ uint4 lds_raw[];
   const int n_cpad = (n_c + 31) & ~31;
   const Lds<SD, ROWS32> s(lds_raw, n_cpad, hash_slots);
@@ -939,59 +951,76 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     sm.inv_n_sub = 1.0f / static_cast<float>(sm.n_sub);
   }
   const int wave = threadIdx.x >> 6;
-  const int h = (threadIdx.x >> 5) & 1;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  int *counter = s.flags + s.kCounter;
 
-  const int64_t first = static_cast<int64_t>(blockIdx.x) * tiles_per_wg;
-  const int64_t last = min(first + tiles_per_wg, total_tiles);
-  int64_t staged = -1;
-  bool exact_tile = false, fold = false;
-  for (int64_t tile = first; tile < last; ++tile) {
-    const int64_t g = tile / tiles_per_group;
+  const int64_t u_first = static_cast<int64_t>(blockIdx.x) * units_per_wg;
+  const int64_t u_last = min(u_first + units_per_wg, total_units);
+  bool first_seg = true;
+  for (int64_t seg = u_first; seg < u_last;) {  // uniform
+    const int64_t g = seg / units_per_group;
+    const int64_t g_unit0 = g * units_per_group;
+    const int64_t seg_end = min(u_last, g_unit0 + units_per_group);
     const int64_t gstart = g * group_len;
     const int64_t gend = min(gstart + group_len, n);
-    const int64_t tbase = gstart + (tile - g * tiles_per_group) * kTile;
-    if (tbase >= gend) continue;  // uniform: tile past a short group's end
+    const int seg_sub0 = SCALED ? static_cast<int>(gstart % sm.n_sub) : 0;
     const int64_t slot = group_map ? static_cast<int64_t>(group_map[g]) : g;
-    if (slot < 0 || slot >= n_codebooks) {
-      if constexpr (SCALED) {
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-          store_codes32(0xFFFFFFFFu, tbase + (wave * T + t) * 32, gend, code_bits, h == 0, out);
-      } else {
-        // all-one codes of 1, 2 or 4 bytes: every byte of the range is 0xFF
-        const int64_t bpc = code_bits / 8;
-        const int64_t bend = min(tbase + kTile, gend) * bpc;
-        for (int64_t b = tbase * bpc + threadIdx.x; b < bend; b += BLOCK) out[b] = 0xFFu;
-      }
-      continue;  // uniform
-    }
-    // the tile's loads are issued first, so that they overlap the staging
+    const bool bad = slot < 0 || slot >= n_codebooks;
+    // the first unit of every wave is fixed; its loads overlap the staging
+    int64_t u = seg + wave;
     uint32_t xw[T][4];
-    load_tile_x<SD, T>(x, tbase, gend, xw);
-    if (slot != staged) {
-      if (staged >= 0) __syncthreads();  // every wave is done with the previous slot
+    if (!bad && u < seg_end) load_unit_x<SD, T>(x, gstart + (u - g_unit0) * kUnit, gend, xw);
+    if (!first_seg) __syncthreads();  // every wave is done with the previous segment
+    first_seg = false;
+    if (threadIdx.x == 0) *counter = kWaves;
+    bool exact_tile = false, fold = false;
+    if (!bad) {
+      // its barrier also publishes the counter
       exact_tile = stage_codebook<SD, kTerms<SD, SCALED>, BF16, ROWS32, BLOCK, kFold<SD, SCALED>>(
           codebook + slot * cb_stride, n_c, n_cpad, s, hash_slots,
           (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len, fold);
-      staged = slot;
+    } else {
+      __syncthreads();
     }
-    set_progress_priority(2 * (tile - first), 2 * (last - first));
-    encode_tile<SD, T, BLOCK, BF16, ROWS32, SCALED>(xw, tbase, gend, n_c, n_cpad, s, exact_tile,
-                                                    fold, sm, code_bits, out, 2 * (tile - first),
-                                                    2 * (last - first));
+    while (u < seg_end) {  // uniform per wave
+      const int64_t ubase = gstart + (u - g_unit0) * kUnit;
+      if (bad) {
+        // a bad slot: all-one codes
+        if constexpr (SCALED) {
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            store_codes32(0xFFFFFFFFu, ubase + t * 32, gend, code_bits, h == 0, out);
+        } else {
+          const int64_t bpc = code_bits / 8;
+          const int64_t bend = min(ubase + kUnit, gend) * bpc;
+          for (int64_t b = ubase * bpc + lane; b < bend; b += 64) out[b] = 0xFFu;
+        }
+      } else {
+        int sub0 = 0;
+        if constexpr (SCALED) {
+          const uint32_t off = static_cast<uint32_t>(u - g_unit0) * kUnit % static_cast<uint32_t>(sm.n_sub);
+          sub0 = mod_small(seg_sub0 + static_cast<int>(off), sm.n_sub, sm.inv_n_sub);
+        }
+        encode_unit<SD, T, BF16, ROWS32, SCALED>(xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold,
+                                                 sm, sub0, code_bits, out);
+      }
+      int next = 0;
+      if (lane == 0) next = atomicAdd(counter, 1);
+      u = seg + __builtin_amdgcn_readfirstlane(next);
+      if (!bad && u < seg_end) load_unit_x<SD, T>(x, gstart + (u - g_unit0) * kUnit, gend, xw);
+    }
+    seg = seg_end;
   }
 }
-
-template <int BLOCK>
-constexpr int tile_of(int T) { return (BLOCK / 64) * T * 32; }
 
 template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
 hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_map, void *out,
                     const Layout &l, const Codes &codes, hipStream_t stream, int64_t cus) {
-  constexpr int kTile = tile_of<BLOCK>(T);
+  constexpr int kUnit = T * 32;
   const int64_t span = l.group_len < l.n ? l.group_len : l.n;
-  const int64_t tiles_per_group = (span + kTile - 1) / kTile;
-  const int64_t total_tiles = tiles_per_group * l.n_groups;
+  const int64_t units_per_group = (span + kUnit - 1) / kUnit;
+  const int64_t total_units = units_per_group * l.n_groups;
   const int n_cpad = (l.n_centroids + 31) & ~31;
   int hash_slots = 64;
   while (hash_slots < 2 * l.n_centroids) hash_slots <<= 1;
@@ -1003,17 +1032,14 @@ hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_ma
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, BLOCK, lds);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1) per_cu = 1;
-  const int64_t wgs = std::min<int64_t>(total_tiles, cus * per_cu);
-  const int64_t tiles_per_wg = (total_tiles + wgs - 1) / wgs;
-  const int64_t grid = (total_tiles + tiles_per_wg - 1) / tiles_per_wg;
+  // one workgroup per CU (small inputs: fewer units than waves per workgroup,
+  // spread over more CUs)
+  const int64_t units_per_wg = (total_units + cus - 1) / cus;
+  const int64_t grid = (total_units + units_per_wg - 1) / units_per_wg;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(BLOCK), lds, stream,
                      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(codebook),
                      l.n, l.n_centroids, l.codebook_stride, l.n_codebooks, l.group_len,
-                     tiles_per_group, total_tiles, tiles_per_wg, group_map,
+                     units_per_group, total_units, units_per_wg, group_map,
                      static_cast<uint8_t *>(out), hash_slots, codes.scale, codes.scale_stride,
                      codes.head_dim, codes.code_bits);
   return hipGetLastError();
@@ -1043,7 +1069,7 @@ hipError_t launch_sd(const void *x, const void *codebook, const int32_t *group_m
   if (l.n_centroids > kRows32MaxCentroids)
     return launch_t<SD, columns<SD, SCALED, false>(), 1024, BF16, false, SCALED>(
         x, codebook, group_map, out, l, codes, stream, cus);
-  return launch_t<SD, columns<SD, SCALED, true>(), 256, BF16, true, SCALED>(
+  return launch_t<SD, columns<SD, SCALED, true>(), 1024, BF16, true, SCALED>(
       x, codebook, group_map, out, l, codes, stream, cus);
 }
 
@@ -1064,10 +1090,9 @@ hipError_t launch_scaled(const void *x, const void *codebook, const int32_t *gro
 bool encode_mfma_supported(const Layout &l) { return l.n_centroids <= kMfmaMaxCentroids; }
 
 int64_t encode_mfma_grid(const Layout &l) {
-  // upper bound on the workgroups of any plan above (one tile per workgroup)
-  const int64_t tile = tile_of<256>(1);
+  // upper bound on the workgroups of any plan above (one 64-row unit each)
   const int64_t span = l.group_len < l.n ? l.group_len : l.n;
-  return (span + tile - 1) / tile * l.n_groups;
+  return (span + 63) / 64 * l.n_groups;
 }
 
 hipError_t launch_encode_mfma(const void *x, const void *codebook, const int32_t *group_map,

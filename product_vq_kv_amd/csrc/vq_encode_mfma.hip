@@ -86,14 +86,21 @@ struct Consts {
 };
 
 // Plain sub_dim 4 leaves K slots 4..7 of the matrix-core dot empty; they
-// carry C instead ("folded"): A = [-c, C_hi, C_lo, 0, 0], B = [x, 1, 1, 0, 0],
-// so the accumulator input is zero and C need not be loaded per block.
+// carry C and the error term instead ("folded"): A = [-c, C_hi, C_lo, -a', 0],
+// B = [x, 1, 1, b', 0], where a' >= kFoldScale a(g) (g the row's group) and
+// b' >= b(x) / kFoldScale are element-type values rounded up, so a' b' >=
+// a(g) b(x) and the dot is already the group's lower bound: the accumulator
+// input is zero, and neither C nor a(g) is loaded per block.
 template <int SD, bool SCALED>
 constexpr bool kFold = (SD == 4 && !SCALED);
+// In fp16 a folded slot has C_hi finite, so |c| <= 362 and a(g) < 2^-11,
+// and fp16 keys have |x| < 2^18: with the scale, a' < 1 and b' < 2^8.  In
+// bf16 both stay far inside the range (|c|, |x| < 2^50).
+constexpr float kFoldScale = 1024.0f;
 
 // Products per matrix-core dot for the error bound.
 template <int SD, bool SCALED>
-constexpr int kTerms = SCALED ? 2 * SD : (kFold<SD, SCALED> ? SD + 1 : SD);
+constexpr int kTerms = SCALED ? 2 * SD : (kFold<SD, SCALED> ? SD + 2 : SD);
 
 template <bool BF16>
 constexpr uint16_t kInfBits = BF16 ? 0x7F80 : 0x7C00;
@@ -123,6 +130,14 @@ __device__ __forceinline__ uint16_t narrow(float v) {
   } else {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
   }
+}
+
+// Smallest element-type value >= v, for v >= 0 (+inf when v exceeds the
+// largest finite value).
+template <bool BF16>
+__device__ __forceinline__ uint16_t round_up(float v) {
+  const uint16_t b = narrow<BF16>(v);
+  return (widen<BF16>(b) < v) ? static_cast<uint16_t>(b + 1u) : b;
 }
 
 // C = hi + lo with hi = rn(C) and lo = C - hi rounded toward -inf (C - hi is
@@ -413,8 +428,9 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
     an = group_max(an);
     if (r < n_cpad) {
       if ((lane & 0x1B) == 0) s.gan[group_of(r)] = an;
-      if constexpr (FOLD) {  // halves 4, 5 carry C (SD == 4)
+      if constexpr (FOLD) {  // halves 4, 5 carry C, half 6 carries -a' (SD == 4)
         if (!split_down<BF16>(cv, k8[4], k8[5])) nofold = 1;
+        k8[6] = round_up<BF16>(an * kFoldScale) ^ 0x8000u;
       }
       s.rows[r] = make_uint4(k8[0] | (static_cast<uint32_t>(k8[1]) << 16),
                              k8[2] | (static_cast<uint32_t>(k8[3]) << 16),
@@ -675,7 +691,8 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       if constexpr (SD == 4) {
         // folded slots: the h = 1 half multiplies C_hi, C_lo by (1, 1)
         bop[t] = (h == 0) ? make_uint2(w[0], w[1])
-                          : make_uint2(fold ? kOnePair<BF16> : 0u, 0u);
+                          : make_uint2(fold ? kOnePair<BF16> : 0u,
+                                       fold ? round_up<BF16>(bn[t] * (1.0f / kFoldScale)) : 0u);
       } else {
         bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(w[2], w[3]);
       }
@@ -711,6 +728,13 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
 
   // accumulator input of block blk: C from LDS, or zero when C is folded
   const f32x16 zero16 = {};
+  // lower bound of this lane's group of block blk for column t (recomputed)
+  auto group_bound = [&](int blk, int t) {
+    const OpT aop = a_operand(blk);
+    if (kFold<SD, SCALED> && fold) return min16(mfma<BF16>(aop, bop[t], zero16));
+    const float an = s.gan[2 * blk + h];
+    return __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], c_operand(blk))));
+  };
 
   // ---- stage 1: group lower bounds on the matrix cores ---------------------
   // With C folded into the product (no accumulator input) there are
@@ -720,15 +744,13 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
   auto stage1 = [&](auto folded) {
     constexpr bool F = decltype(folded)::value;
     OpT aop = a_operand(0);
-    float an = s.gan[h];
+    float an = F ? 0.0f : s.gan[h];
     for (int blk = 0; blk < nblk; ++blk) {
       const OpT a_cur = aop;
       const float an_cur = an;
       const f32x16 cop = F ? zero16 : c_operand(blk);
       if constexpr (F) {
-        const int nxt = min(blk + 1, nblk - 1);
-        aop = a_operand(nxt);
-        an = s.gan[2 * nxt + h];
+        aop = a_operand(min(blk + 1, nblk - 1));
       } else if (blk + 1 < nblk) {
         aop = a_operand(blk + 1);
         an = s.gan[2 * blk + 2 + h];
@@ -739,13 +761,14 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
         g1[t] = (mb < m1[t]) ? grp : g1[t];
         m1[t] = __builtin_amdgcn_fmed3f(m1[t], mb, kNegMax);
       };
-      if constexpr (F && T > 1) {
+      if constexpr (F) {
+        // the error term is in the product: the group minimum is the bound
         f32x16 acc[2];
         acc[0] = mfma<BF16>(a_cur, bop[0], cop);
-        acc[1] = mfma<BF16>(a_cur, bop[1], cop);
+        if constexpr (T > 1) acc[1] = mfma<BF16>(a_cur, bop[1], cop);
         unroll<T>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
-          const float mb = __builtin_fmaf(-an_cur, bn[t], min16(acc[t & 1]));
+          const float mb = min16(acc[t & 1]);
           if constexpr (t + 2 < T) acc[t & 1] = mfma<BF16>(a_cur, bop[t + 2], cop);
           track(t, mb);
         });
@@ -850,10 +873,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       int q0 = -1, q1 = -1;
       bool over = false;
       for (int blk = 0; blk < nblk; ++blk) {
-        const OpT aop = a_operand(blk);
-        const f32x16 cop = (kFold<SD, SCALED> && fold) ? zero16 : c_operand(blk);
-        const float an = s.gan[2 * blk + h];
-        const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
+        const float mb = group_bound(blk, t);
         const int grp = 2 * blk + h;
         if (amb && mb <= U) {
           over = over || q1 >= 0;
@@ -869,10 +889,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       }
       if (__any(over)) {
         for (int blk = 0; blk < nblk; ++blk) {
-          const OpT aop = a_operand(blk);
-          const f32x16 cop = (kFold<SD, SCALED> && fold) ? zero16 : c_operand(blk);
-          const float an = s.gan[2 * blk + h];
-          const float mb = __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], cop)));
+          const float mb = group_bound(blk, t);
           if (over && mb <= U) exact_group<SD, BF16, ROWS32>(s, xv, 2 * blk + h, n_c, fb, fi);
         }
       }

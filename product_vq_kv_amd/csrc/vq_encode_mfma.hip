@@ -83,6 +83,13 @@ struct Consts {
   static constexpr float kInvKappaUp = (1.0f / kKappa) * 1.0000152587890625f;  // >= 1/kappa
   static constexpr float kHalfShrink = 0.5f * (1.0f - kEta - 9.5367431640625e-07f);
   static constexpr float kGamma2 = 2.0f * (SD + 2) * kU * 1.01f;  // >= 1/(1-gamma) - 1
+  // U = fma(best, kUA, fma(n2x, -kUB, kTau)) >= (best (1 + kGamma2) - |x|^2_low) / 2
+  // with |x|^2_low = n2x (1 - (SD + 2) u) <= |x|^2: kUB carries 8u less than
+  // the exact factor and kUA 8u more, which covers the two roundings (each at
+  // most u of its result's magnitude, plus 2^-150 absolute, inside kTau) and
+  // the rounding of the constants themselves.
+  static constexpr float kUA = 0.5f * (1.0f + kGamma2) * (1.0f + 8.0f * kU);
+  static constexpr float kUB = 0.5f * (1.0f - (SD + 2) * kU) * (1.0f - 8.0f * kU);
 };
 
 // Plain sub_dim 4 leaves K slots 4..7 of the matrix-core dot empty; they
@@ -132,12 +139,37 @@ __device__ __forceinline__ uint16_t narrow(float v) {
   }
 }
 
+// Upper bound of sqrt(v) for 0 <= v <= 2^100 (no correctly rounded square
+// root is needed): the hardware square root is within 1 ulp for normal
+// inputs, which kNormUp (1 + 2^-18) covers many times over, and below the
+// normal range sqrt(v) < 2^-63, covered by the floor.
+__device__ __forceinline__ float sqrt_up(float v) {
+  return fmaxf(__builtin_amdgcn_sqrtf(v) * kNormUp, 2.168404344971009e-19f /* 2^-62 */);
+}
+
+// The B value b' >= b / kFoldScale of the folded error term (b >= 0).  fp16:
+// one fused multiply-add rounded once to fp16; the 2^-10 relative and 2^-24
+// absolute margins exceed fp16's rounding error in the normal (2^-11
+// relative) and subnormal (2^-25 absolute) ranges.
+template <bool BF16>
+__device__ __forceinline__ uint16_t fold_b(float b);
+
 // Smallest element-type value >= v, for v >= 0 (+inf when v exceeds the
 // largest finite value).
 template <bool BF16>
 __device__ __forceinline__ uint16_t round_up(float v) {
   const uint16_t b = narrow<BF16>(v);
   return (widen<BF16>(b) < v) ? static_cast<uint16_t>(b + 1u) : b;
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint16_t fold_b(float b) {
+  if constexpr (BF16) {
+    return round_up<true>(b * (1.0f / kFoldScale));
+  } else {
+    constexpr float k = (1.0f / kFoldScale) * (1.0f + 1.0f / 1024.0f);
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(__builtin_fmaf(b, k, 5.960464477539063e-08f)));
+  }
 }
 
 // C = hi + lo with hi = rn(C) and lo = C - hi rounded toward -inf (C - hi is
@@ -422,7 +454,7 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
         flag = 1;
       } else {
         cv = n2c * K::kHalfShrink - 2.0f * kTau;
-        an = __builtin_sqrtf(n2c) * kNormUp * K::kKappa;
+        an = sqrt_up(n2c) * K::kKappa;
       }
     }
     an = group_max(an);
@@ -495,6 +527,44 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
 // visited in ascending order; the index recorded for row c0 + i is k0 + i.
 // With MASK, rows >= n_c (the padding of the last block) are excluded;
 // without it every row is < n_c.
+// The 8 rows of group grp that lane half h evaluates in the exact stage:
+// rows c0 .. c0 + 3 and c0 + 8 .. c0 + 11, c0 = 32 (grp / 2) + 16 h + 4 (grp
+// mod 2), in ascending order; bk gets the offset (0..3, 8..11) of the
+// strict-< minimum.
+template <int SD, bool BF16, bool ROWS32, bool MASK>
+__device__ __forceinline__ void exact8(const Lds<SD, ROWS32> &s, const float (&xv)[SD], int grp,
+                                       int h, int n_c, float &best, int &bk) {
+  const int b = grp >> 1, hh = grp & 1;
+  const int c0 = b * 32 + h * 16 + hh * 4;
+  // c32_offset(c0), spelled out: the row set's padding is 4 (c0 / 4 + c0 / 32)
+  const float *base = s.c32 + b * (32 * SD + 36) + h * (16 * SD + 16) + hh * (4 * SD + 4);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k = (j & 3) + ((j & 4) << 1);
+    const int c = c0 + k;
+    float cv[SD];
+    if constexpr (ROWS32) {
+      // the second row set (k >= 8) is 2 sets further: 8 rows and 8 floats
+      const float *row = base + SD * (k & 3) + ((k & 8) ? (8 * SD + 8) : 0);
+#pragma unroll
+      for (int q = 0; q < SD / 4; ++q) {
+        const float4 w = *reinterpret_cast<const float4 *>(row + 4 * q);
+        cv[4 * q] = w.x;
+        cv[4 * q + 1] = w.y;
+        cv[4 * q + 2] = w.z;
+        cv[4 * q + 3] = w.w;
+      }
+    } else {
+      centroid_in_set<SD, BF16, ROWS32>(s, c0 + (k & 8), k & 3, cv);
+    }
+    float d = sqdist<SD>(xv, cv);
+    if (MASK) d = (c < n_c) ? d : __builtin_inff();
+    const bool lt = d < best;
+    best = lt ? d : best;
+    bk = lt ? k : bk;
+  }
+}
+
 template <int SD, bool BF16, bool ROWS32, bool MASK>
 __device__ __forceinline__ void exact4(const Lds<SD, ROWS32> &s, const float (&xv)[SD], int c0,
                                        int k0, int n_c, float &best, int &bk) {
@@ -668,7 +738,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       const bool ex = !fin || !(nv2 <= kNormCap) || exact_tile;
       full_bits |= (ex ? 1u : 0u) << t;
       bn[t] = ex ? 0.0f
-                 : __builtin_fmaf(esum, K::kInvKappaUp, __builtin_sqrtf(nv2) * kNormUp) * kBnUp;
+                 : __builtin_fmaf(esum, K::kInvKappaUp, sqrt_up(nv2)) * kBnUp;
       // components 0 .. E-1 come from lane h = 0, E .. SD-1 from lane h = 1
       if constexpr (SD == 4) {
         bop[t] = (h == 0) ? make_uint2(keep[0], got[0]) : make_uint2(got[0], keep[0]);
@@ -687,12 +757,12 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       nx2[t] = n2x;
       const bool ex = !(n2x <= kNormCap) || exact_tile;
       full_bits |= (ex ? 1u : 0u) << t;
-      bn[t] = ex ? 0.0f : __builtin_sqrtf(n2x) * kNormUp;
+      bn[t] = ex ? 0.0f : sqrt_up(n2x);
       if constexpr (SD == 4) {
         // folded slots: the h = 1 half multiplies C_hi, C_lo by (1, 1)
         bop[t] = (h == 0) ? make_uint2(w[0], w[1])
                           : make_uint2(fold ? kOnePair<BF16> : 0u,
-                                       fold ? round_up<BF16>(bn[t] * (1.0f / kFoldScale)) : 0u);
+                                       fold ? fold_b<BF16>(bn[t]) : 0u);
       } else {
         bop[t] = (h == 0) ? make_uint2(w[0], w[1]) : make_uint2(w[2], w[3]);
       }
@@ -827,17 +897,14 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     // rows of group cg1 (block b, half hh): b*32 + 8j + 4hh + i; this lane
     // takes j = 2h and 2h + 1 in ascending order, so every row of lane 0
     // precedes every row of lane 1
-    const int c0 = (cg1 >> 1) * 32 + 16 * h + 4 * (cg1 & 1);
     float best = __builtin_inff();
     int bk = 0;
     if (n_c & 31) {  // uniform: the last block has padding rows
-      exact4<SD, BF16, ROWS32, true>(s, xv, c0, 0, n_c, best, bk);
-      exact4<SD, BF16, ROWS32, true>(s, xv, c0 + 8, 4, n_c, best, bk);
+      exact8<SD, BF16, ROWS32, true>(s, xv, cg1, h, n_c, best, bk);
     } else {
-      exact4<SD, BF16, ROWS32, false>(s, xv, c0, 0, n_c, best, bk);
-      exact4<SD, BF16, ROWS32, false>(s, xv, c0 + 8, 4, n_c, best, bk);
+      exact8<SD, BF16, ROWS32, false>(s, xv, cg1, h, n_c, best, bk);
     }
-    int bi = c0 + (bk & 3) + ((bk & 4) << 1);
+    int bi = (cg1 >> 1) * 32 + 16 * h + 4 * (cg1 & 1) + bk;
     {
       const PairVals pd = pair_vals(__float_as_uint(best));
       const PairVals pi = pair_vals(static_cast<uint32_t>(bi));
@@ -853,11 +920,8 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     } else {
       n2x = nx2[t];
     }
-    const float xl = n2x * (1.0f - (SD + 2) * kU);
-    // s(c*) <= (best (1 + 2 gamma) - |x|^2) / 2; the two rounded operations
-    // below are covered by (best + xl) 2u, kTau covers subnormal steps.
-    float U = (best * (1.0f + K::kGamma2) - xl) * 0.5f;
-    U = U + (best + xl) * (2.0f * kU) + kTau;
+    // s(c*) <= (best (1 + 2 gamma) - |x|^2) / 2 <= U
+    const float U = __builtin_fmaf(best, K::kUA, __builtin_fmaf(n2x, -K::kUB, kTau));
     const bool full = ((full_bits >> t) & 1u) || !(best < __builtin_inff());
     const bool amb = !full && !(cm2 > U);
     codes[t] = static_cast<uint32_t>(bi);

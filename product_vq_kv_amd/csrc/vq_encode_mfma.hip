@@ -92,32 +92,35 @@ struct Consts {
   static constexpr float kUB = 0.5f * (1.0f - (SD + 2) * kU) * (1.0f - 8.0f * kU);
 };
 
-// Plain sub_dim 4 leaves K slots 4..7 of the matrix-core dot empty; they
-// carry C and the error term instead ("folded"): A = [-c, C_hi, C_lo, -a', 0],
-// B = [x, 1, 1, b', 0], where a' >= kFoldScale a(g) (g the row's group) and
-// b' >= b(x) / kFoldScale are element-type values rounded up, so a' b' >=
-// a(g) b(x) and the dot is already the group's lower bound: the accumulator
-// input is zero, and neither C nor a(g) is loaded per block.
+// Sub_dim 4 leaves K slots of the matrix-core dot empty; they carry C and
+// the error term instead ("folded").  Plain keys (K = 8): A = [-c, C_hi,
+// C_lo, -a', 0], B = [x, 1, 1, b', 0].  Smoothed keys (K = 16, the split
+// x~ = hi + lo + e): A = [-c, -c, C_hi, C_lo, -a', 0 x 5], B = [hi, lo, 1, 1,
+// b', 0 x 5].  a' >= kFoldScale a(g) (g the row's group) and b' >= b(x) /
+// kFoldScale are element-type values rounded up, so a' b' >= a(g) b(x) and
+// the dot is already the group's lower bound: the accumulator input is
+// zero, and neither C nor a(g) is loaded per block.
 template <int SD, bool SCALED>
-constexpr bool kFold = (SD == 4 && !SCALED);
+constexpr bool kFold = (SD == 4);
 // In fp16 a folded slot has C_hi finite, so |c| <= 362 and a(g) < 2^-11,
 // and fp16 keys have |x| < 2^18: with the scale, a' < 1 and b' < 2^8.  In
 // bf16 both stay far inside the range (|c|, |x| < 2^50).
 constexpr float kFoldScale = 1024.0f;
 
-// Products per matrix-core dot for the error bound.
+// Products per matrix-core dot for the error bound (one more term, the
+// accumulator input or the folded error term, is counted by Consts).
 template <int SD, bool SCALED>
-constexpr int kTerms = SCALED ? 2 * SD : (kFold<SD, SCALED> ? SD + 2 : SD);
+constexpr int kTerms = (SCALED ? 2 * SD : SD) + (kFold<SD, SCALED> ? 2 : 0);
 
 template <bool BF16>
 constexpr uint16_t kInfBits = BF16 ? 0x7F80 : 0x7C00;
 template <bool BF16>
 constexpr uint32_t kOnePair = BF16 ? 0x3F803F80u : 0x3C003C00u;  // (1, 1)
 
-// Matrix-core operands: 4 halves per lane (K = 8), or 8 (K = 16) for the
-// smoothed sub_dim 8 path.
+// Matrix-core operands: 4 halves per lane (K = 8), or 8 (K = 16) for
+// smoothed keys.
 template <int SD, bool SCALED>
-using Op = std::conditional_t<(SD == 8 && SCALED), uint4, uint2>;
+using Op = std::conditional_t<SCALED, uint4, uint2>;
 
 template <bool BF16>
 __device__ __forceinline__ float widen(uint16_t v) {
@@ -727,10 +730,12 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
         }
       }
       uint32_t keep[E / 2], got[E / 2];
+      if constexpr (SD == 8) {
 #pragma unroll
-      for (int q = 0; q < E / 2; ++q) {
-        keep[q] = (h == 0) ? hw[q] : lw[q];
-        got[q] = pair_other((h == 0) ? lw[q] : hw[q], h);
+        for (int q = 0; q < E / 2; ++q) {
+          keep[q] = (h == 0) ? hw[q] : lw[q];
+          got[q] = pair_other((h == 0) ? lw[q] : hw[q], h);
+        }
       }
       nv2 = pair_sum(nv2);
       esum = pair_sum(esum);
@@ -741,7 +746,13 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
                  : __builtin_fmaf(esum, K::kInvKappaUp, sqrt_up(nv2)) * kBnUp;
       // components 0 .. E-1 come from lane h = 0, E .. SD-1 from lane h = 1
       if constexpr (SD == 4) {
-        bop[t] = (h == 0) ? make_uint2(keep[0], got[0]) : make_uint2(got[0], keep[0]);
+        // folded (K = 16): lane 0 of the pair holds [hi, lo], lane 1 the
+        // slots of C and the error term
+        const PairVals ph = pair_vals(hw[0]);
+        const PairVals pl = pair_vals(lw[0]);
+        bop[t] = (h == 0) ? make_uint4(ph.first, ph.second, pl.first, pl.second)
+                          : make_uint4(fold ? kOnePair<BF16> : 0u,
+                                       fold ? fold_b<BF16>(bn[t]) : 0u, 0u, 0u);
         xw[t] = make_uint2(w[0], w[1]);
       } else {
         bop[t] = (h == 0) ? make_uint4(keep[0], keep[1], got[0], got[1])
@@ -778,7 +789,10 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     if constexpr (SCALED && SD == 8) {
       return s.rows[blk * 32 + col];
     } else if constexpr (SCALED) {
-      return reinterpret_cast<const uint2 *>(s.rows)[blk * 64 + 2 * col];
+      // K = 16: lane half 0 takes -c twice (against hi and lo), half 1 the
+      // row's C_hi, C_lo, -a'
+      const uint2 q = reinterpret_cast<const uint2 *>(s.rows)[blk * 64 + 2 * col + h];
+      return (h == 0) ? make_uint4(q.x, q.y, q.x, q.y) : make_uint4(q.x, q.y, 0u, 0u);
     } else {
       return reinterpret_cast<const uint2 *>(s.rows)[blk * 64 + 2 * col + h];
     }
@@ -1141,7 +1155,7 @@ int cu_count() {
 // Columns per wave: the smoothed sub_dim 8 form holds twice the operand
 // registers per column.
 template <int SD, bool SCALED, bool ROWS32>
-constexpr int columns() { return (SCALED && SD == 8) ? 2 : 4; }
+constexpr int columns() { return SCALED ? 2 : 4; }
 
 template <int SD, bool BF16, bool SCALED>
 hipError_t launch_sd(const void *x, const void *codebook, const int32_t *group_map, void *out,

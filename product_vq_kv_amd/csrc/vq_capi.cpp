@@ -166,7 +166,7 @@ vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
       reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
     return VQ_ERR_MISALIGNED;
   if (vqk::encode_grid(l) > kMaxGrid || vqk::encode_mfma_grid(l) > kMaxGrid ||
-      vqk::kmeans_grid(l) > kMaxGrid || n_codebooks * n_centroids / 256 + 1 > kMaxGrid)
+      vqk::kmeans_grid(l) > kMaxGrid || n_codebooks * n_centroids * sub_dim / 32 + 1 > kMaxGrid)
     return VQ_ERR_INVALID_ARG;
   (void)hipGetLastError();
   return device_result(vqk::launch_kmeans(x, codebook, group_map, out_idx, l, iterations,

@@ -10,26 +10,36 @@
 //               nearest even); a centroid without members keeps its value.
 // fp16 values are integer multiples of 2^-24, so member sums are exact int64
 // (|sum| < 2^40 * n); the sums are accumulated per workgroup in LDS with
-// 64-bit integer atomics and flushed with 64-bit global atomics, so the
-// result does not depend on the order of the additions, and the rounding of
-// sum / count is done exactly in integer arithmetic.
+// 64-bit integer atomics and flushed with 64-bit global atomics into one of
+// kReplicas copies of the sums (fewer workgroups contend for one address),
+// which the update adds up.  Integer addition is associative, so the result
+// does not depend on the order of the additions, and the rounding of sum /
+// count is done exactly in integer arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "vq_launch.h"
 
 namespace vqk {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerTile = 4096;      // rows per accumulate workgroup
+constexpr int kThreads = 256;        // update and clear workgroups
+constexpr int kAccThreads = 1024;    // accumulate workgroups
+constexpr int kRowsPerThread = 4;
+constexpr int kRowsPerTile = kAccThreads * kRowsPerThread;  // rows per accumulate workgroup
 constexpr int kLdsMaxCentroids = 512;   // beyond: accumulate straight to global
+constexpr int kReplicas = 8;            // copies of the sums the flush is spread over
 
-// x * 2^24 as an exact integer (fp16 x; non-finite values count as 0).
+// x * 2^24 as an exact integer (fp16 x; non-finite values count as 0): a
+// normal value (1024 + m) 2^(e - 25) gives (1024 + m) 2^(e - 1), a
+// subnormal m 2^-24 gives m.
 __device__ __forceinline__ int64_t units(uint16_t bits) {
-  const float v = static_cast<float>(__builtin_bit_cast(_Float16, bits));
-  if (!(__builtin_fabsf(v) <= 65504.0f)) return 0;
-  return static_cast<int64_t>(v * 16777216.0f);  // exact: 11 significant bits
+  const uint32_t e = (bits >> 10) & 31u, m = bits & 1023u;
+  uint64_t mag = (e == 0) ? m : (static_cast<uint64_t>(1024u | m) << (e - 1));
+  mag = (e == 31) ? 0 : mag;
+  return (bits & 0x8000u) ? -static_cast<int64_t>(mag) : static_cast<int64_t>(mag);
 }
 
 // fp16 bits of S / (n * 2^24) rounded to nearest even (n >= 1, |S| < 2^63).
@@ -66,15 +76,15 @@ struct KmArgs {
   const uint32_t *idx;
   uint16_t *codebook;
   const int32_t *group_map;
-  unsigned long long *sums;    // [n_codebooks][n_c][sd], two's complement
-  unsigned int *counts;        // [n_codebooks][n_c]
+  unsigned long long *sums;    // [kReplicas][n_codebooks][n_c][sd], two's complement
+  unsigned int *counts;        // [kReplicas][n_codebooks][n_c]
   int64_t n, cb_stride, n_codebooks, group_len, tiles_per_group;
   int sd, n_c;
 };
 
 // Member sums and counts of one tile of rows (one group, so one slot).
 template <int SD>
-__global__ void __launch_bounds__(kThreads) km_accumulate(const KmArgs a) {
+__global__ void __launch_bounds__(kAccThreads) km_accumulate(const KmArgs a) {
   extern __shared__ unsigned long long lsum[];  // [n_c][SD] then counts [n_c] (as u64)
   const int64_t tile = blockIdx.x;
   const int64_t g = tile / a.tiles_per_group;
@@ -85,21 +95,45 @@ __global__ void __launch_bounds__(kThreads) km_accumulate(const KmArgs a) {
   const int64_t slot = a.group_map ? static_cast<int64_t>(a.group_map[g]) : g;
   if (slot < 0 || slot >= a.n_codebooks) return;  // whole workgroup: no centroid to train
   const int64_t tend = min(tbase + kRowsPerTile, gend);
-  unsigned long long *gs = a.sums + slot * a.n_c * SD;
-  unsigned int *gc = a.counts + slot * a.n_c;
+  const int64_t cells = a.n_codebooks * a.n_c;
+  const int rep = static_cast<int>(blockIdx.x % kReplicas);
+  unsigned long long *gs = a.sums + rep * cells * SD + slot * a.n_c * SD;
+  unsigned int *gc = a.counts + rep * cells + slot * a.n_c;
   const bool use_lds = a.n_c <= kLdsMaxCentroids;
   unsigned long long *lcnt = lsum + a.n_c * SD;
   if (use_lds) {
-    for (int e = threadIdx.x; e < a.n_c * (SD + 1); e += kThreads) lsum[e] = 0;
+    for (int e = threadIdx.x; e < a.n_c * (SD + 1); e += kAccThreads) lsum[e] = 0;
     __syncthreads();
   }
-  for (int64_t r = tbase + threadIdx.x; r < tend; r += kThreads) {
-    const uint32_t c = a.idx[r];
-    if (c >= static_cast<uint32_t>(a.n_c)) continue;
-    const uint16_t *xr = a.x + r * SD;
+  // every load first (unconditional, from clamped rows), then the additions
+  using Row = std::conditional_t<SD == 4, uint2, uint4>;
+  uint32_t code[kRowsPerThread];
+  Row xr[kRowsPerThread];
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int64_t r = min(tbase + threadIdx.x + k * kAccThreads, tend - 1);
+    code[k] = a.idx[r];
+    xr[k] = reinterpret_cast<const Row *>(a.x)[r];
+  }
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int64_t r = tbase + threadIdx.x + k * kAccThreads;
+    const uint32_t c = code[k];
+    if (r >= tend || c >= static_cast<uint32_t>(a.n_c)) continue;
+    uint32_t w[SD / 2];
+    if constexpr (SD == 4) {
+      w[0] = xr[k].x;
+      w[1] = xr[k].y;
+    } else {
+      w[0] = xr[k].x;
+      w[1] = xr[k].y;
+      w[2] = xr[k].z;
+      w[3] = xr[k].w;
+    }
 #pragma unroll
     for (int i = 0; i < SD; ++i) {
-      const unsigned long long u = static_cast<unsigned long long>(units(xr[i]));
+      const uint16_t bits = static_cast<uint16_t>((i & 1) ? (w[i >> 1] >> 16) : w[i >> 1]);
+      const unsigned long long u = static_cast<unsigned long long>(units(bits));
       if (use_lds) {
         atomicAdd(&lsum[c * SD + i], u);
       } else {
@@ -114,35 +148,49 @@ __global__ void __launch_bounds__(kThreads) km_accumulate(const KmArgs a) {
   }
   if (use_lds) {
     __syncthreads();
-    for (int e = threadIdx.x; e < a.n_c * SD; e += kThreads)
+    for (int e = threadIdx.x; e < a.n_c * SD; e += kAccThreads)
       if (lsum[e]) atomicAdd(&gs[e], lsum[e]);
-    for (int c = threadIdx.x; c < a.n_c; c += kThreads)
+    for (int c = threadIdx.x; c < a.n_c; c += kAccThreads)
       if (lcnt[c]) atomicAdd(&gc[c], static_cast<unsigned int>(lcnt[c]));
   }
 }
 
-// New centroids from the sums (one thread per (slot, centroid)); the sums
-// and counts are cleared for the next iteration.
+// New centroids from the sums, one thread per (slot, centroid, component);
+// a workgroup holds whole centroids, and clears their sums and counts for
+// the next iteration once all of its threads have read them.
 template <int SD>
 __global__ void __launch_bounds__(kThreads) km_update(const KmArgs a) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= a.n_codebooks * a.n_c) return;
-  const int64_t slot = e / a.n_c;
-  const int c = static_cast<int>(e - slot * a.n_c);
-  const unsigned int cnt = a.counts[e];
-  uint16_t *cw = a.codebook + slot * a.cb_stride + static_cast<int64_t>(c) * SD;
+  const int64_t cells = a.n_codebooks * a.n_c;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * (kThreads / SD) + threadIdx.x / SD;
+  const int i = threadIdx.x % SD;
+  const bool live = e < cells;
+  unsigned int cnt = 0;
+  unsigned long long S = 0;  // two's complement: the sum wraps like int64
+  if (live) {
 #pragma unroll
-  for (int i = 0; i < SD; ++i) {
-    const int64_t S = static_cast<int64_t>(a.sums[e * SD + i]);
-    if (cnt > 0) cw[i] = round_mean_f16(S, cnt);
-    a.sums[e * SD + i] = 0;
+    for (int r = 0; r < kReplicas; ++r) {
+      cnt += a.counts[r * cells + e];
+      S += a.sums[(r * cells + e) * SD + i];
+    }
+    if (cnt > 0) {
+      const int64_t slot = e / a.n_c;
+      const int64_t c = e - slot * a.n_c;
+      a.codebook[slot * a.cb_stride + c * SD + i] = round_mean_f16(static_cast<int64_t>(S), cnt);
+    }
   }
-  a.counts[e] = 0;
+  __syncthreads();
+  if (live) {
+#pragma unroll
+    for (int r = 0; r < kReplicas; ++r) {
+      a.sums[(r * cells + e) * SD + i] = 0;
+      if (i == 0) a.counts[r * cells + e] = 0;
+    }
+  }
 }
 
 __global__ void __launch_bounds__(kThreads) km_clear(const KmArgs a) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t nc = a.n_codebooks * a.n_c;
+  const int64_t nc = kReplicas * a.n_codebooks * a.n_c;
   if (e < nc * a.sd) a.sums[e] = 0;
   if (e < nc) a.counts[e] = 0;
 }
@@ -150,7 +198,7 @@ __global__ void __launch_bounds__(kThreads) km_clear(const KmArgs a) {
 template <int SD>
 hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream_t stream) {
   const int64_t cells = a.n_codebooks * a.n_c;
-  const int64_t clear_blocks = (cells * SD + kThreads - 1) / kThreads;
+  const int64_t clear_blocks = (kReplicas * cells * SD + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(km_clear, dim3(static_cast<uint32_t>(clear_blocks)), dim3(kThreads), 0,
                      stream, a);
   hipError_t err = hipGetLastError();
@@ -159,7 +207,7 @@ hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream
   const size_t lds = a.n_c <= kLdsMaxCentroids
                          ? static_cast<size_t>(a.n_c) * (SD + 1) * sizeof(unsigned long long)
                          : 0;
-  const int64_t upd_blocks = (cells + kThreads - 1) / kThreads;
+  const int64_t upd_blocks = (cells * SD + kThreads - 1) / kThreads;
   for (int it = 0; it < iterations; ++it) {
     err = encode_mfma_supported(l)
               ? launch_encode_mfma(a.x, a.codebook, a.group_map, const_cast<uint32_t *>(a.idx), l,
@@ -167,8 +215,8 @@ hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream
               : launch_encode(a.x, a.codebook, a.group_map, const_cast<uint32_t *>(a.idx), l,
                               plain_codes(l), stream);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(km_accumulate<SD>, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), lds,
-                       stream, a);
+    hipLaunchKernelGGL(km_accumulate<SD>, dim3(static_cast<uint32_t>(tiles)), dim3(kAccThreads),
+                       lds, stream, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(km_update<SD>, dim3(static_cast<uint32_t>(upd_blocks)), dim3(kThreads), 0,
@@ -182,8 +230,8 @@ hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream
 }  // namespace
 
 size_t kmeans_workspace_bytes(int sub_dim, int n_centroids, int64_t n_codebooks) {
-  return static_cast<size_t>(n_codebooks) * n_centroids * (sub_dim * sizeof(unsigned long long) +
-                                                           sizeof(unsigned int));
+  return static_cast<size_t>(kReplicas) * n_codebooks * n_centroids *
+         (sub_dim * sizeof(unsigned long long) + sizeof(unsigned int));
 }
 
 int64_t kmeans_grid(const Layout &l) {
@@ -199,7 +247,8 @@ hipError_t launch_kmeans(const void *x, void *codebook, const int32_t *group_map
   a.codebook = static_cast<uint16_t *>(codebook);
   a.group_map = group_map;
   a.sums = static_cast<unsigned long long *>(workspace);
-  a.counts = reinterpret_cast<unsigned int *>(a.sums + l.n_codebooks * l.n_centroids * l.sub_dim);
+  a.counts = reinterpret_cast<unsigned int *>(a.sums + kReplicas * l.n_codebooks * l.n_centroids *
+                                                           l.sub_dim);
   a.n = l.n;
   a.cb_stride = l.codebook_stride;
   a.n_codebooks = l.n_codebooks;

@@ -214,7 +214,8 @@ def km(**over):
 
 
 def test_kmeans_workspace_size():
-    assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4) == 4 * 256 * (8 * 8 + 4)
+    # 8 replicas of the exact int64 member sums and uint32 counts per (slot, centroid)
+    assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4) == 8 * 4 * 256 * (8 * 8 + 4)
     assert vq.lib.vq_kmeans_workspace_bytes(3, 256, 4) == 0
 
 

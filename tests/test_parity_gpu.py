@@ -88,6 +88,34 @@ def test_small_cases_match_oracle(case):
     assert rep.equal == rep.rows, "the encode is exact: every index must equal the oracle's"
 
 
+# Inputs large enough that one workgroup (one per CU) owns several units of
+# several groups: the units of a segment are taken from a counter in LDS by
+# whichever wave is free, and the codebook slot is restaged per segment.
+# Group lengths that are not a multiple of the unit (32 T rows) leave partly
+# filled units at every group end; a map sends several groups to one slot,
+# some to bad slots.
+MULTI = [
+    # (seed, n, sd, n_c, dtype, extra)
+    (50, 200_000, 4, 256, W.F16, dict(n_codebooks=70, group_len=3000)),
+    (51, 150_000, 8, 256, W.BF16, dict(n_codebooks=9, group_len=700, use_map=True)),
+    (52, 120_000, 4, 100, W.F16, dict(n_codebooks=5, group_len=129, use_map=True, stride_pad=3)),
+    (53, 100_000, 8, 2000, W.F16, dict(n_codebooks=3, group_len=9000, use_map=True)),
+]
+
+
+@pytest.mark.parametrize("case", MULTI, ids=[f"m{c[0]}_n{c[1]}_sd{c[2]}_nc{c[3]}" for c in MULTI])
+def test_multi_segment_workgroups_match_oracle(case):
+    seed, n, sd, n_c, dt, extra = case
+    wl = W.random_case(seed, n, sd, n_c, dt, **extra)
+    if wl.group_map is not None:
+        wl.group_map[::7] = -1          # bad slots: sentinel codes
+        wl.group_map[3::11] = wl.n_codebooks
+    print(f"[case] {wl.name} {extra}", flush=True)
+    got = gpu_encode(wl)
+    rep = assert_parity(wl, got)
+    assert rep.equal == rep.rows, "the encode is exact: every index must equal the oracle's"
+
+
 def test_max_centroids():
     wl = W.random_case(30, 2100, 8, 65536, W.BF16, dup_frac=0.01)
     print(f"[case] {wl.name}", flush=True)

@@ -134,6 +134,30 @@ def test_packed_small_cases_match_oracle(case):
     assert_packed_parity(wl, gpu_packed(wl, bits, scale_pad=3 if seed % 2 else 0), bits)
 
 
+# Large enough that one workgroup (one per CU) owns several units of several
+# groups (units taken from a counter in LDS, the slot and its factors
+# restaged per segment).
+MULTI = [
+    # (seed, n, sd, n_c, dtype, code_bits, factors, head_mult, random_case extras)
+    (60, 200_000, 4, 256, W.F16, 8, True, 64, dict(n_codebooks=9, group_len=4096, use_map=True)),
+    (61, 150_000, 8, 64, W.BF16, 6, True, 16, dict(n_codebooks=5, group_len=1008, use_map=True)),
+    (62, 120_000, 4, 32, W.F16, 5, True, 16, dict(n_codebooks=40, group_len=3200)),
+]
+
+
+@pytest.mark.parametrize("case", MULTI,
+                         ids=[f"m{c[0]}_n{c[1]}_sd{c[2]}_nc{c[3]}_b{c[5]}" for c in MULTI])
+def test_packed_multi_segment_workgroups_match_oracle(case):
+    seed, n, sd, n_c, dt, bits, factors, hm, extra = case
+    wl = W.random_case(100 + seed, n, sd, n_c, dt, **extra)
+    if wl.group_map is not None:
+        wl.group_map[::5] = -1
+    if factors:
+        with_factors(wl, seed, hm)
+    print(f"[case] {wl.name} bits={bits} factors={factors} {extra}", flush=True)
+    assert_packed_parity(wl, gpu_packed(wl, bits), bits)
+
+
 def test_shared_factor_vector_across_slots():
     wl = W.random_case(140, 6000, 8, 128, W.F16, n_codebooks=3, group_len=1024, use_map=True)
     with_factors(wl, 40, 4, per_slot=False)

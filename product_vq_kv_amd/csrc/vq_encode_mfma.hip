@@ -639,22 +639,22 @@ template <int SD, int T>
 __device__ __forceinline__ void load_unit_x(const uint16_t *__restrict__ x, int64_t ubase,
                                             int64_t gend, uint32_t (&w)[T][4]) {
   const int lane = threadIdx.x & 63;
+  // rows past the group end load the group's last row (their codes are
+  // never stored); unconditional loads are not waited for one by one
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int64_t row = ubase + t * 32 + (lane & 31);
-    w[t][0] = w[t][1] = w[t][2] = w[t][3] = 0;
-    if (row < gend) {
-      if constexpr (SD == 4) {
-        const uint2 q = *reinterpret_cast<const uint2 *>(x + row * 4);
-        w[t][0] = q.x;
-        w[t][1] = q.y;
-      } else {
-        const uint4 q = *reinterpret_cast<const uint4 *>(x + row * 8);
-        w[t][0] = q.x;
-        w[t][1] = q.y;
-        w[t][2] = q.z;
-        w[t][3] = q.w;
-      }
+    const int64_t row = min(ubase + t * 32 + (lane & 31), gend - 1);
+    if constexpr (SD == 4) {
+      const uint2 q = *reinterpret_cast<const uint2 *>(x + row * 4);
+      w[t][0] = q.x;
+      w[t][1] = q.y;
+      w[t][2] = w[t][3] = 0;
+    } else {
+      const uint4 q = *reinterpret_cast<const uint4 *>(x + row * 8);
+      w[t][0] = q.x;
+      w[t][1] = q.y;
+      w[t][2] = q.z;
+      w[t][3] = q.w;
     }
   }
 }
@@ -1053,8 +1053,14 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
   const int64_t u_first = static_cast<int64_t>(blockIdx.x) * units_per_wg;
   const int64_t u_last = min(u_first + units_per_wg, total_units);
   bool first_seg = true;
-  for (int64_t seg = u_first; seg < u_last;) {  // uniform
-    const int64_t g = seg / units_per_group;
+  // the grid gives every workgroup at least one unit, so the first segment
+  // is entered unconditionally
+  int64_t seg = u_first;
+  do {  // uniform
+    const int64_t g = ((seg | units_per_group) >> 32) == 0
+                          ? static_cast<int64_t>(static_cast<uint32_t>(seg) /
+                                                 static_cast<uint32_t>(units_per_group))
+                          : seg / units_per_group;
     const int64_t g_unit0 = g * units_per_group;
     const int64_t seg_end = min(u_last, g_unit0 + units_per_group);
     const int64_t gstart = g * group_len;
@@ -1106,7 +1112,7 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
       if (!bad && u < seg_end) load_unit_x<SD, T>(x, gstart + (u - g_unit0) * kUnit, gend, xw);
     }
     seg = seg_end;
-  }
+  } while (seg < u_last);
 }
 
 template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>

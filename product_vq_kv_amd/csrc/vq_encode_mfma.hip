@@ -66,6 +66,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMfmaMaxCentroids = 4096;    // whole codebook slot resident in LDS
 constexpr int kRows32MaxCentroids = 1024;  // up to here an fp32 copy is kept too
+// K-means sums: rows a workgroup adds up before it flushes.  Every fp16 value
+// is a multiple of 2^-24 below 2^16 in magnitude, so a sum of at most 2^13 of
+// them is a multiple of 2^-24 below 2^29: exact in fp64 in any order.
+constexpr int kAccMaxRows = 8192;
 constexpr float kU = 5.9604644775390625e-08f;       // 2^-24
 constexpr float kTau = 7.174648137343064e-43f;      // 2^-140: absolute slack
 constexpr float kNormCap = 1.2676506002282294e30f;  // 2^100: beyond it, exact path
@@ -659,13 +663,48 @@ __device__ __forceinline__ void load_unit_x(const uint16_t *__restrict__ x, int6
   }
 }
 
+// K-means: what a unit hands to the member sums (fp16 keys).  Lane h of a
+// pair holds components h SD/2 .. h SD/2 + SD/2 - 1 of its column's row.
+template <int SD, int T>
+struct UnitSums {
+  uint32_t code[T];
+  uint32_t words[T][SD / 4];
+  uint32_t check;  // bit t: column t took the full exact scan (may hold non-finite values)
+};
+
+// Adds a finished unit's rows to their centroids' member sums with fp64 LDS
+// atomics (exact, see kAccMaxRows); lane 0 of a pair counts the member.
+// Non-finite components count as 0.
+template <int SD, int T>
+__device__ __forceinline__ void add_unit_sums(const UnitSums<SD, T> &us, int64_t ubase,
+                                              int64_t gend, double *lsum, uint32_t *lcnt) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (ubase + t * 32 + col < gend) {
+      double *p = lsum + us.code[t] * SD + h * (SD / 2);
+      const bool check = (us.check >> t) & 1u;
+#pragma unroll
+      for (int i = 0; i < SD / 2; ++i) {
+        const uint32_t word = us.words[t][i >> 1];
+        float v = widen<false>(static_cast<uint16_t>((i & 1) ? (word >> 16) : (word & 0xFFFFu)));
+        if (check && !(__builtin_fabsf(v) <= kFltMax)) v = 0.0f;
+        atomicAdd(p + i, static_cast<double>(v));
+      }
+      if (h == 0) atomicAdd(lcnt + us.code[t], 1u);
+    }
+  }
+}
+
 // One unit: the wave encodes T columns of 32 sub-vectors, rows ubase ..
 // ubase + 32 T - 1 (raw words from load_unit_x).
-template <int SD, int T, bool BF16, bool ROWS32, bool SCALED>
+template <int SD, int T, bool BF16, bool ROWS32, bool SCALED, bool ACC>
 __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t gend, int n_c,
                             int n_cpad, const Lds<SD, ROWS32> &s, bool exact_tile, bool fold,
-                            const Smooth sm, int sub0, int code_bits,
-                            uint8_t *__restrict__ out) {
+                            const Smooth sm, int sub0, int code_bits, uint8_t *__restrict__ out,
+                            UnitSums<SD, T> &us) {
   using K = Consts<SD, kTerms<SD, SCALED>>;
   using OpT = Op<SD, SCALED>;
   const int lane = threadIdx.x & 63;
@@ -1017,6 +1056,23 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
         if (row0 + 32 * t < gend) out[row0 + 32 * t] = static_cast<uint8_t>(codes[t]);
     }
   }
+
+  // ---- K-means: the codes and this lane's components for the member sums ---
+  if constexpr (ACC) {
+    static_assert(!SCALED && !BF16, "member sums are taken of plain fp16 keys");
+    us.check = full_bits;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      us.code[t] = codes[t];
+      if constexpr (SD == 4) {
+        const uint32_t w1 = pair_vals(bop[t].y).first;  // lane 0 holds the whole row
+        us.words[t][0] = h ? w1 : bop[t].x;
+      } else {
+        us.words[t][0] = bop[t].x;
+        us.words[t][1] = bop[t].y;
+      }
+    }
+  }
 }
 
 // One workgroup of BLOCK threads per CU.  Workgroup w owns units [w k,
@@ -1026,14 +1082,15 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
 // take units from a counter in LDS: a wave that runs ahead takes more units,
 // so all waves of the CU finish close together (the issue arbiter favours
 // the oldest waves, which would otherwise finish far ahead of the others).
-template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED, bool ACC>
 __global__ void __launch_bounds__(BLOCK, 1)
 encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ codebook,
                    int64_t n, int n_c, int64_t cb_stride, int64_t n_codebooks, int64_t group_len,
                    int64_t units_per_group, int64_t total_units, int64_t units_per_wg,
                    const int32_t *__restrict__ group_map, uint8_t *__restrict__ out,
                    int hash_slots, const float *__restrict__ scale, int64_t scale_stride,
-                   int head_dim, int code_bits) {
+                   int head_dim, int code_bits, unsigned long long *__restrict__ acc_sums,
+                   unsigned int *__restrict__ acc_counts) {
   constexpr int kWaves = BLOCK / 64;
   constexpr int kUnit = T * 32;
   extern __shared__ uint4 lds_raw[];
@@ -1049,6 +1106,17 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;
   int *counter = s.flags + s.kCounter;
+  // K-means member sums of the current segment: [n_c][SD] fp64, then the
+  // counts, after the staging areas (a plain encode stages no factors)
+  double *lsum = nullptr;
+  uint32_t *lcnt = nullptr;
+  UnitSums<SD, T> us;
+  if constexpr (ACC) {
+    lsum = reinterpret_cast<double *>(s.scale);
+    lcnt = reinterpret_cast<uint32_t *>(lsum + n_c * SD);
+    for (int e = threadIdx.x; e < n_c * SD; e += BLOCK) lsum[e] = 0.0;
+    for (int e = threadIdx.x; e < n_c; e += BLOCK) lcnt[e] = 0u;
+  }
 
   const int64_t u_first = static_cast<int64_t>(blockIdx.x) * units_per_wg;
   const int64_t u_last = min(u_first + units_per_wg, total_units);
@@ -1103,21 +1171,49 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
           const uint32_t off = static_cast<uint32_t>(u - g_unit0) * kUnit % static_cast<uint32_t>(sm.n_sub);
           sub0 = mod_small(seg_sub0 + static_cast<int>(off), sm.n_sub, sm.inv_n_sub);
         }
-        encode_unit<SD, T, BF16, ROWS32, SCALED>(xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold,
-                                                 sm, sub0, code_bits, out);
+        encode_unit<SD, T, BF16, ROWS32, SCALED, ACC>(xw, ubase, gend, n_c, n_cpad, s, exact_tile,
+                                                      fold, sm, sub0, code_bits, out, us);
       }
+      // the next unit is taken (a returning LDS atomic, which would wait
+      // behind the member-sum atomics) and its loads issued before this
+      // unit's rows join the sums
       int next = 0;
       if (lane == 0) next = atomicAdd(counter, 1);
       u = seg + __builtin_amdgcn_readfirstlane(next);
       if (!bad && u < seg_end) load_unit_x<SD, T>(x, gstart + (u - g_unit0) * kUnit, gend, xw);
+      if constexpr (ACC) {
+        if (!bad) add_unit_sums<SD, T>(us, ubase, gend, lsum, lcnt);
+      }
+    }
+    if constexpr (ACC) {
+      // flush the segment's sums into the workspace copy of this workgroup
+      // (int64 units of 2^-24: the fp64 sums are exact multiples of 2^-24)
+      // and clear them; the next segment adds only after its staging barrier
+      __syncthreads();  // every wave has added its rows
+      if (!bad) {
+        const int64_t cell0 = (static_cast<int64_t>(blockIdx.x % kKmReplicas) * n_codebooks + slot) * n_c;
+        for (int e = threadIdx.x; e < n_c * SD; e += BLOCK) {
+          const double v = lsum[e];
+          if (v != 0.0)
+            atomicAdd(acc_sums + cell0 * SD + e,
+                      static_cast<unsigned long long>(static_cast<int64_t>(v * 16777216.0)));
+          lsum[e] = 0.0;
+        }
+        for (int e = threadIdx.x; e < n_c; e += BLOCK) {
+          const uint32_t k = lcnt[e];
+          if (k) atomicAdd(acc_counts + cell0 + e, k);
+          lcnt[e] = 0u;
+        }
+      }
     }
     seg = seg_end;
   } while (seg < u_last);
 }
 
-template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED>
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED, bool ACC = false>
 hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_map, void *out,
-                    const Layout &l, const Codes &codes, hipStream_t stream, int64_t cus) {
+                    const Layout &l, const Codes &codes, hipStream_t stream, int64_t cus,
+                    const KmSums &acc = KmSums{nullptr, nullptr}) {
   constexpr int kUnit = T * 32;
   const int64_t span = l.group_len < l.n ? l.group_len : l.n;
   const int64_t units_per_group = (span + kUnit - 1) / kUnit;
@@ -1125,8 +1221,9 @@ hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_ma
   const int n_cpad = (l.n_centroids + 31) & ~31;
   int hash_slots = 64;
   while (hash_slots < 2 * l.n_centroids) hash_slots <<= 1;
-  const size_t lds = Lds<SD, ROWS32>::bytes(n_cpad, hash_slots, SCALED ? codes.head_dim : 0);
-  auto kern = encode_mfma_kernel<SD, T, BLOCK, BF16, ROWS32, SCALED>;
+  const size_t lds = Lds<SD, ROWS32>::bytes(n_cpad, hash_slots, SCALED ? codes.head_dim : 0) +
+                     (ACC ? static_cast<size_t>(l.n_centroids) * (SD * 8 + 4) : 0);
+  auto kern = encode_mfma_kernel<SD, T, BLOCK, BF16, ROWS32, SCALED, ACC>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1135,14 +1232,16 @@ hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_ma
   }
   // one workgroup per CU (small inputs: fewer units than waves per workgroup,
   // spread over more CUs)
-  const int64_t units_per_wg = (total_units + cus - 1) / cus;
+  // (member sums: at most kAccMaxRows rows per workgroup)
+  int64_t units_per_wg = (total_units + cus - 1) / cus;
+  if (ACC && units_per_wg > kAccMaxRows / kUnit) units_per_wg = kAccMaxRows / kUnit;
   const int64_t grid = (total_units + units_per_wg - 1) / units_per_wg;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(BLOCK), lds, stream,
                      static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(codebook),
                      l.n, l.n_centroids, l.codebook_stride, l.n_codebooks, l.group_len,
                      units_per_group, total_units, units_per_wg, group_map,
                      static_cast<uint8_t *>(out), hash_slots, codes.scale, codes.scale_stride,
-                     codes.head_dim, codes.code_bits);
+                     codes.head_dim, codes.code_bits, acc.sums, acc.counts);
   return hipGetLastError();
 }
 
@@ -1189,6 +1288,24 @@ hipError_t launch_scaled(const void *x, const void *codebook, const int32_t *gro
 }  // namespace
 
 bool encode_mfma_supported(const Layout &l) { return l.n_centroids <= kMfmaMaxCentroids; }
+
+bool encode_mfma_kmeans_supported(const Layout &l) {
+  return !l.bf16 && l.n_centroids <= kKmFusedMaxCentroids &&
+         (l.sub_dim == 4 || l.sub_dim == 8);
+}
+
+hipError_t launch_encode_mfma_kmeans(const void *x, const void *codebook,
+                                     const int32_t *group_map, uint32_t *out, const Layout &l,
+                                     const KmSums &acc, hipStream_t stream) {
+  static_assert(kKmFusedMaxCentroids <= kRows32MaxCentroids, "the sums follow the fp32 rows");
+  const int64_t cus = cu_count();
+  const Codes codes = plain_codes(l);
+  if (l.sub_dim == 4)
+    return launch_t<4, columns<4, false, true>(), 1024, false, true, false, true>(
+        x, codebook, group_map, out, l, codes, stream, cus, acc);
+  return launch_t<8, columns<8, false, true>(), 1024, false, true, false, true>(
+      x, codebook, group_map, out, l, codes, stream, cus, acc);
+}
 
 int64_t encode_mfma_grid(const Layout &l) {
   // upper bound on the workgroups of any plan above (one 64-row unit each)

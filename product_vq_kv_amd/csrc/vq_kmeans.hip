@@ -9,12 +9,16 @@
 //   update:     centroid = exact member mean rounded once to fp16 (round to
 //               nearest even); a centroid without members keeps its value.
 // fp16 values are integer multiples of 2^-24, so member sums are exact int64
-// (|sum| < 2^40 * n); the sums are accumulated per workgroup in LDS with
-// 64-bit integer atomics and flushed with 64-bit global atomics into one of
-// kReplicas copies of the sums (fewer workgroups contend for one address),
-// which the update adds up.  Integer addition is associative, so the result
-// does not depend on the order of the additions, and the rounding of sum /
-// count is done exactly in integer arithmetic.
+// (|sum| < 2^40 * n).  Up to 512 centroids the encode itself adds every
+// sub-vector to its centroid's sums (fp64 LDS atomics, exact for the at most
+// 8192 rows a workgroup adds before it flushes, see vq_encode_mfma.hip);
+// otherwise km_accumulate reads the rows and codes back and adds them in LDS
+// with 64-bit integer atomics (or straight to global memory above 512
+// centroids).  Either way the per-workgroup sums are flushed with 64-bit
+// global atomics into one of kReplicas copies (fewer workgroups contend for
+// one address), which the update adds up.  Integer addition is associative,
+// so the result does not depend on the order of the additions, and the
+// rounding of sum / count is done exactly in integer arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,7 +34,7 @@ constexpr int kAccThreads = 1024;    // accumulate workgroups
 constexpr int kRowsPerThread = 4;
 constexpr int kRowsPerTile = kAccThreads * kRowsPerThread;  // rows per accumulate workgroup
 constexpr int kLdsMaxCentroids = 512;   // beyond: accumulate straight to global
-constexpr int kReplicas = 8;            // copies of the sums the flush is spread over
+constexpr int kReplicas = kKmReplicas;  // copies of the sums the flush is spread over
 
 // x * 2^24 as an exact integer (fp16 x; non-finite values count as 0): a
 // normal value (1024 + m) 2^(e - 25) gives (1024 + m) 2^(e - 1), a
@@ -208,7 +212,19 @@ hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream
                          ? static_cast<size_t>(a.n_c) * (SD + 1) * sizeof(unsigned long long)
                          : 0;
   const int64_t upd_blocks = (cells * SD + kThreads - 1) / kThreads;
+  // up to 512 fp16 centroids the encode adds the member sums itself
+  const bool fused = encode_mfma_kmeans_supported(l);
   for (int it = 0; it < iterations; ++it) {
+    if (fused) {
+      err = launch_encode_mfma_kmeans(a.x, a.codebook, a.group_map, const_cast<uint32_t *>(a.idx),
+                                      l, KmSums{a.sums, a.counts}, stream);
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL(km_update<SD>, dim3(static_cast<uint32_t>(upd_blocks)), dim3(kThreads), 0,
+                         stream, a);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      continue;
+    }
     err = encode_mfma_supported(l)
               ? launch_encode_mfma(a.x, a.codebook, a.group_map, const_cast<uint32_t *>(a.idx), l,
                                    plain_codes(l), stream)

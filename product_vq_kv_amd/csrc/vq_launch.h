@@ -47,6 +47,24 @@ hipError_t launch_encode_mfma(const void *x, const void *codebook, const int32_t
                               void *out, const Layout &l, const Codes &codes,
                               hipStream_t stream);
 
+// K-means member sums in the caller's workspace: kKmReplicas copies of
+// sums [n_codebooks][n_c][sub_dim] (int64 units of 2^-24, two's complement)
+// and counts [n_codebooks][n_c]; a workgroup adds into copy (index mod
+// kKmReplicas).
+constexpr int kKmReplicas = 8;
+struct KmSums {
+  unsigned long long *sums;
+  unsigned int *counts;
+};
+
+// The matrix-core encode that also adds every sub-vector to its centroid's
+// member sums (fp16, unsmoothed, uint32 indices): up to this many centroids.
+constexpr int kKmFusedMaxCentroids = 512;
+bool encode_mfma_kmeans_supported(const Layout &l);
+hipError_t launch_encode_mfma_kmeans(const void *x, const void *codebook,
+                                     const int32_t *group_map, uint32_t *out, const Layout &l,
+                                     const KmSums &acc, hipStream_t stream);
+
 hipError_t launch_decode(const uint32_t *idx, const void *codebook, const int32_t *group_map,
                          void *out_x, const Layout &l, hipStream_t stream);
 

@@ -4,7 +4,9 @@ Every update is the exact member mean rounded once to fp16 on both sides, so
 the codebooks and assignments must be bit-identical after every iteration.
 Cases cover sub_dim 4 and 8, LDS and global accumulation (n_centroids above
 512), the matrix-core and direct assignment kernels (up to 5000 centroids),
-several slots with group maps and bad slots, exactly representable clusters,
+several slots with group maps and bad slots, workgroups spanning several
+groups, member sums at the limit of their exact accumulation, exactly
+representable clusters,
 the Falcon3-7B keys at full size, and whole slots sampled from the 256-slot
 full cache trained in one call.
 """
@@ -66,6 +68,9 @@ CASES = [
     (7, 9000, 8, 32, 3, dict(n_codebooks=4, group_len=2048, use_map=True)),
     (8, 7000, 4, 100, 3, dict(n_codebooks=7, group_len=1000, stride_pad=5)),
     (9, 30000, 4, 16, 6, dict(scale=1e-3)),
+    # workgroups whose units span several groups (member sums flushed per group)
+    (10, 200000, 4, 64, 2, dict(n_codebooks=10, group_len=1000, use_map=True)),
+    (11, 150000, 8, 128, 2, dict(n_codebooks=5, group_len=700, use_map=True)),
 ]
 
 
@@ -98,6 +103,25 @@ def test_kmeans_exact_clusters():
     assert f[0].tolist() == [1, 1, 1, 1] and f[1].tolist() == [11] * 4
     assert f[2].tolist() == [-7, 5, -7, 5] and f[3].tolist() == [100] * 4
     assert_kmeans_parity(wl, 3)
+
+
+def test_kmeans_member_sums_at_the_exactness_limit():
+    """Members of +-65504 and 2^-24: per workgroup the encode adds up to 8192
+    rows in fp64, whose sums then reach 2^29 at a resolution of 2^-24 (53
+    bits), so any lost bit changes a mean."""
+    rng = np.random.default_rng(341)
+    n = 3 * 2 ** 20
+    sign = np.where(rng.random(n) < 0.5, 1.0, -1.0)
+    x = np.empty((n, 4))
+    x[:, 1:] = sign[:, None] * rng.choice([65504.0, 65472.0, 64000.0], size=(n, 3))
+    tiny = rng.random(n) < 0.3
+    x[:, 0] = np.where(tiny, sign * 2.0 ** -24, sign * 65504.0)
+    x[rng.random(n) < 0.01, 0] = 2.0 ** -14 + 2.0 ** -24   # subnormal and normal mix
+    init = np.array([[1000.0] * 4, [-1000.0] * 4, [0.0, 0.0, 0.0, 5.0]])
+    wl = W.Workload("exactness limit", W.to_f16_bits(x).reshape(-1, 4),
+                    W.to_f16_bits(init).reshape(-1), 4, 3, W.F16, 12, 1, n)
+    print(f"[case] {wl.name}: {n} rows", flush=True)
+    assert_kmeans_parity(wl, 2)
 
 
 def test_kmeans_falcon_keys_full_size():

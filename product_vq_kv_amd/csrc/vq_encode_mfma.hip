@@ -49,6 +49,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -1245,15 +1246,22 @@ hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_ma
   return hipGetLastError();
 }
 
+// CUs of the current device (cached per device; safe to call from several
+// host threads).
 int cu_count() {
-  static int cached = 0;
-  if (cached > 0) return cached;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     return 256;
-  cached = cus;
+  if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 

@@ -530,15 +530,13 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
   return exact;
 }
 
-// Strict-< minimum of the exact distance over the 4 consecutive rows c0 ..
-// c0 + 3 (c0 a multiple of 4, c0 + 3 < n_cpad: padding rows are staged too),
-// visited in ascending order; the index recorded for row c0 + i is k0 + i.
-// With MASK, rows >= n_c (the padding of the last block) are excluded;
-// without it every row is < n_c.
 // The 8 rows of group grp that lane half h evaluates in the exact stage:
 // rows c0 .. c0 + 3 and c0 + 8 .. c0 + 11, c0 = 32 (grp / 2) + 16 h + 4 (grp
-// mod 2), in ascending order; bk gets the offset (0..3, 8..11) of the
-// strict-< minimum.
+// mod 2), in ascending order.  best and bk are set to the minimum exact
+// distance and the offset (0..3, 8..11) of its first row, the result of a
+// strict-< scan from (+inf, 0) whenever that minimum is finite.  With MASK,
+// rows >= n_c (the padding of the last block) are excluded; without it every
+// row is < n_c.
 template <int SD, bool BF16, bool ROWS32, bool MASK>
 __device__ __forceinline__ void exact8(const Lds<SD, ROWS32> &s, const float (&xv)[SD], int grp,
                                        int h, int n_c, float &best, int &bk) {
@@ -546,6 +544,7 @@ __device__ __forceinline__ void exact8(const Lds<SD, ROWS32> &s, const float (&x
   const int c0 = b * 32 + h * 16 + hh * 4;
   // c32_offset(c0), spelled out: the row set's padding is 4 (c0 / 4 + c0 / 32)
   const float *base = s.c32 + b * (32 * SD + 36) + h * (16 * SD + 16) + hh * (4 * SD + 4);
+  float d[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int k = (j & 3) + ((j & 4) << 1);
@@ -565,14 +564,24 @@ __device__ __forceinline__ void exact8(const Lds<SD, ROWS32> &s, const float (&x
     } else {
       centroid_in_set<SD, BF16, ROWS32>(s, c0 + (k & 8), k & 3, cv);
     }
-    float d = sqdist<SD>(xv, cv);
-    if (MASK) d = (c < n_c) ? d : __builtin_inff();
-    const bool lt = d < best;
-    best = lt ? d : best;
-    bk = lt ? k : bk;
+    d[j] = sqdist<SD>(xv, cv);
+    if (MASK) d[j] = (c < n_c) ? d[j] : __builtin_inff();
   }
+  // the strict-< scan from (+inf, 0) keeps the first row of the minimum: take
+  // the minimum, then the lowest row equal to it (rows after the first at an
+  // infinite or NaN minimum differ from the scan; such a column takes the
+  // full exact scan, which replaces this result)
+  best = __builtin_fminf(__builtin_fminf(__builtin_fminf(d[0], d[1]), __builtin_fminf(d[2], d[3])),
+                         __builtin_fminf(__builtin_fminf(d[4], d[5]), __builtin_fminf(d[6], d[7])));
+  bk = 11;
+#pragma unroll
+  for (int j = 6; j >= 0; --j) bk = (d[j] == best) ? (j & 3) + ((j & 4) << 1) : bk;
 }
 
+// Strict-< minimum of the exact distance over the 4 consecutive rows c0 ..
+// c0 + 3 (c0 a multiple of 4, c0 + 3 < n_cpad: padding rows are staged too),
+// visited in ascending order; the index recorded for row c0 + i is k0 + i.
+// MASK as for exact8.
 template <int SD, bool BF16, bool ROWS32, bool MASK>
 __device__ __forceinline__ void exact4(const Lds<SD, ROWS32> &s, const float (&xv)[SD], int c0,
                                        int k0, int n_c, float &best, int &bk) {

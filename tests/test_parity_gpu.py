@@ -253,6 +253,43 @@ def test_misaligned_x_raises():
         vq.encode(x, cb)
 
 
+def test_side_streams_and_host_threads():
+    """Encodes on two side streams, and from two host threads at once (each
+    with its own stream), match the oracle: every launch runs on the stream
+    it is given, and the launch path keeps no state that calls share."""
+    import threading
+    cases = [W.random_case(37, 70000, 4, 256, W.F16), W.random_case(38, 50000, 8, 100, W.BF16),
+             W.random_case(39, 30000, 8, 256, W.F16, n_codebooks=3, group_len=10000)]
+    devs = [to_dev(wl) for wl in cases]
+    want = [oracle.encode(wl.x, wl.codebook, wl.sub_dim, wl.n_centroids, wl.dtype, threads=8,
+                          **wl.kwargs()) for wl in cases]
+    streams = [torch.cuda.Stream(device=DEV) for _ in cases]   # default priority
+    torch.cuda.synchronize()
+
+    def run(k, outs):
+        wl, (x, cb3, gmap) = cases[k], devs[k]
+        cb = cb3[0] if wl.n_codebooks == 1 else cb3
+        with torch.cuda.stream(streams[k]):
+            outs[k] = vq.encode(x, cb, group_len=wl.group_len, group_map=gmap,
+                                stream=streams[k])
+
+    outs = [None] * len(cases)
+    for k in range(len(cases)):          # back to back, no synchronization between
+        run(k, outs)
+    torch.cuda.synchronize()
+    for k in range(len(cases)):
+        assert np.array_equal(outs[k].cpu().numpy().view(np.uint32), want[k]), k
+    outs = [None] * len(cases)
+    threads = [threading.Thread(target=run, args=(k, outs)) for k in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for k in range(len(cases)):
+        assert np.array_equal(outs[k].cpu().numpy().view(np.uint32), want[k]), k
+
+
 def test_no_device_memory_is_allocated():
     wl = W.random_case(36, 50000, 4, 256, W.F16)
     x, cb3, _ = to_dev(wl)

@@ -469,7 +469,14 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
     if (r < n_cpad) {
       if ((lane & 0x1B) == 0) s.gan[group_of(r)] = an;
       if constexpr (FOLD) {  // halves 4, 5 carry C, half 6 carries -a' (SD == 4)
-        if (!split_down<BF16>(cv, k8[4], k8[5])) nofold = 1;
+        // C beyond the element type: the slot takes the unfolded form, which
+        // adds C in fp32 and multiplies these halves by 0, so they must be
+        // finite (an infinite half would make the row's product NaN, and the
+        // minimum would drop the row)
+        if (!split_down<BF16>(cv, k8[4], k8[5])) {
+          nofold = 1;
+          k8[4] = k8[5] = 0;
+        }
         k8[6] = round_up<BF16>(an * kFoldScale) ^ 0x8000u;
       }
       s.rows[r] = make_uint4(k8[0] | (static_cast<uint32_t>(k8[1]) << 16),
@@ -520,7 +527,9 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
           const uint32_t prev = atomicMin(&s.hash[slot], key);
           const int dup = max(static_cast<int>(prev & 0xFFFu), r);
           s.cval[dup] = __builtin_inff();
-          if constexpr (FOLD) s.rows[dup].z = kInfBits<BF16>;  // C_hi = +inf, C_lo = 0
+          // folded: C_hi = +inf, C_lo = 0 (an unfolded slot multiplies these
+          // halves by 0 and takes C = +inf from cval alone)
+          if (FOLD && fold_ok) s.rows[dup].z = kInfBits<BF16>;
           break;
         }
         slot = (slot + 1) & mask;

@@ -203,6 +203,20 @@ def test_near_tied_centroids_across_groups(sd, dt):
     assert rep.equal == rep.rows
 
 
+@pytest.mark.parametrize("sd,scale,dups", [(4, 300.0, 0.0), (4, 150.0, 0.0), (8, 300.0, 0.0),
+                                           (4, 300.0, 0.2)])
+def test_codebook_norms_beyond_fp16_c(sd, scale, dups):
+    """fp16 centroids with |c|^2 / 2 above the fp16 range (|c| > 362): such a
+    slot cannot carry C in the product's spare slots and takes the unfolded
+    form; every centroid must still be bounded (none may drop out), and
+    duplicate rows in such a slot are excluded through C alone."""
+    wl = W.random_case(41, 20000, sd, 256, W.F16, scale=scale, dup_frac=dups)
+    print(f"[case] {wl.name} scale {scale} duplicates {dups}", flush=True)
+    got = gpu_encode(wl)
+    rep = assert_parity(wl, got)
+    assert rep.equal == rep.rows, "the encode is exact: every index must equal the oracle's"
+
+
 def test_huge_codebook_norms_odd_bf16():
     sd, n_c = 8, 33
     r = np.random.default_rng(39)

@@ -120,6 +120,10 @@ PACKED = [
     # no factors, byte-wide codes: the plain kernel writes them directly
     (18, 6000, 8, 300, W.F16, 16, False, 1, dict(n_codebooks=3, group_len=1024, use_map=True)),
     (19, 7777, 4, 200, W.BF16, 8, False, 1, dict(n_codebooks=2, group_len=4000)),
+    # |c|^2 / 2 beyond the fp16 range: the slot takes the unfolded form (with
+    # duplicate rows in it)
+    (20, 8192, 4, 256, W.F16, 8, True, 64, dict(scale=300.0)),
+    (21, 8192, 4, 256, W.F16, 8, True, 16, dict(dup_frac=0.2, scale=300.0)),
 ]
 
 

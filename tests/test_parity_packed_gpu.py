@@ -276,3 +276,16 @@ def test_full_cache_smoothed_sampled_chunks():
                                     channel_scale=wl.channel_scale[g], head_dim=wl.head_dim,
                                     code_bits=8)
         assert np.array_equal(got[r0:r0 + length], want), f"chunk at row {r0} (group {g})"
+
+
+def test_smoothed_keys_beyond_the_fp16_error_operand():
+    """Factors of about 2^14 lift smoothed keys past 2^26 in norm: the error
+    term's key operand b' no longer fits fp16, so the bounds of those keys
+    become -inf and every group of theirs is evaluated exactly (fp32 distances
+    near 1e16 also tie often).  The codes must still equal the oracle's."""
+    wl = W.random_case(42, 6000, 4, 256, W.F16, scale=1000.0)
+    wl = with_factors(wl, 42, head_mult=16, per_slot=False)
+    wl.channel_scale = (wl.channel_scale * np.float32(2.0 ** 14)).astype(np.float32)
+    print(f"[case] {wl.name} factors x 2^14", flush=True)
+    got = gpu_packed(wl, 8)
+    assert_packed_parity(wl, got, 8)

@@ -322,6 +322,39 @@ def test_no_device_memory_is_allocated():
 # full-size workloads
 # ---------------------------------------------------------------------------
 
+def test_more_than_2_31_sub_vectors_sampled():
+    """2^31 + 4099 sub-vectors (17 GB of keys): row offsets, unit indices and
+    byte addresses pass 2^31.  Keys are drawn on the device from a seeded
+    generator; sampled rows (random, around 2^31 and the ragged tail) are
+    copied back and checked against the oracle on the same values."""
+    n = 2 ** 31 + 4099
+    sd = 4
+    cbw = W.random_case(44, 1, sd, 256, W.F16)
+    x = torch.empty(n, sd, dtype=torch.float16, device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(44)
+    step = 2 ** 28
+    for i in range(0, n, step):
+        j = min(n, i + step)
+        x[i:j] = torch.randn(j - i, sd, generator=gen, device=DEV).to(torch.float16)
+    cb = torch.from_numpy(cbw.codebook.view(np.int16)).view(torch.float16).to(DEV).view(256, sd)
+    out = vq.encode(x, cb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(44)
+    rows = np.unique(np.concatenate([
+        rng.integers(0, n, 1 << 16), np.arange(2 ** 31 - 300, 2 ** 31 + 300),
+        np.arange(n - 5000, n), np.arange(0, 300)]))
+    idx = torch.from_numpy(rows).to(DEV)
+    xs = x[idx].cpu().view(torch.int16).numpy().view(np.uint16)
+    got = out.view(torch.int32)[idx].cpu().numpy().view(np.uint32)
+    del x, out
+    torch.cuda.empty_cache()
+    want = oracle.encode(xs, cbw.codebook, sd, 256, W.F16, threads=8)
+    print(f"[parity] {n} sub-vectors, {rows.size} sampled rows: "
+          f"{int(np.sum(got == want))} equal", flush=True)
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 5])
 def test_full_size_config_every_row(cfg):
     wl = W.config(cfg)

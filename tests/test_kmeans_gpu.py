@@ -71,6 +71,9 @@ CASES = [
     # workgroups whose units span several groups (member sums flushed per group)
     (10, 200000, 4, 64, 2, dict(n_codebooks=10, group_len=1000, use_map=True)),
     (11, 150000, 8, 128, 2, dict(n_codebooks=5, group_len=700, use_map=True)),
+    # the largest codebook whose sums the encode adds itself, and one more
+    (12, 40000, 4, 512, 2, dict(dup_frac=0.02)),
+    (13, 40000, 8, 513, 2, {}),
 ]
 
 

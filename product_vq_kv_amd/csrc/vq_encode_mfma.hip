@@ -347,6 +347,7 @@ template <int SD, bool ROWS32>
 struct Lds {
   static constexpr int kFlags = 16;  // one per wave, at most 1024 threads
   static constexpr int kCounter = kFlags;  // flags[kCounter]: next unit of the segment
+  uint4 *arows;  // smoothed sub_dim 4: the K = 16 A operand, one 16-byte half per lane half
   uint4 *rows;
   float *cval;
   float *gan;
@@ -360,8 +361,9 @@ struct Lds {
     return ROWS32 ? SD * n_cpad + 4 * (n_cpad / 4 + n_cpad / 32 + 1) : 0;
   }
   static __device__ __forceinline__ int c32_offset(int r) { return SD * r + 4 * ((r >> 2) + (r >> 5)); }
-  __device__ Lds(uint4 *base, int n_cpad, int hash_slots) {
-    rows = base;
+  __device__ Lds(uint4 *base, int n_cpad, int hash_slots, int arows_len) {
+    arows = base;
+    rows = base + arows_len;
     cval = reinterpret_cast<float *>(rows + n_cpad);
     gan = cval + n_cpad;
     c32 = gan + gan_len(n_cpad);
@@ -369,8 +371,8 @@ struct Lds {
     flags = reinterpret_cast<int *>(hash + hash_slots);
     scale = reinterpret_cast<float *>(flags + kFlags + 4);
   }
-  static size_t bytes(int n_cpad, int hash_slots, int scale_len) {
-    return static_cast<size_t>(n_cpad) * (16 + 4) + static_cast<size_t>(c32_len(n_cpad)) * 4 +
+  static size_t bytes(int n_cpad, int hash_slots, int scale_len, int arows_len) {
+    return static_cast<size_t>(arows_len) * 16 + static_cast<size_t>(n_cpad) * (16 + 4) + static_cast<size_t>(c32_len(n_cpad)) * 4 +
            static_cast<size_t>(gan_len(n_cpad)) * 4 + static_cast<size_t>(hash_slots) * 4 +
            (kFlags + 4) * 4 + static_cast<size_t>(scale_len) * 4;
   }
@@ -424,7 +426,7 @@ __device__ __forceinline__ float group_max(float v) {
 // Returns true when some centroid has a non-finite or huge norm: then every
 // sub-vector of the slot takes the full exact scan.  One barrier, after the
 // rows are written; duplicate rows are marked after it.
-template <int SD, int NT, bool BF16, bool ROWS32, int BLOCK, bool FOLD>
+template <int SD, int NT, bool BF16, bool ROWS32, int BLOCK, bool FOLD, bool AROWS>
 __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_cpad,
                                const Lds<SD, ROWS32> &s, int hash_slots,
                                const float *__restrict__ scale, int scale_len, bool &fold_ok) {
@@ -479,10 +481,15 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
         }
         k8[6] = round_up<BF16>(an * kFoldScale) ^ 0x8000u;
       }
-      s.rows[r] = make_uint4(k8[0] | (static_cast<uint32_t>(k8[1]) << 16),
-                             k8[2] | (static_cast<uint32_t>(k8[3]) << 16),
-                             k8[4] | (static_cast<uint32_t>(k8[5]) << 16),
-                             k8[6] | (static_cast<uint32_t>(k8[7]) << 16));
+      const uint4 row = make_uint4(k8[0] | (static_cast<uint32_t>(k8[1]) << 16),
+                                   k8[2] | (static_cast<uint32_t>(k8[3]) << 16),
+                                   k8[4] | (static_cast<uint32_t>(k8[5]) << 16),
+                                   k8[6] | (static_cast<uint32_t>(k8[7]) << 16));
+      s.rows[r] = row;
+      if constexpr (AROWS) {  // lane half 0: -c against hi and lo; half 1: C, -a'
+        s.arows[2 * r] = make_uint4(row.x, row.y, row.x, row.y);
+        s.arows[2 * r + 1] = make_uint4(row.z, row.w, 0u, 0u);
+      }
       s.cval[r] = cv;
       if constexpr (ROWS32) {
 #pragma unroll
@@ -529,7 +536,10 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
           s.cval[dup] = __builtin_inff();
           // folded: C_hi = +inf, C_lo = 0 (an unfolded slot multiplies these
           // halves by 0 and takes C = +inf from cval alone)
-          if (FOLD && fold_ok) s.rows[dup].z = kInfBits<BF16>;
+          if (FOLD && fold_ok) {
+            s.rows[dup].z = kInfBits<BF16>;
+            if constexpr (AROWS) s.arows[2 * dup + 1].x = kInfBits<BF16>;
+          }
           break;
         }
         slot = (slot + 1) & mask;
@@ -846,9 +856,11 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
   auto a_operand = [&](int blk) -> OpT {
     if constexpr (SCALED && SD == 8) {
       return s.rows[blk * 32 + col];
-    } else if constexpr (SCALED) {
-      // K = 16: lane half 0 takes -c twice (against hi and lo), half 1 the
+    } else if constexpr (SCALED && ROWS32) {
+      // K = 16, staged per lane half: -c twice (against hi and lo), or the
       // row's C_hi, C_lo, -a'
+      return s.arows[(blk * 32 + col) * 2 + h];
+    } else if constexpr (SCALED) {
       const uint2 q = reinterpret_cast<const uint2 *>(s.rows)[blk * 64 + 2 * col + h];
       return (h == 0) ? make_uint4(q.x, q.y, q.x, q.y) : make_uint4(q.x, q.y, 0u, 0u);
     } else {
@@ -1114,7 +1126,8 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
   constexpr int kUnit = T * 32;
   extern __shared__ uint4 lds_raw[];
   const int n_cpad = (n_c + 31) & ~31;
-  const Lds<SD, ROWS32> s(lds_raw, n_cpad, hash_slots);
+  constexpr bool kARows = SCALED && SD == 4 && ROWS32;
+  const Lds<SD, ROWS32> s(lds_raw, n_cpad, hash_slots, kARows ? 2 * n_cpad : 0);
   const int scale_len = SCALED ? head_dim : 0;
   Smooth sm{1, 1.0f};
   if constexpr (SCALED) {
@@ -1165,7 +1178,8 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     bool exact_tile = false, fold = false;
     if (!bad) {
       // its barrier also publishes the counter
-      exact_tile = stage_codebook<SD, kTerms<SD, SCALED>, BF16, ROWS32, BLOCK, kFold<SD, SCALED>>(
+      exact_tile = stage_codebook<SD, kTerms<SD, SCALED>, BF16, ROWS32, BLOCK, kFold<SD, SCALED>,
+                                  kARows>(
           codebook + slot * cb_stride, n_c, n_cpad, s, hash_slots,
           (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len, fold);
     } else {
@@ -1240,8 +1254,10 @@ hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_ma
   const int n_cpad = (l.n_centroids + 31) & ~31;
   int hash_slots = 64;
   while (hash_slots < 2 * l.n_centroids) hash_slots <<= 1;
-  const size_t lds = Lds<SD, ROWS32>::bytes(n_cpad, hash_slots, SCALED ? codes.head_dim : 0) +
-                     (ACC ? static_cast<size_t>(l.n_centroids) * (SD * 8 + 4) : 0);
+  const int arows_len = (SCALED && SD == 4 && ROWS32) ? 2 * n_cpad : 0;
+  const size_t lds =
+      Lds<SD, ROWS32>::bytes(n_cpad, hash_slots, SCALED ? codes.head_dim : 0, arows_len) +
+      (ACC ? static_cast<size_t>(l.n_centroids) * (SD * 8 + 4) : 0);
   auto kern = encode_mfma_kernel<SD, T, BLOCK, BF16, ROWS32, SCALED, ACC>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),

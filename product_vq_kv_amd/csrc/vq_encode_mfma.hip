@@ -776,7 +776,6 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       }
       uint32_t hw[E / 2], lw[E / 2];
       float nv2 = 0.0f, esum = 0.0f;
-      bool fin = true;
 #pragma unroll
       for (int i = 0; i < E; ++i) {
         const float xt = xo[i] * f[i];
@@ -788,7 +787,6 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
         esum += __builtin_fabsf(r - lf);
         const float v = __builtin_fabsf(hf) + __builtin_fabsf(lf);
         nv2 = __builtin_fmaf(v, v, nv2);
-        fin = fin && (__builtin_fabsf(hf) <= kFltMax);
         if (i & 1) {
           hw[i >> 1] |= static_cast<uint32_t>(hb) << 16;
           lw[i >> 1] |= static_cast<uint32_t>(lb) << 16;
@@ -807,8 +805,9 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       }
       nv2 = pair_sum(nv2);
       esum = pair_sum(esum);
-      fin = fin && (pair_other(fin ? 1u : 0u, h) != 0u);
-      const bool ex = !fin || !(nv2 <= kNormCap) || exact_tile;
+      // a non-finite part (x~ beyond the element type, or not finite) makes
+      // nv2 infinite or NaN, which sends the column to the full exact scan
+      const bool ex = !(nv2 <= kNormCap) || exact_tile;
       full_bits |= (ex ? 1u : 0u) << t;
       bn[t] = ex ? 0.0f
                  : __builtin_fmaf(esum, K::kInvKappaUp, sqrt_up(nv2)) * kBnUp;

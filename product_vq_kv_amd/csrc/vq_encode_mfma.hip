@@ -664,7 +664,14 @@ __device__ __forceinline__ void factors(const Lds<SD, ROWS32> &s, int m, float (
 struct Smooth {
   int n_sub;
   float inv_n_sub;
+  int mask;  // n_sub - 1 when n_sub is a power of two (every usual head_dim), else -1
 };
+
+// v mod n_sub for 0 <= v < 2^24 (a mask when n_sub is a power of two)
+template <bool POW2>
+__device__ __forceinline__ int sub_mod(int v, const Smooth &sm) {
+  return POW2 ? (v & sm.mask) : mod_small(v, sm.n_sub, sm.inv_n_sub);
+}
 
 // Raw words of the T sub-vectors this lane loads for a unit: column t, row
 // ubase + 32 t + lane mod 32 (zero past the group's end).
@@ -729,7 +736,7 @@ __device__ __forceinline__ void add_unit_sums(const UnitSums<SD, T> &us, int64_t
 
 // One unit: the wave encodes T columns of 32 sub-vectors, rows ubase ..
 // ubase + 32 T - 1 (raw words from load_unit_x).
-template <int SD, int T, bool BF16, bool ROWS32, bool SCALED, bool ACC>
+template <int SD, int T, bool BF16, bool ROWS32, bool SCALED, bool ACC, bool POW2>
 __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t gend, int n_c,
                             int n_cpad, const Lds<SD, ROWS32> &s, bool exact_tile, bool fold,
                             const Smooth sm, int sub0, int code_bits, uint8_t *__restrict__ out,
@@ -749,7 +756,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
   int g1[T];
   uint32_t codes[T];
   // smoothed keys: sub-slot of this lane's column 0 (sub0 = ubase mod n_sub)
-  const int m0 = SCALED ? mod_small(sub0 + col, sm.n_sub, sm.inv_n_sub) : 0;
+  const int m0 = SCALED ? sub_mod<POW2>(sub0 + col, sm) : 0;
   uint32_t full_bits = 0;  // bit t: column t takes the full exact scan
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -760,7 +767,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       // the half of the other operand for the half it lacks: h = 0 builds the
       // hi operand, h = 1 the lo operand
       constexpr int E = SD / 2;
-      const int m = mod_small(m0 + 32 * t, sm.n_sub, sm.inv_n_sub);
+      const int m = sub_mod<POW2>(m0 + 32 * t, sm);
       // this lane's E components: words 0 .. E/2-1 (h = 0) or E/2 .. E-1
       // (a mask select: a select between array elements becomes an indexed
       // load from private memory)
@@ -951,7 +958,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
         column_x<SD, BF16>(xw[t], xv);
       }
       float f[SD];
-      factors<SD, ROWS32>(s, mod_small(m0 + 32 * t, sm.n_sub, sm.inv_n_sub), f);
+      factors<SD, ROWS32>(s, sub_mod<POW2>(m0 + 32 * t, sm), f);
 #pragma unroll
       for (int i = 0; i < SD; ++i) xv[i] = xv[i] * f[i];
     } else {
@@ -1128,10 +1135,11 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
   constexpr bool kARows = SCALED && SD == 4 && ROWS32;
   const Lds<SD, ROWS32> s(lds_raw, n_cpad, hash_slots, kARows ? 2 * n_cpad : 0);
   const int scale_len = SCALED ? head_dim : 0;
-  Smooth sm{1, 1.0f};
+  Smooth sm{1, 1.0f, 0};
   if constexpr (SCALED) {
     sm.n_sub = head_dim / SD;
     sm.inv_n_sub = 1.0f / static_cast<float>(sm.n_sub);
+    sm.mask = (sm.n_sub & (sm.n_sub - 1)) == 0 ? sm.n_sub - 1 : -1;
   }
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -1198,13 +1206,23 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
           for (int64_t b = ubase * bpc + lane; b < bend; b += 64) out[b] = 0xFFu;
         }
       } else {
-        int sub0 = 0;
         if constexpr (SCALED) {
-          const uint32_t off = static_cast<uint32_t>(u - g_unit0) * kUnit % static_cast<uint32_t>(sm.n_sub);
-          sub0 = mod_small(seg_sub0 + static_cast<int>(off), sm.n_sub, sm.inv_n_sub);
+          // sub-slot of the unit's first row: (group start + unit offset) mod n_sub
+          const uint32_t rel = static_cast<uint32_t>(u - g_unit0) * kUnit;
+          if (sm.mask >= 0) {  // uniform
+            const int sub0 = (seg_sub0 + static_cast<int>(rel & static_cast<uint32_t>(sm.mask))) & sm.mask;
+            encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, true>(
+                xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, sub0, code_bits, out, us);
+          } else {
+            const uint32_t off = rel % static_cast<uint32_t>(sm.n_sub);
+            const int sub0 = mod_small(seg_sub0 + static_cast<int>(off), sm.n_sub, sm.inv_n_sub);
+            encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, false>(
+                xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, sub0, code_bits, out, us);
+          }
+        } else {
+          encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, false>(
+              xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, 0, code_bits, out, us);
         }
-        encode_unit<SD, T, BF16, ROWS32, SCALED, ACC>(xw, ubase, gend, n_c, n_cpad, s, exact_tile,
-                                                      fold, sm, sub0, code_bits, out, us);
       }
       // the next unit is taken (a returning LDS atomic, which would wait
       // behind the member-sum atomics) and its loads issued before this

@@ -1119,7 +1119,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
 // take units from a counter in LDS: a wave that runs ahead takes more units,
 // so all waves of the CU finish close together (the issue arbiter favours
 // the oldest waves, which would otherwise finish far ahead of the others).
-template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED, bool ACC>
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED, bool ACC, bool POW2>
 __global__ void __launch_bounds__(BLOCK, 1)
 encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ codebook,
                    int64_t n, int n_c, int64_t cb_stride, int64_t n_codebooks, int64_t group_len,
@@ -1209,16 +1209,15 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
         if constexpr (SCALED) {
           // sub-slot of the unit's first row: (group start + unit offset) mod n_sub
           const uint32_t rel = static_cast<uint32_t>(u - g_unit0) * kUnit;
-          if (sm.mask >= 0) {  // uniform
-            const int sub0 = (seg_sub0 + static_cast<int>(rel & static_cast<uint32_t>(sm.mask))) & sm.mask;
-            encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, true>(
-                xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, sub0, code_bits, out, us);
+          int sub0;
+          if constexpr (POW2) {  // the host launches this form only for a power of two
+            sub0 = (seg_sub0 + static_cast<int>(rel & static_cast<uint32_t>(sm.mask))) & sm.mask;
           } else {
             const uint32_t off = rel % static_cast<uint32_t>(sm.n_sub);
-            const int sub0 = mod_small(seg_sub0 + static_cast<int>(off), sm.n_sub, sm.inv_n_sub);
-            encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, false>(
-                xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, sub0, code_bits, out, us);
+            sub0 = mod_small(seg_sub0 + static_cast<int>(off), sm.n_sub, sm.inv_n_sub);
           }
+          encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, POW2>(
+              xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, sub0, code_bits, out, us);
         } else {
           encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, false>(
               xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, 0, code_bits, out, us);
@@ -1260,7 +1259,8 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
   } while (seg < u_last);
 }
 
-template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED, bool ACC = false>
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED, bool ACC = false,
+          bool POW2 = false>
 hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_map, void *out,
                     const Layout &l, const Codes &codes, hipStream_t stream, int64_t cus,
                     const KmSums &acc = KmSums{nullptr, nullptr}) {
@@ -1275,7 +1275,7 @@ hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_ma
   const size_t lds =
       Lds<SD, ROWS32>::bytes(n_cpad, hash_slots, SCALED ? codes.head_dim : 0, arows_len) +
       (ACC ? static_cast<size_t>(l.n_centroids) * (SD * 8 + 4) : 0);
-  auto kern = encode_mfma_kernel<SD, T, BLOCK, BF16, ROWS32, SCALED, ACC>;
+  auto kern = encode_mfma_kernel<SD, T, BLOCK, BF16, ROWS32, SCALED, ACC, POW2>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1321,15 +1321,29 @@ int cu_count() {
 template <int SD, bool SCALED, bool ROWS32>
 constexpr int columns() { return SCALED ? 2 : 4; }
 
+template <int SD, bool BF16, bool SCALED, bool POW2>
+hipError_t launch_sd_p(const void *x, const void *codebook, const int32_t *group_map, void *out,
+                       const Layout &l, const Codes &codes, hipStream_t stream) {
+  const int64_t cus = cu_count();
+  if (l.n_centroids > kRows32MaxCentroids)
+    return launch_t<SD, columns<SD, SCALED, false>(), 1024, BF16, false, SCALED, false, POW2>(
+        x, codebook, group_map, out, l, codes, stream, cus);
+  return launch_t<SD, columns<SD, SCALED, true>(), 1024, BF16, true, SCALED, false, POW2>(
+      x, codebook, group_map, out, l, codes, stream, cus);
+}
+
+// Smoothed keys: the channel index is a mask when head_dim / sub_dim is a
+// power of two (a form of its own, so that neither form holds the other's
+// registers).
 template <int SD, bool BF16, bool SCALED>
 hipError_t launch_sd(const void *x, const void *codebook, const int32_t *group_map, void *out,
                      const Layout &l, const Codes &codes, hipStream_t stream) {
-  const int64_t cus = cu_count();
-  if (l.n_centroids > kRows32MaxCentroids)
-    return launch_t<SD, columns<SD, SCALED, false>(), 1024, BF16, false, SCALED>(
-        x, codebook, group_map, out, l, codes, stream, cus);
-  return launch_t<SD, columns<SD, SCALED, true>(), 1024, BF16, true, SCALED>(
-      x, codebook, group_map, out, l, codes, stream, cus);
+  if constexpr (SCALED) {
+    const int n_sub = codes.head_dim / SD;
+    if ((n_sub & (n_sub - 1)) == 0)
+      return launch_sd_p<SD, BF16, true, true>(x, codebook, group_map, out, l, codes, stream);
+  }
+  return launch_sd_p<SD, BF16, SCALED, false>(x, codebook, group_map, out, l, codes, stream);
 }
 
 // The plain kernel handles unsmoothed keys with 8, 16 or 32-bit codes (one

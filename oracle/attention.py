@@ -31,7 +31,10 @@ returns the quantities the GPU comparison's error bound is built from.
 Pinned by ``tests/test_oracle_attention.py`` against torch's float64
 scaled-dot-product attention, closed forms (one token, equal keys, zero
 query), the LUT identity, grouped-query and window brute force, and planted
-mistakes.
+mistakes.  ``tolerance_terms`` is pinned by
+``tests/test_oracle_attention_bound.py``: hand-worked A, T and M (one token,
+a window over a grouped-query group with closed-form weights, equal keys)
+and planted mistakes in each of the three.
 """
 from __future__ import annotations
 

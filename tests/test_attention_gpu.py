@@ -1,28 +1,27 @@
 """GPU parity of decode attention over VQ codes against the float64 oracle.
 
 ``vq_attention_decode`` (through its C ABI) must match oracle/attention.py
-within an error bound derived from its fp32 arithmetic:
+within the error bound of tests/attention_bound.py, derived from fp32
+arithmetic in any summation order:
 
-  score error (natural-log units)  Delta <= 1.5 (sd_k + n_sub_k + 4) u A
-      A = scale * max_t sum_i |q_i k_ti|: the LUT entry is an sd_k-term fp32
-      dot product, the score a sum of n_sub_k entries, plus q / f, the
-      scale * log2(e) multiply and the base change (4 roundings);
-  |out - ref|  <=  (2 Delta + (3 T + 32) u) * M_d  (+ 1e-30)
-      M_d = sum_t p_t |v_td|; T attended tokens: exp2 and its input roundings,
-      the fp32 sums of weights and of weighted values, the chunk rescales.
+  |out - ref|  <=  (2 Delta + (3 T + 32) u) * M_d,
+  Delta = 1.5 (sd_k + n_sub_k + 4) u A,
 
-The bound is what the arithmetic guarantees in the worst case; the measured
-error is reported too and is typically ~1e-7 of M.  Cases cover both code
-sub-dims for keys and values, fp16 and bf16, smoothed and plain keys,
-grouped-query groups 1..8, head_dim 16..256, multi-chunk and ragged lengths
-(empty and one-token sequences), windows, codes past the codebook, a dirty
-workspace, and the Falcon3-7B decode workload at full size.
+with A, T and M_d from the (pinned) ``tolerance_terms``.  The measured error
+is reported too and is typically ~1e-7 of M.  Cases cover both code sub-dims
+for keys and values, fp16 and bf16, smoothed and plain keys, grouped-query
+groups 1..8, head_dim 16..256, multi-chunk and ragged lengths (empty and
+one-token sequences), windows, codes past the codebook, a dirty workspace,
+the Falcon3-7B decode workload at full size, and that workload with the
+tokens next to every 256-token chunk boundary carrying the attention (so a
+dropped, repeated or misweighted boundary token is far outside the bound).
 """
 import numpy as np
 import pytest
 
 import workloads as W
 from oracle import attention as A
+from tests import attention_bound as AB
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +32,6 @@ if not torch.cuda.is_available():
 import product_vq_kv_amd as vq  # noqa: E402
 
 DEV = torch.device("cuda:0")
-U = 2.0 ** -24
 
 
 def to_dev(wl):
@@ -72,9 +70,8 @@ def assert_attention_parity(wl):
     got = gpu_attention(wl)
     sdk = D // wl.k_codes.shape[3]
     n_sub_k = wl.k_codes.shape[3]
-    delta = 1.5 * (sdk + n_sub_k + 4) * U * Aq
-    rel = 2 * delta + (3 * T + 32) * U
-    bound = rel[:, :, None] * M + 1e-30
+    rel = AB.relative_bound(Aq, T, sdk, n_sub_k)
+    bound = AB.bound(Aq, T, M, sdk, n_sub_k)
     err = np.abs(got - ref)
     worst = float(np.max(err / np.maximum(M, 1e-300))) if M.size else 0.0
     print(f"[parity] {wl.name}: max |err| / M = {worst:.3e}, "
@@ -137,5 +134,13 @@ def test_all_sequences_empty():
 
 def test_falcon_decode_workload_full_size():
     wl = W.falcon_decode_attention()
+    print(f"[case] {wl.name}", flush=True)
+    assert_attention_parity(wl)
+
+
+def test_falcon_decode_boundary_tokens_carry_the_attention():
+    wl = W.falcon_decode_attention(B=8)
+    AB.make_boundary_tokens_heavy(wl)
+    wl.name += ", boundary tokens heavy"
     print(f"[case] {wl.name}", flush=True)
     assert_attention_parity(wl)

@@ -42,7 +42,7 @@ STATUS = {0: "VQ_OK", -1: "VQ_ERR_INVALID_ARG", -2: "VQ_ERR_UNSUPPORTED",
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvq.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m product_vq_kv_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python product_vq_kv_amd/build.py` "
                       "(there is no CPU fallback)")
 
 lib = ctypes.CDLL(LIB_PATH)

@@ -1,6 +1,6 @@
 """Compile the HIP library libvq.so for gfx950, in-tree.
 
-    python -m product_vq_kv_amd.build
+    python product_vq_kv_amd/build.py     (a script: it imports nothing of the package)
 
 Flags:
   * --offload-arch=gfx950: CDNA4 only, no other targets;

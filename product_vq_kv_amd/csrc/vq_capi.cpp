@@ -59,13 +59,9 @@ vq_status launch(const void *x, const void *codebook, const int32_t *group_map, 
     return VQ_ERR_INVALID_ARG;
   (void)hipGetLastError();  // drop a stale error so it is not reported as ours
   const hipStream_t s = static_cast<hipStream_t>(stream);
-#ifdef VQ_ENCODE_DIRECT_ONLY
-  return device_result(vqk::launch_encode(x, codebook, group_map, out, l, codes, s));
-#else
   if (vqk::encode_mfma_supported(l))
     return device_result(vqk::launch_encode_mfma(x, codebook, group_map, out, l, codes, s));
   return device_result(vqk::launch_encode(x, codebook, group_map, out, l, codes, s));
-#endif
 }
 
 }  // namespace

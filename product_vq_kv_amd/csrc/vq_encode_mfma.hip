@@ -1207,13 +1207,16 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
         }
       } else {
         if constexpr (SCALED) {
-          // sub-slot of the unit's first row: (group start + unit offset) mod n_sub
-          const uint32_t rel = static_cast<uint32_t>(u - g_unit0) * kUnit;
+          // sub-slot of the unit's first row: (group start + unit offset) mod
+          // n_sub; the offset can pass 2^32 rows in one group
+          const int64_t rel = (u - g_unit0) * kUnit;
           int sub0;
           if constexpr (POW2) {  // the host launches this form only for a power of two
-            sub0 = (seg_sub0 + static_cast<int>(rel & static_cast<uint32_t>(sm.mask))) & sm.mask;
+            sub0 = (seg_sub0 + static_cast<int>(rel & sm.mask)) & sm.mask;
           } else {
-            const uint32_t off = rel % static_cast<uint32_t>(sm.n_sub);
+            const uint32_t off = (rel >> 32) == 0
+                                     ? static_cast<uint32_t>(rel) % static_cast<uint32_t>(sm.n_sub)
+                                     : static_cast<uint32_t>(rel % sm.n_sub);
             sub0 = mod_small(seg_sub0 + static_cast<int>(off), sm.n_sub, sm.inv_n_sub);
           }
           encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, POW2>(

@@ -4,10 +4,9 @@ Small seeded cases span several tiles (1024 sub-vectors per workgroup) and
 LDS chunks (1024 centroids), with ragged tails, groups that do not align with
 tiles, padded slot strides, group maps with invalid slots, duplicate rows,
 non-finite values and the largest codebook the ABI allows.  The five full-size
-workloads run in the launch configuration the benchmark times; the oracle
-checks every row of the smaller ones and a seeded sample (plus the first and
-last tiles of several groups) of the full cache.  Acceptance rule: see
-tests/parity.py.
+workloads run in the launch configuration the benchmark times and the
+oracle (threaded over the host cores) checks every row of each, the full
+cache's 33,554,432 included.  Acceptance rule: see tests/parity.py.
 """
 import numpy as np
 import pytest
@@ -374,14 +373,14 @@ def test_full_size_config_every_row(cfg):
     assert abs(mse_gpu - mse_ref) <= 1e-6 * mse_ref
 
 
-def test_full_cache_sampled_rows():
+def test_full_cache_every_row():
+    """The full batched cache (33,554,432 sub-vectors, 256 codebook slots):
+    every row against the oracle, threaded over the host cores."""
     wl = W.config(4)
     print(f"[config 4] {wl.name} n={wl.n}", flush=True)
     got = gpu_encode(wl)
-    r = np.random.default_rng(44)
-    rows = [r.choice(wl.n, size=1 << 17, replace=False)]
-    for g in (0, 1, 127, 128, 200, 255):      # first and last tiles of some groups
-        lo = g * wl.group_len
-        rows += [np.arange(lo, lo + 1024), np.arange(lo + wl.group_len - 1024, lo + wl.group_len)]
-    rows = np.unique(np.concatenate(rows))
-    assert_parity(wl, got, rows)
+    ref = parity.oracle_indices(wl)
+    rep = parity.compare(wl, got, ref_idx=ref)
+    print(f"[parity] {wl.name}: {rep.summary()}", flush=True)
+    assert rep.ok, rep.summary()
+    assert rep.rows == wl.n == 33554432

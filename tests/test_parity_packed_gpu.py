@@ -7,9 +7,8 @@ sub-vector lengths, every kernel form (matrix-core with and without the fp32
 codebook copy, one and two columns per wave, the direct kernel beyond 4096
 centroids), ragged tails, several slots with per-slot factors, group maps with
 bad slots, and extreme factors (overflow, subnormal, zero, negative, NaN).
-The smoothed Falcon3-7B-shape cache runs at full size and every row is
-checked; the smoothed full cache is checked on seeded whole chunks and group
-boundaries.  Acceptance: the same rule as the plain encode (exact equality
+The smoothed Falcon3-7B-shape cache and the smoothed full cache (33,554,432
+sub-vectors, 256 slots) run at full size and every row is checked.  Acceptance: the same rule as the plain encode (exact equality
 except near-ties within 1e-6 relative); the kernels are exact, so every byte
 is required to match.
 """
@@ -124,6 +123,19 @@ PACKED = [
     # duplicate rows in it)
     (20, 8192, 4, 256, W.F16, 8, True, 64, dict(scale=300.0)),
     (21, 8192, 4, 256, W.F16, 8, True, 16, dict(dup_frac=0.2, scale=300.0)),
+    # 128 sub-slots per key (head_dim 512 / 1024): a unit's first row and a
+    # group's first row sit at nonzero sub-slots (power-of-two form); group
+    # lengths that are not multiples of the key length
+    (22, 4700, 4, 256, W.F16, 8, True, 128, dict(n_codebooks=5, group_len=1000)),
+    (23, 5000, 8, 256, W.F16, 8, True, 128, dict(n_codebooks=3, group_len=1800)),
+    (24, 3000, 4, 300, W.BF16, 9, True, 256, dict(n_codebooks=2, group_len=2016)),
+    # key lengths that are not a power of two (general sub-slot form): sub_dim
+    # 8, bf16, more than 1024 centroids, several groups
+    (25, 3000, 8, 2000, W.BF16, 11, True, 10, dict(n_codebooks=2, group_len=1600)),
+    (26, 2600, 4, 1500, W.BF16, 11, True, 24, {}),
+    (27, 3000, 8, 256, W.F16, 8, True, 12, dict(n_codebooks=3, group_len=1004)),
+    (28, 4000, 4, 256, W.F16, 8, True, 20, dict(n_codebooks=4, group_len=1004, use_map=True)),
+    (29, 2100, 8, 5000, W.BF16, 13, True, 6, {}),
 ]
 
 
@@ -257,25 +269,13 @@ def test_full_size_falcon_smoothed_every_row():
     assert_packed_parity(wl, gpu_packed(wl, 8), 8)
 
 
-def test_full_cache_smoothed_sampled_chunks():
+def test_full_cache_smoothed_every_row():
+    """The smoothed full cache (33,554,432 sub-vectors, 256 slots with their
+    own factors): every code byte against the oracle."""
     wl = W.full_cache_smoothed()
-    print(f"[case] {wl.name}", flush=True)
-    got = gpu_packed(wl, 8)
-    r = np.random.default_rng(147)
-    glen, n_sub = wl.group_len, wl.head_dim // wl.sub_dim
-    starts = list(r.integers(0, wl.n // n_sub - 64, size=48) * n_sub)
-    for g in (0, 1, 100, 255):          # first and last rows of some groups
-        starts += [g * glen, (g + 1) * glen - 64 * n_sub]
-    stride = wl.codebook_stride
-    for r0 in starts:
-        r0 = int(r0)
-        g = r0 // glen
-        length = min(64 * n_sub, (g + 1) * glen - r0)
-        want = oracle.encode_packed(wl.x[r0:r0 + length], wl.codebook[g * stride:(g + 1) * stride],
-                                    wl.sub_dim, wl.n_centroids, wl.dtype,
-                                    channel_scale=wl.channel_scale[g], head_dim=wl.head_dim,
-                                    code_bits=8)
-        assert np.array_equal(got[r0:r0 + length], want), f"chunk at row {r0} (group {g})"
+    print(f"[case] {wl.name} n={wl.n}", flush=True)
+    assert wl.n == 33554432
+    assert_packed_parity(wl, gpu_packed(wl, 8), 8)
 
 
 def test_smoothed_keys_beyond_the_fp16_error_operand():
@@ -289,3 +289,49 @@ def test_smoothed_keys_beyond_the_fp16_error_operand():
     print(f"[case] {wl.name} factors x 2^14", flush=True)
     got = gpu_packed(wl, 8)
     assert_packed_parity(wl, got, 8)
+
+
+@pytest.mark.parametrize("head_dim", [80, 128])
+def test_one_group_past_2_32_rows_sampled(head_dim):
+    """One group of 2^32 + 2^20 + 100 smoothed sub-vectors of sub_dim 4 (32 GiB
+    of keys): unit offsets inside the group pass 2^32 rows, where the
+    sub-slot of a unit's first row must still be (group start + offset) mod
+    n_sub, for a key length that is not a power of two (80 / 4 = 20 sub-slots)
+    and one that is (128 / 4 = 32).  Keys are drawn on the device; seeded whole
+    keys around 2^32, at random and at the ragged tail are checked against
+    the oracle."""
+    sd = 4
+    n_sub = head_dim // sd
+    n = 2 ** 32 + 2 ** 20 + 100
+    cbw = W.random_case(45, 1, sd, 256, W.F16)
+    f = np.exp(0.5 * np.random.default_rng([901, head_dim]).standard_normal(head_dim))
+    f = f.astype(np.float32)
+    x = torch.empty(n, sd, dtype=torch.float16, device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(45)
+    step = 2 ** 28
+    for i in range(0, n, step):
+        j = min(n, i + step)
+        x[i:j] = torch.randn(j - i, sd, generator=gen, device=DEV).to(torch.float16)
+    cb = torch.from_numpy(cbw.codebook.view(np.int16)).view(torch.float16).to(DEV).view(256, sd)
+    codes = vq.encode_packed(x, cb, channel_scale=torch.from_numpy(f).to(DEV), head_dim=head_dim,
+                             code_bits=8)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(45)
+    key = 64 * n_sub          # whole keys of 64 tokens
+    starts = [0, (2 ** 32 // n_sub) * n_sub - key, (2 ** 32 // n_sub) * n_sub,
+              ((n - key) // n_sub) * n_sub]
+    starts += [int(r) * n_sub for r in rng.integers(0, (n - key) // n_sub, 24)]
+    checked = 0
+    for r0 in starts:
+        r1 = min(n, r0 + key)
+        xs = x[r0:r1].cpu().view(torch.int16).numpy().view(np.uint16)
+        got = codes[r0:r1].cpu().numpy()
+        want = oracle.encode_packed(xs, cbw.codebook, sd, 256, W.F16, channel_scale=f,
+                                    head_dim=head_dim, code_bits=8)
+        assert np.array_equal(got, want), f"rows {r0}..{r1} (head_dim {head_dim})"
+        checked += r1 - r0
+    del x, codes
+    torch.cuda.empty_cache()
+    print(f"[parity] one group of {n} rows, head_dim {head_dim}: {checked} sampled rows equal",
+          flush=True)

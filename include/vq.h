@@ -60,7 +60,9 @@ typedef enum {
                                 packed groups not ending on a 32-bit word of the stream */
     VQ_ERR_MISALIGNED = -3,  /* x not aligned to 2*sub_dim bytes, codebook to 2,
                                 idx/out/codes/factors to 4 */
-    VQ_ERR_DEVICE = -4       /* the HIP launch failed; see vq_last_hip_error() */
+    VQ_ERR_DEVICE = -4,      /* the HIP launch failed; see vq_last_hip_error() */
+    VQ_ERR_TOO_LARGE = -5    /* the call needs more scratch than the static buffer of
+                                vq_attention_decode_static holds */
 } vq_status;
 
 /* Index written for every sub-vector of a group whose group_map entry is not
@@ -71,7 +73,8 @@ typedef enum {
 #define VQ_ATTN_MAX_HEAD_DIM 256
 #define VQ_ATTN_MAX_GROUP 8
 #define VQ_KMEANS_MAX_SLOT_ROWS (1 << 23)
-#define VQ_ABI_VERSION 4
+#define VQ_ATTN_STATIC_SCRATCH_BYTES (32u << 20)
+#define VQ_ABI_VERSION 5
 
 /*
  * vq_encode -- nearest-centroid index of every sub-vector.
@@ -238,6 +241,33 @@ vq_status vq_attention_decode(const void *q, const uint8_t *k_codes, const uint8
                               int32_t n_centroids, vq_dtype dtype, int32_t window,
                               float softmax_scale, float *out, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/*
+ * vq_attention_decode_static -- vq_attention_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  Same arguments, arithmetic and
+ * result as vq_attention_decode, without `workspace` / `workspace_bytes`:
+ * the chunk partials go to a static device buffer of
+ * VQ_ATTN_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  Its address is resolved once per device, on the
+ * first call with that device current.  The call allocates nothing.
+ *
+ * Returns VQ_ERR_TOO_LARGE (and launches nothing) when
+ * vq_attention_workspace_bytes(batch, n_q_heads, head_dim, max_kv_len)
+ * exceeds VQ_ATTN_STATIC_SCRATCH_BYTES (e.g. 32 sequences x 12 query heads x
+ * 4096 tokens x head_dim 256 needs 6.3 MB).  Every call on one GPU shares that
+ * GPU's buffer: calls must be ordered (one stream, or synchronised); calls that
+ * overlap on one GPU race and their results are undefined.  Nothing in the
+ * buffer needs to start at zero (every partial is written before it is read).
+ */
+vq_status vq_attention_decode_static(const void *q, const uint8_t *k_codes,
+                                     const uint8_t *v_codes, const void *k_codebook,
+                                     const void *v_codebook, const float *k_scale,
+                                     const int32_t *kv_len, int32_t batch, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t head_dim, int32_t max_kv_len,
+                                     int32_t k_sub_dim, int32_t v_sub_dim, int32_t n_centroids,
+                                     vq_dtype dtype, int32_t window, float softmax_scale,
+                                     float *out, void *stream);
 
 /*
  * vq_decode -- gather used to check encode: row n of out_x is centroid idx[n]

@@ -28,7 +28,8 @@ import torch  # loads the HIP runtime that libvq.so binds to (same soname)
 
 __all__ = ["encode", "decode", "encode_packed", "packed_bytes", "attention_decode",
            "attention_workspace_bytes", "kmeans", "kmeans_workspace_bytes", "kmeans_raw", "encode_raw", "decode_raw", "encode_packed_raw",
-           "attention_decode_raw", "VQError", "lib", "LIB_PATH", "F16", "BF16", "BAD_SLOT",
+           "attention_decode_raw", "attention_decode_static", "attention_decode_static_raw",
+           "ATTN_STATIC_SCRATCH_BYTES", "VQError", "lib", "LIB_PATH", "F16", "BF16", "BAD_SLOT",
            "MAX_CENTROIDS", "MAX_HEAD_DIM", "STATUS"]
 
 F16 = 0
@@ -36,8 +37,9 @@ BF16 = 1
 BAD_SLOT = 0xFFFFFFFF
 MAX_CENTROIDS = 65536
 MAX_HEAD_DIM = 4096
+ATTN_STATIC_SCRATCH_BYTES = 32 << 20
 STATUS = {0: "VQ_OK", -1: "VQ_ERR_INVALID_ARG", -2: "VQ_ERR_UNSUPPORTED",
-          -3: "VQ_ERR_MISALIGNED", -4: "VQ_ERR_DEVICE"}
+          -3: "VQ_ERR_MISALIGNED", -4: "VQ_ERR_DEVICE", -5: "VQ_ERR_TOO_LARGE"}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvq.so")
 
@@ -61,6 +63,10 @@ lib.vq_attention_decode.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32
                                     _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _p,
                                     ctypes.c_size_t, _p]
 lib.vq_attention_decode.restype = _i32
+lib.vq_attention_decode_static.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32,
+                                           _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
+                                           _p, _p]
+lib.vq_attention_decode_static.restype = _i32
 lib.vq_kmeans_workspace_bytes.argtypes = [_i32, _i32, _i64]
 lib.vq_kmeans_workspace_bytes.restype = ctypes.c_size_t
 lib.vq_kmeans.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _i32, _p, _p,
@@ -290,12 +296,40 @@ def attention_decode_raw(q_ptr, k_codes_ptr, v_codes_ptr, k_cb_ptr, v_cb_ptr, k_
            "vq_attention_decode")
 
 
+def attention_decode_static_raw(q_ptr, k_codes_ptr, v_codes_ptr, k_cb_ptr, v_cb_ptr,
+                                k_scale_ptr, kv_len_ptr, batch, n_q_heads, n_kv_heads, head_dim,
+                                max_kv_len, k_sub_dim, v_sub_dim, n_centroids, dtype, window,
+                                softmax_scale, out_ptr, stream) -> None:
+    """Direct call of ``vq_attention_decode_static`` (raises on error)."""
+    _check(lib.vq_attention_decode_static(q_ptr, k_codes_ptr, v_codes_ptr, k_cb_ptr, v_cb_ptr,
+                                          k_scale_ptr, kv_len_ptr, batch, n_q_heads, n_kv_heads,
+                                          head_dim, max_kv_len, k_sub_dim, v_sub_dim,
+                                          n_centroids, dtype, window, softmax_scale, out_ptr,
+                                          stream),
+           "vq_attention_decode_static")
+
+
+def attention_decode_static(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor,
+                            k_codebook: torch.Tensor, v_codebook: torch.Tensor, *,
+                            k_scale: Optional[torch.Tensor] = None,
+                            kv_len: Optional[torch.Tensor] = None, window: int = 0,
+                            softmax_scale: Optional[float] = None, out: torch.Tensor,
+                            stream=None) -> torch.Tensor:
+    """``attention_decode`` through the allocation-free entry point: the
+    caller passes `out` (fp32 [B, Hq, D]); the chunk partials use the
+    library's static per-GPU scratch, so nothing is allocated."""
+    return attention_decode(q, k_codes, v_codes, k_codebook, v_codebook, k_scale=k_scale,
+                            kv_len=kv_len, window=window, softmax_scale=softmax_scale, out=out,
+                            stream=stream, _static=True)
+
+
 def attention_decode(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor,
                      k_codebook: torch.Tensor, v_codebook: torch.Tensor, *,
                      k_scale: Optional[torch.Tensor] = None,
                      kv_len: Optional[torch.Tensor] = None, window: int = 0,
                      softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                     workspace: Optional[torch.Tensor] = None, stream=None,
+                     _static: bool = False) -> torch.Tensor:
     """Decode attention from 8-bit VQ codes: fp32 [B, Hq, D].
 
     q           fp16/bf16 [B, Hq, D]
@@ -340,6 +374,12 @@ def attention_decode(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tens
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     elif out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, D) or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp32 tensor [B, Hq, D]")
+    if _static:
+        attention_decode_static_raw(q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
+                                    k_codebook.data_ptr(), v_codebook.data_ptr(), sptr, lptr, B,
+                                    Hq, Hkv, D, S, sdk, sdv, n_c, dt, window, softmax_scale,
+                                    out.data_ptr(), _stream_of(q.device, stream))
+        return out
     need = attention_workspace_bytes(B, Hq, D, S)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)

@@ -28,7 +28,10 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
+#include "vq.h"
 #include "vq_launch.h"
 
 namespace vqk {
@@ -965,6 +968,34 @@ hipError_t launch_attn_dt(const AttnArgs &a, int sdk, int sdv, bool mfma, hipStr
 }
 
 }  // namespace
+
+// Chunk partials of vq_attention_decode_static, for callers that cannot
+// allocate: one copy per GPU (the code object's device data), held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[VQ_ATTN_STATIC_SCRATCH_BYTES];
+
+hipError_t attention_static_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 int attention_chunks(int max_kv_len) { return std::max(1, (max_kv_len + kMChunk - 1) / kMChunk); }
 

@@ -64,6 +64,64 @@ vq_status launch(const void *x, const void *codebook, const int32_t *group_map, 
   return device_result(vqk::launch_encode(x, codebook, group_map, out, l, codes, s));
 }
 
+// Checks of the attention arguments shared by both entry points (all but the
+// workspace); fills everything in *l except l->workspace.
+vq_status check_attention(const void *q, const uint8_t *k_codes, const uint8_t *v_codes,
+                          const void *k_codebook, const void *v_codebook, const float *k_scale,
+                          const int32_t *kv_len, int32_t batch, int32_t n_q_heads,
+                          int32_t n_kv_heads, int32_t head_dim, int32_t max_kv_len,
+                          int32_t k_sub_dim, int32_t v_sub_dim, int32_t n_centroids,
+                          vq_dtype dtype, int32_t window, float softmax_scale, float *out,
+                          vqk::AttnLayout *l) {
+  if ((k_sub_dim != 4 && k_sub_dim != 8) || (v_sub_dim != 4 && v_sub_dim != 8))
+    return VQ_ERR_UNSUPPORTED;
+  if (dtype != VQ_F16 && dtype != VQ_BF16) return VQ_ERR_UNSUPPORTED;
+  if (n_centroids < 1 || n_centroids > 256) return VQ_ERR_UNSUPPORTED;  // 8-bit codes
+  if (head_dim < 1 || head_dim > VQ_ATTN_MAX_HEAD_DIM) return VQ_ERR_UNSUPPORTED;
+  // key rows are read four codes at a time; value sub-spaces map to lanes
+  if (head_dim % (4 * k_sub_dim) != 0 || head_dim % v_sub_dim != 0) return VQ_ERR_UNSUPPORTED;
+  if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || max_kv_len < 0 || window < 0)
+    return VQ_ERR_INVALID_ARG;
+  if (n_q_heads % n_kv_heads != 0) return VQ_ERR_INVALID_ARG;
+  if (n_q_heads / n_kv_heads > VQ_ATTN_MAX_GROUP) return VQ_ERR_UNSUPPORTED;
+  if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+    return VQ_ERR_INVALID_ARG;
+  if (batch > 65535 || n_kv_heads > 65535) return VQ_ERR_INVALID_ARG;  // grid y / z
+  if (static_cast<int64_t>(batch) * n_q_heads > kMaxGrid) return VQ_ERR_INVALID_ARG;
+  if (batch == 0) return VQ_OK;
+  if (!q || !out || !k_codebook || !v_codebook) return VQ_ERR_INVALID_ARG;
+  if (max_kv_len > 0 && (!k_codes || !v_codes)) return VQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(q) % 2 || reinterpret_cast<uintptr_t>(k_codebook) % 2 ||
+      reinterpret_cast<uintptr_t>(v_codebook) % 2 || reinterpret_cast<uintptr_t>(k_codes) % 4 ||
+      reinterpret_cast<uintptr_t>(out) % 4 || reinterpret_cast<uintptr_t>(k_scale) % 4 ||
+      reinterpret_cast<uintptr_t>(kv_len) % 4)
+    return VQ_ERR_MISALIGNED;
+  if (vqk::attention_lds_bytes(k_sub_dim, v_sub_dim, head_dim, n_q_heads / n_kv_heads) >
+      160 * 1024)
+    return VQ_ERR_UNSUPPORTED;
+  l->q = q;
+  l->k_codes = k_codes;
+  l->v_codes = v_codes;
+  l->k_codebook = k_codebook;
+  l->v_codebook = v_codebook;
+  l->k_scale = k_scale;
+  l->kv_len = kv_len;
+  l->out = out;
+  l->workspace = nullptr;
+  l->batch = batch;
+  l->n_q_heads = n_q_heads;
+  l->n_kv_heads = n_kv_heads;
+  l->head_dim = head_dim;
+  l->max_kv_len = max_kv_len;
+  l->k_sub_dim = k_sub_dim;
+  l->v_sub_dim = v_sub_dim;
+  l->n_centroids = n_centroids;
+  l->bf16 = dtype == VQ_BF16 ? 1 : 0;
+  l->window = window;
+  l->softmax_scale = softmax_scale;
+  return VQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,57 +242,43 @@ vq_status vq_attention_decode(const void *q, const uint8_t *k_codes, const uint8
                               int32_t n_centroids, vq_dtype dtype, int32_t window,
                               float softmax_scale, float *out, void *workspace,
                               size_t workspace_bytes, void *stream) {
-  if ((k_sub_dim != 4 && k_sub_dim != 8) || (v_sub_dim != 4 && v_sub_dim != 8))
-    return VQ_ERR_UNSUPPORTED;
-  if (dtype != VQ_F16 && dtype != VQ_BF16) return VQ_ERR_UNSUPPORTED;
-  if (n_centroids < 1 || n_centroids > 256) return VQ_ERR_UNSUPPORTED;  // 8-bit codes
-  if (head_dim < 1 || head_dim > VQ_ATTN_MAX_HEAD_DIM) return VQ_ERR_UNSUPPORTED;
-  // key rows are read four codes at a time; value sub-spaces map to lanes
-  if (head_dim % (4 * k_sub_dim) != 0 || head_dim % v_sub_dim != 0) return VQ_ERR_UNSUPPORTED;
-  if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || max_kv_len < 0 || window < 0)
-    return VQ_ERR_INVALID_ARG;
-  if (n_q_heads % n_kv_heads != 0) return VQ_ERR_INVALID_ARG;
-  if (n_q_heads / n_kv_heads > VQ_ATTN_MAX_GROUP) return VQ_ERR_UNSUPPORTED;
-  if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
-    return VQ_ERR_INVALID_ARG;
-  if (batch > 65535 || n_kv_heads > 65535) return VQ_ERR_INVALID_ARG;  // grid y / z
-  if (static_cast<int64_t>(batch) * n_q_heads > kMaxGrid) return VQ_ERR_INVALID_ARG;
-  if (batch == 0) return VQ_OK;
-  if (!q || !out || !k_codebook || !v_codebook) return VQ_ERR_INVALID_ARG;
-  if (max_kv_len > 0 && (!k_codes || !v_codes || !workspace)) return VQ_ERR_INVALID_ARG;
+  vqk::AttnLayout l;
+  const vq_status st = check_attention(q, k_codes, v_codes, k_codebook, v_codebook, k_scale,
+                                       kv_len, batch, n_q_heads, n_kv_heads, head_dim, max_kv_len,
+                                       k_sub_dim, v_sub_dim, n_centroids, dtype, window,
+                                       softmax_scale, out, &l);
+  if (st != VQ_OK || batch == 0) return st;
+  if (!workspace) return VQ_ERR_INVALID_ARG;
   if (workspace_bytes < vq_attention_workspace_bytes(batch, n_q_heads, head_dim, max_kv_len))
     return VQ_ERR_INVALID_ARG;
-  if (reinterpret_cast<uintptr_t>(q) % 2 || reinterpret_cast<uintptr_t>(k_codebook) % 2 ||
-      reinterpret_cast<uintptr_t>(v_codebook) % 2 || reinterpret_cast<uintptr_t>(k_codes) % 4 ||
-      reinterpret_cast<uintptr_t>(out) % 4 || reinterpret_cast<uintptr_t>(workspace) % 4 ||
-      reinterpret_cast<uintptr_t>(k_scale) % 4 || reinterpret_cast<uintptr_t>(kv_len) % 4)
-    return VQ_ERR_MISALIGNED;
-  if (!workspace) return VQ_ERR_INVALID_ARG;
-  vqk::AttnLayout l;
-  l.q = q;
-  l.k_codes = k_codes;
-  l.v_codes = v_codes;
-  l.k_codebook = k_codebook;
-  l.v_codebook = v_codebook;
-  l.k_scale = k_scale;
-  l.kv_len = kv_len;
-  l.out = out;
+  if (reinterpret_cast<uintptr_t>(workspace) % 4) return VQ_ERR_MISALIGNED;
   l.workspace = static_cast<float *>(workspace);
-  l.batch = batch;
-  l.n_q_heads = n_q_heads;
-  l.n_kv_heads = n_kv_heads;
-  l.head_dim = head_dim;
-  l.max_kv_len = max_kv_len;
-  l.k_sub_dim = k_sub_dim;
-  l.v_sub_dim = v_sub_dim;
-  l.n_centroids = n_centroids;
-  l.bf16 = dtype == VQ_BF16 ? 1 : 0;
-  l.window = window;
-  l.softmax_scale = softmax_scale;
-  if (vqk::attention_lds_bytes(k_sub_dim, v_sub_dim, head_dim, n_q_heads / n_kv_heads) >
-      160 * 1024)
-    return VQ_ERR_UNSUPPORTED;
   (void)hipGetLastError();
+  return device_result(vqk::launch_attention(l, static_cast<hipStream_t>(stream)));
+}
+
+vq_status vq_attention_decode_static(const void *q, const uint8_t *k_codes,
+                                     const uint8_t *v_codes, const void *k_codebook,
+                                     const void *v_codebook, const float *k_scale,
+                                     const int32_t *kv_len, int32_t batch, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t head_dim, int32_t max_kv_len,
+                                     int32_t k_sub_dim, int32_t v_sub_dim, int32_t n_centroids,
+                                     vq_dtype dtype, int32_t window, float softmax_scale,
+                                     float *out, void *stream) {
+  vqk::AttnLayout l;
+  const vq_status st = check_attention(q, k_codes, v_codes, k_codebook, v_codebook, k_scale,
+                                       kv_len, batch, n_q_heads, n_kv_heads, head_dim, max_kv_len,
+                                       k_sub_dim, v_sub_dim, n_centroids, dtype, window,
+                                       softmax_scale, out, &l);
+  if (st != VQ_OK || batch == 0) return st;
+  if (vq_attention_workspace_bytes(batch, n_q_heads, head_dim, max_kv_len) >
+      VQ_ATTN_STATIC_SCRATCH_BYTES)
+    return VQ_ERR_TOO_LARGE;
+  void *scratch = nullptr;
+  (void)hipGetLastError();
+  const hipError_t e = vqk::attention_static_scratch(&scratch);
+  if (e != hipSuccess) return device_result(e);
+  l.workspace = static_cast<float *>(scratch);
   return device_result(vqk::launch_attention(l, static_cast<hipStream_t>(stream)));
 }
 
@@ -246,6 +290,8 @@ const char *vq_status_str(int32_t status) {
       return "unsupported sub_dim, dtype, n_centroids or packed group layout";
     case VQ_ERR_MISALIGNED: return "misaligned pointer";
     case VQ_ERR_DEVICE: return "HIP launch failed";
+    case VQ_ERR_TOO_LARGE:
+      return "the call needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }

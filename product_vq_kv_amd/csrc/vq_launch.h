@@ -94,5 +94,8 @@ hipError_t launch_kmeans(const void *x, void *codebook, const int32_t *group_map
 int attention_chunks(int max_kv_len);
 size_t attention_lds_bytes(int k_sub_dim, int v_sub_dim, int head_dim, int group);
 hipError_t launch_attention(const AttnLayout &l, hipStream_t stream);
+// Address of the static attention scratch (VQ_ATTN_STATIC_SCRATCH_BYTES) on
+// the current device, resolved once per device.
+hipError_t attention_static_scratch(void **ptr);
 
 }  // namespace vqk

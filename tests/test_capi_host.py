@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "vq.h")
 
 vq = pytest.importorskip("product_vq_kv_amd")
 
-OK, INVALID, UNSUPPORTED, MISALIGNED = 0, -1, -2, -3
+OK, INVALID, UNSUPPORTED, MISALIGNED, TOO_LARGE = 0, -1, -2, -3, -5
 FAKE = 0x10000  # aligned, never dereferenced by a rejected call
 
 
@@ -27,6 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == ["vq_abi_version", "vq_attention_decode",
+                                    "vq_attention_decode_static",
                                     "vq_attention_workspace_bytes", "vq_decode", "vq_encode",
                                     "vq_encode_packed", "vq_kmeans", "vq_kmeans_workspace_bytes",
                                     "vq_last_hip_error", "vq_status_str"]
@@ -39,8 +40,8 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert vq.lib.vq_abi_version() == 4
-    for code in (0, -1, -2, -3, -4, 99):
+    assert vq.lib.vq_abi_version() == 5
+    for code in (0, -1, -2, -3, -4, -5, 99):
         assert isinstance(vq.lib.vq_status_str(code), bytes)
     assert vq.lib.vq_status_str(-3) == b"misaligned pointer"
     assert vq.lib.vq_last_hip_error() == 0
@@ -202,6 +203,40 @@ def test_attention_workspace_size():
 ])
 def test_attention_rejects_on_host(over, code):
     assert attn(**over) == code
+
+
+def attn_static(**over):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, kcb=FAKE, vcb=FAKE, ks=None, kl=None, B=2, Hq=12, Hkv=4,
+             D=256, S=100, sdk=4, sdv=4, n_c=256, dt=0, window=0, scale=0.0625, out=FAKE,
+             stream=None)
+    a.update(over)
+    return vq.lib.vq_attention_decode_static(a["q"], a["kc"], a["vc"], a["kcb"], a["vcb"],
+                                             a["ks"], a["kl"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                             a["S"], a["sdk"], a["sdv"], a["n_c"], a["dt"],
+                                             a["window"], a["scale"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(sdk=2), UNSUPPORTED), (dict(n_c=257), UNSUPPORTED), (dict(Hq=13), INVALID),
+    (dict(B=-1), INVALID), (dict(scale=float("nan")), INVALID), (dict(q=None), INVALID),
+    (dict(kc=None), INVALID), (dict(q=FAKE + 1), MISALIGNED), (dict(out=FAKE + 2), MISALIGNED),
+    # partials beyond the static buffer: 1024 x 8 x 16 chunks x 258 floats
+    (dict(B=1024, Hq=8, Hkv=1, S=4096), TOO_LARGE),
+    (dict(B=64, Hq=32, Hkv=8, S=8192), TOO_LARGE),
+    (dict(B=0), OK), (dict(B=0, q=None, out=None), OK),
+])
+def test_attention_static_rejects_on_host(over, code):
+    assert attn_static(**over) == code
+
+
+def test_attention_static_limit_is_the_header_constant():
+    assert vq.ATTN_STATIC_SCRATCH_BYTES == 32 << 20
+    text = open(HEADER).read()
+    assert "#define VQ_ATTN_STATIC_SCRATCH_BYTES (32u << 20)" in text
+    # the largest Falcon3-7B decode batch at 4096 tokens that fits
+    need = vq.lib.vq_attention_workspace_bytes(160, 12, 256, 4096)
+    assert need <= vq.ATTN_STATIC_SCRATCH_BYTES < vq.lib.vq_attention_workspace_bytes(170, 12, 256,
+                                                                                     4096)
 
 
 def km(**over):

@@ -11,15 +11,30 @@ KV heads x head_dim 256, sub_dim 4 -> 1,048,576 sub-vectors, 256 centroids),
 with seeded per-channel-scaled Gaussian keys and outlier channels.  Inputs are
 resident in HBM before the timed region starts.
 
-Printed: one JSON line with sub-vectors/s over the timed region, the
-roofline position of the encode kernel (algorithmic fp32 flops,
-3*sub_dim*n_centroids per sub-vector, per launch divided by the launch's
-average duration measured with HIP events on the launch stream, against the
-MI355X fp32 vector peak) and the CPU oracle's rate on a bounded sample on the
-host (``cpu_baseline``).  Other workloads (``--config``) are for exploration.
+Printed: one JSON line.  Headline: sub-vectors/s over the timed region (W
+untimed warmup steps, then K steps between synchronisations) and the encode
+kernel's roofline position: algorithmic fp32 flops per launch divided by the
+launch's average duration (HIP events on the launch stream) against the
+MI355X fp32 vector peak.  The flops are those of the direct form, 3 * sub_dim
+* n_centroids per sub-vector (a subtraction, a multiply and an add per
+component per centroid).  The kernel does not execute them: it bounds the
+distances on the matrix cores and recomputes a few candidates exactly, so the
+figure is a direct-form-equivalent rate, which can exceed the vector peak on
+large codebooks.  What binds the kernel is read from rocprofv3 counters
+committed under profiles/ and reported next to it (``utilization``: VALU
+issue busy, matrix-core busy, shader clock), as is the HBM traffic.
 
-``--rows`` adds the steps adjacent to the encode, each timed the same way on
-its own synthetic workload and reported under ``"rows"`` in the same line:
+``cpu_baseline`` is the CPU oracle on the host: on all host threads (the
+headline baseline, ``cores`` = threads used) and on one core, with the CPU
+model.  Its all-thread run covers every row of the Falcon-shape workload and
+supplies the parity sample.
+
+``--configs`` adds the other encode workloads as rows (default all four):
+  config1  tiny: 2,048 sub-vectors, 256 centroids of sub_dim 8 (launch-bound)
+  config2  Llama-3.1-8B keys: 524,288 sub-vectors, sub_dim 8
+  config4  full batched cache: 33,554,432 sub-vectors, 256 codebook slots
+  config5  large codebook: 1,048,576 bf16 sub-vectors, 4,096 centroids
+``--rows`` adds the steps adjacent to the encode:
   fused  ``vq_encode_packed``: per-channel smoothing + 8-bit packed codes on
          the smoothed Falcon3-7B-shape cache.
   attention  ``vq_attention_decode``: one decode step of Falcon3-7B (32
@@ -29,7 +44,11 @@ its own synthetic workload and reported under ``"rows"`` in the same line:
   kmeans  ``vq_kmeans``: 5 Lloyd iterations per call on the Falcon3-7B keys
          (1,048,576 sub-vectors, 256 centroids, sub_dim 4); fp32 vector
          roofline on the assignment's algorithmic flops.
-``--only ROW`` runs just that row's leg (for profiling its kernel alone).
+Every row is timed after a short GPU warm-up: its launches are enqueued
+behind a short spin kernel, so the events measure the launches back to back
+(``kernel_ms_per_launch``) however fast the host enqueues; ``host_ms_per_call``
+is the wall time per call of the same loop.  ``--only ROW`` runs one row
+alone (for profiling its kernel).
 """
 from __future__ import annotations
 
@@ -43,16 +62,23 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X published fp32 vector peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X published fp32 vector peak (2.4 GHz)
+PEAK_CLOCK_GHZ = 2.4
 HBM_PEAK_GBS = 8000.0             # MI355X published HBM3E bandwidth
 # Pages' own figure for the same workload, on an Apple-Silicon GPU (context):
 # 1,048,576 sub-vectors in 7.98 ms (post's "The Numbers" throughput table).
 PAGES_FALCON_SUBVEC_PER_S = 1048576 / 7.98e-3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_falcon3_traffic.txt")
-FUSED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_fused_falcon3_traffic.txt")
-ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_falcon3_decode_traffic.txt")
 KMEANS_ITERATIONS = 5
 KERNEL_SOURCES = os.path.join(ROOT, "product_vq_kv_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+# profile summary name of each encode workload
+CONFIG_TAGS = {1: "encode_tiny", 2: "encode_llama8b", 3: "encode_falcon3", 4: "encode_full_cache",
+               5: "encode_large_codebook"}
+ROW_TAGS = {"fused": "encode_fused_falcon3", "attention": "attention_falcon3_decode",
+            "kmeans": "kmeans_falcon3"}
+# rows of each config the oracle checks in the bench (the tests check all)
+PARITY_ROWS = {1: 2048, 2: 1 << 18, 4: 1 << 18, 5: 1 << 14}
 
 
 def log(msg: str) -> None:
@@ -63,6 +89,7 @@ def log(msg: str) -> None:
 # valid while these files are unchanged.
 ENCODE_SOURCES = ("vq_encode_mfma.hip", "vq_codes.h")
 ATTENTION_SOURCES = ("vq_attention.hip",)
+KMEANS_SOURCES = ("vq_encode_mfma.hip", "vq_codes.h", "vq_kmeans.hip")
 
 
 def kernel_source_hash(names=ENCODE_SOURCES) -> str:
@@ -75,10 +102,9 @@ def kernel_source_hash(names=ENCODE_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_bytes_per_launch(path: str = TRAFFIC_FILE):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when there is none or the kernel's sources changed since it was
-    taken."""
+def _summary_json(path: str):
+    """The JSON line of a committed counter summary, or None when there is
+    none or the kernel's sources changed since it was taken."""
     try:
         with open(path) as f:
             rows = [ln for ln in f if ln.strip() and not ln.startswith("#")]
@@ -88,20 +114,72 @@ def traffic_bytes_per_launch(path: str = TRAFFIC_FILE):
         return None
     if t.get("kernel_source_sha256_16") != kernel_source_hash(names):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
 
 
-def cpu_baseline(wl, sample_rows: int):
+def traffic_bytes_per_launch(tag: str):
+    """HBM bytes per launch from profiles/<tag>_traffic.txt (None if stale)."""
+    t = _summary_json(os.path.join(PROFILES, f"{tag}_traffic.txt"))
+    return None if t is None else t.get("hbm_bytes_per_launch")
+
+
+def utilization(tag: str):
+    """Counter-derived busy fractions and shader clock from
+    profiles/<tag>_counters.txt (None if stale)."""
+    t = _summary_json(os.path.join(PROFILES, f"{tag}_counters.txt"))
+    if t is None:
+        return None
+    keep = ("valu_busy", "mfma_busy", "sclk_ghz", "valu_insts_per_wave", "lds_bank_conflict_frac")
+    out = {k: t[k] for k in keep if k in t}
+    out["source"] = f"profiles/{tag}_counters.txt"
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """Threads the host grants this process (the GPU machine sets OMP_NUM_THREADS
+    to its CPU share)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(wl, rows_one: int, rows_all: int):
+    """The oracle on one core and on all host threads (same single-threaded C
+    routine per slice; results do not depend on the slicing).  Returns the
+    all-thread indices and the baseline object."""
     import numpy as np
     import oracle
-    rows = min(sample_rows, wl.n)
-    xs = np.ascontiguousarray(wl.x[:rows])
+    threads = host_threads()
+    rows_one = min(rows_one, wl.n)
+    rows_all = min(rows_all, wl.n)
     t0 = time.perf_counter()
-    idx = oracle.encode(xs, wl.codebook, wl.sub_dim, wl.n_centroids, wl.dtype, threads=1)
-    dt = time.perf_counter() - t0
-    return idx, dict(value=rows / dt, unit="sub-vectors/s", cores=1, kind="oracle",
-                     sample=f"first {rows} of {wl.n} sub-vectors of the same workload, "
-                            f"one thread, {dt:.1f} s")
+    oracle.encode(np.ascontiguousarray(wl.x[:rows_one]), wl.codebook, wl.sub_dim,
+                  wl.n_centroids, wl.dtype, threads=1)
+    dt1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    idx = oracle.encode(np.ascontiguousarray(wl.x[:rows_all]), wl.codebook, wl.sub_dim,
+                        wl.n_centroids, wl.dtype, threads=threads)
+    dta = time.perf_counter() - t0
+    model = cpu_model()
+    return idx, dict(
+        value=rows_all / dta, unit="sub-vectors/s", cores=threads, kind="oracle",
+        sample=f"first {rows_all} of {wl.n} sub-vectors of the same workload, {threads} threads "
+               f"slicing the rows, {dta:.1f} s",
+        cpu_model=model, host_cpus_visible=len(os.sched_getaffinity(0)),
+        one_core=dict(value=rows_one / dt1, unit="sub-vectors/s", cores=1,
+                      sample=f"first {rows_one} sub-vectors, one thread, {dt1:.1f} s"))
 
 
 def copy_calibration(torch, dev) -> None:
@@ -114,22 +192,88 @@ def copy_calibration(torch, dev) -> None:
     log("copy calibration: 5 x 268435456-byte device copies")
 
 
-def time_launches(fn, steps: int, warmup: int, stream):
-    """(wall seconds per call, event seconds per call) over `steps` calls."""
+def time_row(fn, steps: int, stream, warm_s: float = 0.05):
+    """(host seconds per call, GPU seconds per launch) over `steps` calls.
+
+    A warm-up of `warm_s` seconds of calls first (the shader clock drops
+    while the GPU idles, e.g. during the CPU baseline).  The timed launches
+    are enqueued behind a spin kernel, so the events bracket them back to
+    back even when the host enqueues more slowly than the GPU runs them."""
     import torch
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
         fn()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
+    # long enough for the host to enqueue every launch first (~25 us per call)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(2.0e9 * max(0.01, 25e-6 * steps)))
     e0.record(stream)
+    t0 = time.perf_counter()
     for _ in range(steps):
         fn()
+    host = (time.perf_counter() - t0) / steps
     e1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return wall / steps, e0.elapsed_time(e1) / 1e3 / steps
+    return host, e0.elapsed_time(e1) / 1e3 / steps
+
+
+def encode_roofline(wl, launch_s: float, tag: str):
+    flops = 3.0 * wl.sub_dim * wl.n_centroids * wl.n
+    achieved = flops / launch_s / 1e12
+    return {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
+            "traffic": traffic_bytes_per_launch(tag)}
+
+
+def encode_bytes(wl) -> float:
+    """Algorithmic HBM bytes of one encode launch: keys, indices, codebooks."""
+    return wl.n * (2 * wl.sub_dim + 4) + wl.n_codebooks * wl.n_centroids * wl.sub_dim * 2
+
+
+def leg_config(cfg: int):
+    def leg(args, dev, stream):
+        import numpy as np
+        import torch
+        import workloads as W
+        import product_vq_kv_amd as vq
+        from tests import parity
+        wl = W.config(cfg)
+        log(f"row config{cfg}: {wl.name} (n={wl.n})")
+        tdt = torch.float16 if wl.dtype == W.F16 else torch.bfloat16
+        x = torch.from_numpy(wl.x.view(np.int16)).view(tdt).to(dev)
+        cb = torch.from_numpy(wl.codebook.view(np.int16)).view(tdt).to(dev)
+        out = torch.empty(wl.n, dtype=torch.uint32, device=dev)
+        call = (x.data_ptr(), cb.data_ptr(), wl.n, wl.sub_dim, wl.n_centroids, wl.dtype,
+                wl.codebook_stride, wl.n_codebooks, wl.group_len, None, out.data_ptr(),
+                stream.cuda_stream)
+        steps = max(args.steps, 20)
+        host, launch_s = time_row(lambda: vq.encode_raw(*call), steps, stream)
+        parity_sample = None
+        if args.cpu_sample > 0:
+            got = out.cpu().numpy().view(np.uint32)
+            k = min(PARITY_ROWS.get(cfg, 1 << 16), wl.n)
+            rows = np.sort(np.random.default_rng(cfg).choice(wl.n, size=k, replace=False))
+            ref = parity.oracle_indices(wl, rows, threads=host_threads())
+            parity_sample = dict(rows=int(k), equal=int(np.sum(ref == got[rows])),
+                                 threads=host_threads())
+        tag = CONFIG_TAGS[cfg]
+        gbs = encode_bytes(wl) / launch_s / 1e9
+        return {
+            "workload": wl.name,
+            "value": wl.n / launch_s,
+            "unit": "sub-vectors/s",
+            "kernel_ms_per_launch": launch_s * 1e3,
+            "host_ms_per_call": host * 1e3,
+            "launches": steps,
+            "roofline": encode_roofline(wl, launch_s, tag),
+            "utilization": utilization(tag),
+            "algorithmic_gb_per_s": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS,
+            "parity_sample": parity_sample,
+        }
+    return leg
 
 
 def leg_fused(args, dev, stream):
@@ -148,8 +292,8 @@ def leg_fused(args, dev, stream):
     call = (x.data_ptr(), cb.data_ptr(), wl.n, wl.sub_dim, wl.n_centroids, wl.dtype,
             wl.codebook_stride, wl.n_codebooks, wl.group_len, None, sc.data_ptr(), wl.head_dim,
             0, bits, out.data_ptr(), stream.cuda_stream)
-    wall, launch_s = time_launches(lambda: vq.encode_packed_raw(*call), args.steps, args.warmup,
-                                   stream)
+    steps = max(args.steps, 20)
+    host, launch_s = time_row(lambda: vq.encode_packed_raw(*call), steps, stream)
     flops = 3.0 * wl.sub_dim * wl.n_centroids * wl.n
     algo_bytes = wl.n * (2 * wl.sub_dim + bits / 8) + wl.n_centroids * wl.sub_dim * 2 + wl.head_dim * 4
     achieved = flops / launch_s / 1e12
@@ -158,54 +302,67 @@ def leg_fused(args, dev, stream):
         import oracle
         rows = min(args.cpu_sample // 4, wl.n)
         ref = oracle.encode_packed(wl.x[:rows], wl.codebook, wl.sub_dim, wl.n_centroids, wl.dtype,
-                                   code_bits=bits, **wl.packed_kwargs())
+                                   code_bits=bits, threads=host_threads(), **wl.packed_kwargs())
         got = out.cpu().numpy()[:ref.size]
         parity = dict(rows=int(rows), equal=int(np.sum(ref == got)))
+    tag = ROW_TAGS["fused"]
     return {
         "workload": wl.name + ", 8-bit codes",
-        "value": wl.n / wall,
+        "value": wl.n / launch_s,
         "unit": "sub-vectors/s",
         "kernel_ms_per_launch": launch_s * 1e3,
+        "host_ms_per_call": host * 1e3,
+        "launches": steps,
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
-                     "traffic": traffic_bytes_per_launch(FUSED_TRAFFIC_FILE)},
+                     "traffic": traffic_bytes_per_launch(tag)},
+        "utilization": utilization(tag),
         "algorithmic_gb_per_s": algo_bytes / launch_s / 1e9,
         "parity_sample": parity,
     }
 
 
-def leg_attention(args, dev, stream):
-    """One decode-attention step over the VQ-coded Falcon3-7B cache."""
+def attention_call(wl, dev, stream):
+    """Device buffers and the C-ABI argument tuple of one decode-attention call."""
     import numpy as np
     import torch
     import workloads as W
     import product_vq_kv_amd as vq
-    wl = W.falcon_decode_attention()
-    log(f"row attention: {wl.name}")
     B, Hq, Hkv, D, S = wl.shape
 
     def bits(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.float16).to(dev)
 
-    q, kcb, vcb = bits(wl.q), bits(wl.k_codebook), bits(wl.v_codebook)
-    kc = torch.from_numpy(wl.k_codes).to(dev)
-    vc = torch.from_numpy(wl.v_codes).to(dev)
-    ks = torch.from_numpy(wl.k_scale).to(dev)
-    kl = torch.from_numpy(wl.kv_len).to(dev)
-    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    keep = dict(q=bits(wl.q), kcb=bits(wl.k_codebook), vcb=bits(wl.v_codebook),
+                kc=torch.from_numpy(wl.k_codes).to(dev), vc=torch.from_numpy(wl.v_codes).to(dev),
+                ks=torch.from_numpy(wl.k_scale).to(dev), kl=torch.from_numpy(wl.kv_len).to(dev),
+                out=torch.empty((B, Hq, D), dtype=torch.float32, device=dev))
     wsb = vq.attention_workspace_bytes(B, Hq, D, S)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    keep["ws"] = torch.empty(wsb, dtype=torch.uint8, device=dev)
     sdk, sdv = D // wl.k_codes.shape[3], D // wl.v_codes.shape[3]
     n_c = wl.k_codebook.shape[1]
-    scale = 1.0 / D ** 0.5
-    call = (q.data_ptr(), kc.data_ptr(), vc.data_ptr(), kcb.data_ptr(), vcb.data_ptr(),
-            ks.data_ptr(), kl.data_ptr(), B, Hq, Hkv, D, S, sdk, sdv, n_c, W.F16, 0, scale,
-            out.data_ptr(), ws.data_ptr(), wsb, stream.cuda_stream)
-    wall, launch_s = time_launches(lambda: vq.attention_decode_raw(*call), args.steps,
-                                   args.warmup, stream)
+    call = (keep["q"].data_ptr(), keep["kc"].data_ptr(), keep["vc"].data_ptr(),
+            keep["kcb"].data_ptr(), keep["vcb"].data_ptr(), keep["ks"].data_ptr(),
+            keep["kl"].data_ptr(), B, Hq, Hkv, D, S, sdk, sdv, n_c, W.F16, 0, 1.0 / D ** 0.5,
+            keep["out"].data_ptr(), keep["ws"].data_ptr(), wsb, stream.cuda_stream)
     toks = int(np.sum(wl.kv_len)) * Hkv
     algo_bytes = (toks * (D // sdk + D // sdv) + B * Hq * D * (2 + 4)
                   + Hkv * n_c * (sdk + sdv) * 2 + Hkv * D * 4)
+    return keep, call, algo_bytes
+
+
+def leg_attention(args, dev, stream):
+    """One decode-attention step over the VQ-coded Falcon3-7B cache, plus the
+    same step at 64 and 128 sequences (the rate as the batch grows)."""
+    import numpy as np
+    import workloads as W
+    import product_vq_kv_amd as vq
+    wl = W.falcon_decode_attention()
+    log(f"row attention: {wl.name}")
+    B, Hq, Hkv, D, S = wl.shape
+    keep, call, algo_bytes = attention_call(wl, dev, stream)
+    steps = max(args.steps, 20)
+    host, launch_s = time_row(lambda: vq.attention_decode_raw(*call), steps, stream)
     achieved = algo_bytes / launch_s / 1e9
     parity = None
     if args.cpu_sample > 0:
@@ -214,20 +371,31 @@ def leg_attention(args, dev, stream):
         ref = A.decode_attention(wl.q[:nb], wl.k_codes[:nb], wl.v_codes[:nb], wl.k_codebook,
                                  wl.v_codebook, wl.dtype, k_scale=wl.k_scale,
                                  kv_len=wl.kv_len[:nb])
-        got = out.cpu().numpy()[:nb].astype(np.float64)
+        got = keep["out"].cpu().numpy()[:nb].astype(np.float64)
         parity = dict(sequences=nb, max_abs_err=float(np.max(np.abs(got - ref))),
                       max_abs_ref=float(np.max(np.abs(ref))))
+    batches = {}
+    for nb in (64, 128):
+        wlb = W.falcon_decode_attention(B=nb)
+        _, callb, bytes_b = attention_call(wlb, dev, stream)
+        _, ls = time_row(lambda: vq.attention_decode_raw(*callb), steps, stream, warm_s=0.02)
+        batches[str(nb)] = dict(kernel_ms_per_launch=ls * 1e3,
+                                algorithmic_gb_per_s=bytes_b / ls / 1e9,
+                                frac=bytes_b / ls / 1e9 / HBM_PEAK_GBS)
+    tag = ROW_TAGS["attention"]
     return {
         "workload": wl.name,
-        "value": B / wall,
+        "value": B / launch_s,
         "unit": "decode steps (sequences) / s",
-        "ms_per_call": wall * 1e3,
         "kernel_ms_per_launch": launch_s * 1e3,
+        "host_ms_per_call": host * 1e3,
+        "launches": steps,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_bytes_per_launch(ATTN_TRAFFIC_FILE)},
+                     "traffic": traffic_bytes_per_launch(tag)},
         "algorithmic_bytes_per_launch": algo_bytes,
         "tokens_attended_per_launch": int(np.sum(wl.kv_len)) * Hq,
+        "by_batch": batches,
         "parity_sample": parity,
     }
 
@@ -249,9 +417,8 @@ def leg_kmeans(args, dev, stream):
     call = (x.data_ptr(), cb.data_ptr(), wl.n, wl.sub_dim, wl.n_centroids, wl.dtype,
             wl.codebook_stride, 1, wl.group_len, None, KMEANS_ITERATIONS, idx.data_ptr(),
             ws.data_ptr(), wsb, stream.cuda_stream)
-    steps = max(1, args.steps // 10)
-    wall, launch_s = time_launches(lambda: vq.kmeans_raw(*call), steps, min(args.warmup, 3),
-                                   stream)
+    steps = max(args.steps, 20)
+    host, launch_s = time_row(lambda: vq.kmeans_raw(*call), steps, stream)
     it_s = launch_s / KMEANS_ITERATIONS
     flops = 3.0 * wl.sub_dim * wl.n_centroids * wl.n
     achieved = flops / it_s / 1e12
@@ -263,26 +430,30 @@ def leg_kmeans(args, dev, stream):
         vq.kmeans_raw(*call)
         torch.cuda.synchronize()
         want_cb, want_idx, _ = K.kmeans(wl.x, wl.codebook, wl.sub_dim, wl.n_centroids,
-                                        KMEANS_ITERATIONS, threads=16)
+                                        KMEANS_ITERATIONS, threads=host_threads())
         got_cb = cb.cpu().numpy().view(np.uint16)
         parity = dict(iterations=KMEANS_ITERATIONS,
                       codebook_equal=int(np.sum(got_cb == want_cb)), codebook_size=int(want_cb.size),
                       assignment_equal=int(np.sum(idx.cpu().numpy().view(np.uint32) == want_idx)),
                       rows=int(wl.n))
+    tag = ROW_TAGS["kmeans"]
     return {
         "workload": wl.name + f", Lloyd x{KMEANS_ITERATIONS} per call",
-        "value": wl.n * KMEANS_ITERATIONS / wall,
+        "value": wl.n * KMEANS_ITERATIONS / launch_s,
         "unit": "sub-vector-iterations/s",
-        "ms_per_call": wall * 1e3,
+        "kernel_ms_per_launch": launch_s * 1e3,
+        "host_ms_per_call": host * 1e3,
         "ms_per_iteration": it_s * 1e3,
+        "launches": steps,
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
-                     "traffic": None},
+                     "traffic": traffic_bytes_per_launch(tag)},
         "parity_sample": parity,
     }
 
 
 ROW_LEGS = {"fused": leg_fused, "attention": leg_attention, "kmeans": leg_kmeans}
+ROW_LEGS.update({f"config{c}": leg_config(c) for c in (1, 2, 4, 5)})
 
 
 def main() -> int:
@@ -292,9 +463,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-sample", type=int, default=1 << 19,
-                    help="rows the CPU oracle encodes for cpu_baseline (0 = skip)")
+                    help="rows the CPU oracle encodes on one core (0 = no CPU work at all)")
+    ap.add_argument("--cpu-sample-all", type=int, default=1 << 22,
+                    help="rows the CPU oracle encodes on all host threads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter scaling)")
+    ap.add_argument("--configs", default="config1,config2,config4,config5",
+                    help="comma-separated encode workloads to add as rows ('' = none)")
     ap.add_argument("--rows", default="fused,attention,kmeans",
                     help="comma-separated adjacent rows to time after the headline ('' = none)")
     ap.add_argument("--only", choices=sorted(ROW_LEGS), default=None,
@@ -360,23 +535,24 @@ def main() -> int:
 
     ms_per_step = wall * 1e3 / args.steps
     launch_s = gpu_ms / 1e3 / args.steps
-    flops = 3.0 * wl.sub_dim * wl.n_centroids * wl.n
-    algo_bytes = wl.n * (2 * wl.sub_dim + 4) + wl.n_codebooks * wl.n_centroids * wl.sub_dim * 2
-    achieved = flops / launch_s / 1e12
+    algo_bytes = encode_bytes(wl)
     value = wl.n / (ms_per_step / 1e3)
+    tag = CONFIG_TAGS[args.config]
 
     gpu_idx = out.cpu().numpy().view(np.uint32)
     cpu = None
     parity_sample = None
     if args.cpu_sample > 0:
-        log(f"cpu baseline: oracle on {min(args.cpu_sample, wl.n)} rows, one thread")
-        ref, cpu = cpu_baseline(wl, args.cpu_sample)
+        log(f"cpu baseline: oracle on {min(args.cpu_sample, wl.n)} rows on one core, "
+            f"{min(args.cpu_sample_all, wl.n)} rows on {host_threads()} threads")
+        ref, cpu = cpu_baseline(wl, args.cpu_sample, args.cpu_sample_all)
         parity_sample = dict(rows=int(ref.size), equal=int(np.sum(ref == gpu_idx[:ref.size])))
 
     cfg = dict(workload=wl.name, n_subvectors=wl.n, sub_dim=wl.sub_dim,
                n_centroids=wl.n_centroids, element="fp16" if wl.dtype == W.F16 else "bf16",
                n_codebooks=wl.n_codebooks, **{k: v for k, v in wl.meta.items()
                                                if isinstance(v, (int, float, str))})
+    util = utilization(tag)
     line = {
         "metric": "sub-vectors encoded/sec and % fp32 VALU peak (Falcon3-7B shape, 1 GPU)",
         "value": value,
@@ -391,22 +567,25 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic (seeded; per-channel LogNormal-scaled Gaussian keys, outlier channels)",
         "config": cfg,
-        "roofline": {
-            "bound": "alu",
-            "achieved": achieved,
-            "peak": FP32_VECTOR_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
-            "traffic": traffic_bytes_per_launch() if args.config == 3 else None,
-        },
+        "roofline": encode_roofline(wl, launch_s, tag),
+        "roofline_note": ("achieved = direct-form-equivalent fp32 flops (3 * sub_dim * "
+                          "n_centroids per sub-vector) / kernel time; the kernel executes a "
+                          "matrix-core bound plus an exact recompute of few candidates, and "
+                          "what binds it is in 'utilization'"),
+        "utilization": util,
         "cpu_baseline": cpu,
+        "vs_cpu_oracle": (value / cpu["value"]) if cpu else None,
         "kernel_ms_per_launch": launch_s * 1e3,
         "algorithmic_gb_per_s": algo_bytes / launch_s / 1e9,
         "hbm_frac": algo_bytes / launch_s / 1e9 / HBM_PEAK_GBS,
         "parity_sample": parity_sample,
-        "vs_baseline_note": "pages' Apple-Silicon Metal kernel on the same shape (context only)",
+        "vs_baseline_note": ("pages' Apple-Silicon Metal kernel on the same shape, 1,048,576 "
+                             "sub-vectors in 7.98 ms (context only, another machine)"),
     }
-    rows = [r for r in args.rows.split(",") if r]
+    if util and util.get("sclk_ghz"):
+        line["roofline"]["peak_at_measured_clock"] = (FP32_VECTOR_PEAK_TFLOPS * util["sclk_ghz"]
+                                                      / PEAK_CLOCK_GHZ)
+    rows = [r for r in (args.configs.split(",") + args.rows.split(",")) if r]
     if rows:
         line["rows"] = {}
         for r in rows:

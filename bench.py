@@ -123,14 +123,20 @@ def traffic_bytes_per_launch(tag: str):
     return None if t is None else t.get("hbm_bytes_per_launch")
 
 
-def utilization(tag: str):
-    """Counter-derived busy fractions and shader clock from
-    profiles/<tag>_counters.txt (None if stale)."""
+def utilization(tag: str, launch_s: float):
+    """Counter-derived busy fractions from profiles/<tag>_counters.txt (None
+    if stale), and the shader clock of this run: the busy shader cycles per
+    launch the counters measured (the kernel is compute-bound, so its cycle
+    count does not depend on the clock) over the launch time measured here."""
     t = _summary_json(os.path.join(PROFILES, f"{tag}_counters.txt"))
     if t is None:
         return None
-    keep = ("valu_busy", "mfma_busy", "sclk_ghz", "valu_insts_per_wave", "lds_bank_conflict_frac")
+    keep = ("valu_busy", "mfma_busy", "valu_insts_per_wave", "lds_conflict_cycles_per_inst",
+            "busy_cycles_per_launch")
     out = {k: t[k] for k in keep if k in t}
+    if t.get("busy_cycles_per_launch"):
+        out["sclk_ghz"] = t["busy_cycles_per_launch"] / launch_s / 1e9
+        out["peak_tflops_at_sclk"] = FP32_VECTOR_PEAK_TFLOPS * out["sclk_ghz"] / PEAK_CLOCK_GHZ
     out["source"] = f"profiles/{tag}_counters.txt"
     return out
 
@@ -268,7 +274,7 @@ def leg_config(cfg: int):
             "host_ms_per_call": host * 1e3,
             "launches": steps,
             "roofline": encode_roofline(wl, launch_s, tag),
-            "utilization": utilization(tag),
+            "utilization": utilization(tag, launch_s),
             "algorithmic_gb_per_s": gbs,
             "hbm_frac": gbs / HBM_PEAK_GBS,
             "parity_sample": parity_sample,
@@ -316,7 +322,7 @@ def leg_fused(args, dev, stream):
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
                      "traffic": traffic_bytes_per_launch(tag)},
-        "utilization": utilization(tag),
+        "utilization": utilization(tag, launch_s),
         "algorithmic_gb_per_s": algo_bytes / launch_s / 1e9,
         "parity_sample": parity,
     }
@@ -375,7 +381,7 @@ def leg_attention(args, dev, stream):
         parity = dict(sequences=nb, max_abs_err=float(np.max(np.abs(got - ref))),
                       max_abs_ref=float(np.max(np.abs(ref))))
     batches = {}
-    for nb in (64, 128):
+    for nb in [int(b) for b in args.attention_batches.split(",") if b]:
         wlb = W.falcon_decode_attention(B=nb)
         _, callb, bytes_b = attention_call(wlb, dev, stream)
         _, ls = time_row(lambda: vq.attention_decode_raw(*callb), steps, stream, warm_s=0.02)
@@ -472,6 +478,8 @@ def main() -> int:
                     help="comma-separated encode workloads to add as rows ('' = none)")
     ap.add_argument("--rows", default="fused,attention,kmeans",
                     help="comma-separated adjacent rows to time after the headline ('' = none)")
+    ap.add_argument("--attention-batches", default="64,128",
+                    help="extra sequence counts the attention row is timed at ('' = none)")
     ap.add_argument("--only", choices=sorted(ROW_LEGS), default=None,
                     help="run only this row's leg and print its object")
     args = ap.parse_args()
@@ -552,7 +560,7 @@ def main() -> int:
                n_centroids=wl.n_centroids, element="fp16" if wl.dtype == W.F16 else "bf16",
                n_codebooks=wl.n_codebooks, **{k: v for k, v in wl.meta.items()
                                                if isinstance(v, (int, float, str))})
-    util = utilization(tag)
+    util = utilization(tag, launch_s)
     line = {
         "metric": "sub-vectors encoded/sec and % fp32 VALU peak (Falcon3-7B shape, 1 GPU)",
         "value": value,
@@ -582,9 +590,6 @@ def main() -> int:
         "vs_baseline_note": ("pages' Apple-Silicon Metal kernel on the same shape, 1,048,576 "
                              "sub-vectors in 7.98 ms (context only, another machine)"),
     }
-    if util and util.get("sclk_ghz"):
-        line["roofline"]["peak_at_measured_clock"] = (FP32_VECTOR_PEAK_TFLOPS * util["sclk_ghz"]
-                                                      / PEAK_CLOCK_GHZ)
     rows = [r for r in (args.configs.split(",") + args.rows.split(",")) if r]
     if rows:
         line["rows"] = {}

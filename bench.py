@@ -418,7 +418,7 @@ def leg_kmeans(args, dev, stream):
     cb0 = torch.from_numpy(wl.codebook.view(np.int16)).view(torch.float16).to(dev)
     cb = cb0.clone()
     idx = torch.empty(wl.n, dtype=torch.uint32, device=dev)
-    wsb = vq.kmeans_workspace_bytes(wl.sub_dim, wl.n_centroids, 1)
+    wsb = vq.kmeans_workspace_bytes(wl.sub_dim, wl.n_centroids, 1, wl.dtype)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     call = (x.data_ptr(), cb.data_ptr(), wl.n, wl.sub_dim, wl.n_centroids, wl.dtype,
             wl.codebook_stride, 1, wl.group_len, None, KMEANS_ITERATIONS, idx.data_ptr(),

@@ -74,7 +74,7 @@ typedef enum {
 #define VQ_ATTN_MAX_GROUP 8
 #define VQ_KMEANS_MAX_SLOT_ROWS (1 << 23)
 #define VQ_ATTN_STATIC_SCRATCH_BYTES (32u << 20)
-#define VQ_ABI_VERSION 5
+#define VQ_ABI_VERSION 6
 
 /*
  * vq_encode -- nearest-centroid index of every sub-vector.
@@ -160,14 +160,18 @@ vq_status vq_encode_packed(const void *x, const void *codebook, int64_t n, int32
  * trained on the sub-vectors of the groups mapped to it:
  *     assignment: out_idx = vq_encode of every sub-vector (same arithmetic)
  *     update:     every centroid with members becomes the exact mean of its
- *                 members rounded once to fp16 (to nearest, ties to even);
- *                 a centroid without members keeps its value.
- * The codebook is updated in place; out_idx holds the assignment of the last
- * iteration (made against the codebook before its last update).  Results
- * are deterministic and identical to the CPU oracle's.
+ *                 members rounded once to the element type (to nearest,
+ *                 ties to even); a centroid without members keeps its value.
+ * Exact means: every finite fp16 value is an integer multiple of 2^-24 and
+ * every finite bf16 value one of 2^-133, so member sums are exact integers
+ * (int64 for fp16, 9 limbs of 32 bits for bf16) and the mean is rounded once,
+ * in integer arithmetic.  A non-finite component adds 0 to its sum (its row
+ * still counts as a member).  The codebook is updated in place; out_idx holds
+ * the assignment of the last iteration (made against the codebook before its
+ * last update).  Results are deterministic and identical to the CPU oracle's.
  *
- *   x, n, sub_dim, n_centroids, codebook_stride, n_codebooks, group_len,
- *   group_map   as for vq_encode; dtype must be VQ_F16; x must be finite.
+ *   x, n, sub_dim, n_centroids, dtype, codebook_stride, n_codebooks,
+ *   group_len, group_map   as for vq_encode.
  *   codebook    device, read and written.
  *   iterations  >= 0 (0: nothing is done).
  *   out_idx     device uint32 [n], 4-aligned.
@@ -176,9 +180,11 @@ vq_status vq_encode_packed(const void *x, const void *codebook, int64_t n, int32
  *               not matter.  Calls sharing a workspace must be ordered.
  * A slot may receive at most VQ_KMEANS_MAX_SLOT_ROWS sub-vectors (n with a
  * group_map, else min(group_len, n)), else VQ_ERR_UNSUPPORTED: the exact
- * member sums are 64-bit integers.
+ * member sums and their limbs are 64-bit integers.
+ * vq_kmeans_workspace_bytes returns 0 for arguments vq_kmeans rejects.
  */
-size_t vq_kmeans_workspace_bytes(int32_t sub_dim, int32_t n_centroids, int64_t n_codebooks);
+size_t vq_kmeans_workspace_bytes(int32_t sub_dim, int32_t n_centroids, int64_t n_codebooks,
+                                 vq_dtype dtype);
 
 vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
                     int32_t n_centroids, vq_dtype dtype, int64_t codebook_stride,

@@ -67,7 +67,7 @@ lib.vq_attention_decode_static.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i3
                                            _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
                                            _p, _p]
 lib.vq_attention_decode_static.restype = _i32
-lib.vq_kmeans_workspace_bytes.argtypes = [_i32, _i32, _i64]
+lib.vq_kmeans_workspace_bytes.argtypes = [_i32, _i32, _i64, _i32]
 lib.vq_kmeans_workspace_bytes.restype = ctypes.c_size_t
 lib.vq_kmeans.argtypes = [_p, _p, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _p, _i32, _p, _p,
                           ctypes.c_size_t, _p]
@@ -393,8 +393,9 @@ def attention_decode(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tens
     return out
 
 
-def kmeans_workspace_bytes(sub_dim: int, n_centroids: int, n_codebooks: int = 1) -> int:
-    return int(lib.vq_kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks))
+def kmeans_workspace_bytes(sub_dim: int, n_centroids: int, n_codebooks: int = 1,
+                           dtype: int = F16) -> int:
+    return int(lib.vq_kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks, dtype))
 
 
 def kmeans_raw(x_ptr, codebook_ptr, n, sub_dim, n_centroids, dtype, codebook_stride, n_codebooks,
@@ -409,7 +410,7 @@ def kmeans(x: torch.Tensor, codebook: torch.Tensor, iterations: int, *,
            group_len: Optional[int] = None, group_map: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            stream=None) -> torch.Tensor:
-    """Lloyd K-means on the device: `codebook` (fp16, [n_c, sd] or
+    """Lloyd K-means on the device: `codebook` (fp16 or bf16, [n_c, sd] or
     [slots, n_c, sd]) is updated in place; returns the last assignment
     (uint32 [N])."""
     dt, k, n_c, sd, stride, n = _keys(x, codebook)
@@ -420,7 +421,7 @@ def kmeans(x: torch.Tensor, codebook: torch.Tensor, iterations: int, *,
         out = torch.empty(n, dtype=torch.uint32, device=x.device)
     elif out.dtype != torch.uint32 or out.numel() != n or not out.is_contiguous():
         raise ValueError("out must be a contiguous uint32 tensor with one entry per sub-vector")
-    need = kmeans_workspace_bytes(sd, n_c, k)
+    need = kmeans_workspace_bytes(sd, n_c, k, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=x.device)
     elif workspace.numel() * workspace.element_size() < need:

@@ -190,11 +190,12 @@ vq_status vq_decode(const uint32_t *idx, const void *codebook, int64_t n, int32_
       vqk::launch_decode(idx, codebook, group_map, out_x, l, static_cast<hipStream_t>(stream)));
 }
 
-size_t vq_kmeans_workspace_bytes(int32_t sub_dim, int32_t n_centroids, int64_t n_codebooks) {
+size_t vq_kmeans_workspace_bytes(int32_t sub_dim, int32_t n_centroids, int64_t n_codebooks,
+                                 vq_dtype dtype) {
   if ((sub_dim != 4 && sub_dim != 8) || n_centroids < 1 || n_centroids > VQ_MAX_CENTROIDS ||
-      n_codebooks < 1)
+      n_codebooks < 1 || (dtype != VQ_F16 && dtype != VQ_BF16))
     return 0;
-  return vqk::kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks);
+  return vqk::kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks, dtype == VQ_BF16);
 }
 
 vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
@@ -206,21 +207,24 @@ vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
   vq_status st = check_common(codebook, n, sub_dim, n_centroids, dtype, codebook_stride,
                               n_codebooks, group_len, group_map, &l);
   if (st != VQ_OK) return st;
-  if (dtype != VQ_F16) return VQ_ERR_UNSUPPORTED;  // exact sums need fp16's fixed grid
   if (iterations < 0) return VQ_ERR_INVALID_ARG;
-  // exact int64 member sums: at most 2^23 members of +-65504 per slot
+  // exact int64 member sums (fp16) and limbs (bf16): at most 2^23 members per slot
   const int64_t per_slot = group_map ? n : (group_len < n ? group_len : n);
   if (per_slot > (int64_t(1) << 23)) return VQ_ERR_UNSUPPORTED;
   if (n == 0 || iterations == 0) return VQ_OK;
   if (!x || !out_idx || !workspace) return VQ_ERR_INVALID_ARG;
-  if (workspace_bytes < vqk::kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks))
+  if (workspace_bytes <
+      vqk::kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks, dtype == VQ_BF16))
     return VQ_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(x) % (2 * sub_dim) != 0 ||
       reinterpret_cast<uintptr_t>(out_idx) % 4 != 0 ||
       reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
     return VQ_ERR_MISALIGNED;
   if (vqk::encode_grid(l) > kMaxGrid || vqk::encode_mfma_grid(l) > kMaxGrid ||
-      vqk::kmeans_grid(l) > kMaxGrid || n_codebooks * n_centroids * sub_dim / 32 + 1 > kMaxGrid)
+      vqk::kmeans_grid(l) > kMaxGrid || n_codebooks * n_centroids * sub_dim / 32 + 1 > kMaxGrid ||
+      // the clear kernel: one thread per int64 word of the sums
+      vqk::kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks, dtype == VQ_BF16) / 8 / 256 +
+              1 > kMaxGrid)
     return VQ_ERR_INVALID_ARG;
   (void)hipGetLastError();
   return device_result(vqk::launch_kmeans(x, codebook, group_map, out_idx, l, iterations,

@@ -6,19 +6,27 @@
 // Care", step 2).  Lloyd's algorithm, every codebook slot trained on the
 // sub-vectors of its own groups:
 //   assignment: the encode (nearest centroid, exact) -> out_idx
-//   update:     centroid = exact member mean rounded once to fp16 (round to
-//               nearest even); a centroid without members keeps its value.
-// fp16 values are integer multiples of 2^-24, so member sums are exact int64
-// (|sum| < 2^40 * n).  Up to 512 centroids the encode itself adds every
+//   update:     centroid = exact member mean rounded once to the element type
+//               (round to nearest even); a centroid without members keeps
+//               its value.
+// fp16: every value is an integer multiple of 2^-24, so member sums are exact
+// int64 (|sum| < 2^40 * n).  Up to 512 centroids the encode itself adds every
 // sub-vector to its centroid's sums (fp64 LDS atomics, exact for the at most
 // 8192 rows a workgroup adds before it flushes, see vq_encode_mfma.hip);
 // otherwise km_accumulate reads the rows and codes back and adds them in LDS
 // with 64-bit integer atomics (or straight to global memory above 512
 // centroids).  Either way the per-workgroup sums are flushed with 64-bit
 // global atomics into one of kReplicas copies (fewer workgroups contend for
-// one address), which the update adds up.  Integer addition is associative,
-// so the result does not depend on the order of the additions, and the
-// rounding of sum / count is done exactly in integer arithmetic.
+// one address), which the update adds up.
+// bf16: every finite value is an integer multiple of 2^-133 below 2^261, so a
+// member sum is an integer below 2^285.  It is kept as kLimbs signed int64
+// limbs of 32 bits each (limb j weighs 2^(32 j)); a member's 8-bit
+// significand lands in at most two limbs (two 64-bit global atomics), and a
+// limb stays below 2^55 in magnitude for up to 2^23 members.  The update
+// propagates the carries into one 320-bit integer and divides it by the count.
+// Integer addition is associative, so the result does not depend on the order
+// of the additions, and the rounding of sum / count is done exactly in
+// integer arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,6 +43,7 @@ constexpr int kRowsPerThread = 4;
 constexpr int kRowsPerTile = kAccThreads * kRowsPerThread;  // rows per accumulate workgroup
 constexpr int kLdsMaxCentroids = 512;   // beyond: accumulate straight to global
 constexpr int kReplicas = kKmReplicas;  // copies of the sums the flush is spread over
+constexpr int kLimbs = kKmBf16Limbs;    // 32-bit limbs of an exact bf16 member sum
 
 // x * 2^24 as an exact integer (fp16 x; non-finite values count as 0): a
 // normal value (1024 + m) 2^(e - 25) gives (1024 + m) 2^(e - 1), a
@@ -75,6 +84,50 @@ __device__ uint16_t round_mean_f16(int64_t S, uint32_t n) {
   return sign | static_cast<uint16_t>(((e + 15) << 10) | (m - 1024));
 }
 
+// bf16 bits of A / (n * 2^133) rounded to nearest even, A = the magnitude
+// of an exact sum as 10 little-endian 32-bit words, n >= 1 (the count).
+__device__ uint16_t round_mean_bf16(uint32_t (&A)[10], uint32_t n, uint16_t sign) {
+  // Q = floor(A / n), r = A mod n, one word at a time from the top
+  uint32_t Q[10];
+  uint64_t rem = 0;
+#pragma unroll
+  for (int w = 9; w >= 0; --w) {
+    const uint64_t cur = (rem << 32) | A[w];
+    Q[w] = static_cast<uint32_t>(cur / n);
+    rem = cur - static_cast<uint64_t>(Q[w]) * n;
+  }
+  const uint32_t r = static_cast<uint32_t>(rem);
+  int bl = 0;  // bit length of Q
+#pragma unroll
+  for (int w = 0; w < 10; ++w)
+    if (Q[w]) bl = 32 * w + 32 - __clz(static_cast<int>(Q[w]));
+  // value = (Q + r / n) 2^-133; significand m = the value in ulps of its
+  // binade (2^(e - 7), e >= -126), which is Q / 2^k with k = max(bl - 8, 0)
+  const int k = bl > 8 ? bl - 8 : 0;
+  auto bit = [&](int i) -> uint32_t { return (Q[i >> 5] >> (i & 31)) & 1u; };
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (k + i < 320) m |= bit(k + i) << i;
+  bool up;
+  if (k == 0) {
+    up = 2ull * r > n || (2ull * r == n && (m & 1u));
+  } else {
+    bool sticky = r != 0;
+    for (int i = 0; i < k - 1; ++i) sticky = sticky || bit(i);
+    up = bit(k - 1) && (sticky || (m & 1u));
+  }
+  m += up ? 1u : 0u;
+  int e = k - 126;  // exponent of the binade (-126 for subnormals)
+  if (m == 256) {
+    m = 128;
+    ++e;
+  }
+  if (e > 127) return sign | 0x7F80u;
+  if (m < 128) return sign | static_cast<uint16_t>(m);  // subnormal (or zero)
+  return sign | static_cast<uint16_t>(((e + 127) << 7) | (m - 128));
+}
+
 struct KmArgs {
   const uint16_t *x;
   const uint32_t *idx;
@@ -84,6 +137,7 @@ struct KmArgs {
   unsigned int *counts;        // [kReplicas][n_codebooks][n_c]
   int64_t n, cb_stride, n_codebooks, group_len, tiles_per_group;
   int sd, n_c;
+  int limbs;  // 1 (fp16) or kLimbs (bf16) int64 words per (slot, centroid, component)
 };
 
 // Member sums and counts of one tile of rows (one group, so one slot).
@@ -159,6 +213,122 @@ __global__ void __launch_bounds__(kAccThreads) km_accumulate(const KmArgs a) {
   }
 }
 
+// bf16 member sums of one tile of rows (one group, so one slot), straight to
+// the global limbs: component bits (sign, exponent field E, fraction F) are
+// (128 + F) 2^(E - 1) units of 2^-133 when E > 0 and F units when E = 0; the
+// at most 9 significant bits land in limbs p / 32 and p / 32 + 1.
+template <int SD>
+__global__ void __launch_bounds__(kAccThreads) km_accumulate_bf16(const KmArgs a) {
+  const int64_t tile = blockIdx.x;
+  const int64_t g = tile / a.tiles_per_group;
+  const int64_t gstart = g * a.group_len;
+  const int64_t gend = min(gstart + a.group_len, a.n);
+  const int64_t tbase = gstart + (tile - g * a.tiles_per_group) * kRowsPerTile;
+  if (tbase >= gend) return;  // whole workgroup
+  const int64_t slot = a.group_map ? static_cast<int64_t>(a.group_map[g]) : g;
+  if (slot < 0 || slot >= a.n_codebooks) return;  // whole workgroup: no centroid to train
+  const int64_t tend = min(tbase + kRowsPerTile, gend);
+  const int64_t cells = a.n_codebooks * a.n_c;
+  const int rep = static_cast<int>(blockIdx.x % kReplicas);
+  unsigned long long *gs = a.sums + (rep * cells + slot * a.n_c) * SD * kLimbs;
+  unsigned int *gc = a.counts + rep * cells + slot * a.n_c;
+  using Row = std::conditional_t<SD == 4, uint2, uint4>;
+  uint32_t code[kRowsPerThread];
+  Row xr[kRowsPerThread];
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int64_t r = min(tbase + threadIdx.x + k * kAccThreads, tend - 1);
+    code[k] = a.idx[r];
+    xr[k] = reinterpret_cast<const Row *>(a.x)[r];
+  }
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int64_t r = tbase + threadIdx.x + k * kAccThreads;
+    const uint32_t c = code[k];
+    if (r >= tend || c >= static_cast<uint32_t>(a.n_c)) continue;
+    uint32_t w[SD / 2];
+    if constexpr (SD == 4) {
+      w[0] = xr[k].x;
+      w[1] = xr[k].y;
+    } else {
+      w[0] = xr[k].x;
+      w[1] = xr[k].y;
+      w[2] = xr[k].z;
+      w[3] = xr[k].w;
+    }
+#pragma unroll
+    for (int i = 0; i < SD; ++i) {
+      const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+      const uint32_t E = (bits >> 7) & 0xFFu, F = bits & 0x7Fu;
+      const uint32_t m = (E == 0) ? F : (128u | F);
+      if (E == 255u || m == 0) continue;  // non-finite adds 0
+      const uint32_t p = (E == 0) ? 0u : E - 1u;
+      const uint64_t v = static_cast<uint64_t>(m) << (p & 31u);
+      const bool neg = (bits & 0x8000u) != 0;
+      unsigned long long *limb = gs + (static_cast<int64_t>(c) * SD + i) * kLimbs + (p >> 5);
+      const uint64_t lo = v & 0xFFFFFFFFull, hi = v >> 32;
+      if (lo) atomicAdd(limb, neg ? 0ull - lo : lo);
+      if (hi) atomicAdd(limb + 1, neg ? 0ull - hi : hi);
+    }
+    atomicAdd(&gc[c], 1u);
+  }
+}
+
+// New bf16 centroids from the limbs, one thread per (slot, centroid,
+// component); the workgroup then clears what it read (as km_update).
+template <int SD>
+__global__ void __launch_bounds__(kThreads) km_update_bf16(const KmArgs a) {
+  const int64_t cells = a.n_codebooks * a.n_c;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * (kThreads / SD) + threadIdx.x / SD;
+  const int i = threadIdx.x % SD;
+  const bool live = e < cells;
+  if (live) {
+    unsigned int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kReplicas; ++r) cnt += a.counts[r * cells + e];
+    if (cnt > 0) {
+      // limb sums over the replicas (each below 2^58 in magnitude), then the
+      // carries into 10 words of a 320-bit two's complement integer
+      uint32_t W[10];
+      int64_t carry = 0;
+#pragma unroll
+      for (int j = 0; j < kLimbs; ++j) {
+        int64_t L = 0;
+#pragma unroll
+        for (int r = 0; r < kReplicas; ++r)
+          L += static_cast<int64_t>(a.sums[((r * cells + e) * SD + i) * kLimbs + j]);
+        const int64_t t = L + carry;
+        W[j] = static_cast<uint32_t>(t);
+        carry = t >> 32;  // arithmetic: floor(t / 2^32)
+      }
+      W[9] = static_cast<uint32_t>(carry);
+      const bool neg = carry < 0;
+      if (neg) {  // magnitude: invert and add one
+        uint64_t c1 = 1;
+#pragma unroll
+        for (int j = 0; j < 10; ++j) {
+          const uint64_t t = static_cast<uint64_t>(~W[j]) + c1;
+          W[j] = static_cast<uint32_t>(t);
+          c1 = t >> 32;
+        }
+      }
+      const int64_t slot = e / a.n_c;
+      const int64_t c = e - slot * a.n_c;
+      a.codebook[slot * a.cb_stride + c * SD + i] =
+          round_mean_bf16(W, cnt, neg ? static_cast<uint16_t>(0x8000u) : static_cast<uint16_t>(0));
+    }
+  }
+  __syncthreads();
+  if (live) {
+#pragma unroll
+    for (int r = 0; r < kReplicas; ++r) {
+#pragma unroll
+      for (int j = 0; j < kLimbs; ++j) a.sums[((r * cells + e) * SD + i) * kLimbs + j] = 0;
+      if (i == 0) a.counts[r * cells + e] = 0;
+    }
+  }
+}
+
 // New centroids from the sums, one thread per (slot, centroid, component);
 // a workgroup holds whole centroids, and clears their sums and counts for
 // the next iteration once all of its threads have read them.
@@ -195,14 +365,14 @@ __global__ void __launch_bounds__(kThreads) km_update(const KmArgs a) {
 __global__ void __launch_bounds__(kThreads) km_clear(const KmArgs a) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t nc = kReplicas * a.n_codebooks * a.n_c;
-  if (e < nc * a.sd) a.sums[e] = 0;
+  if (e < nc * a.sd * a.limbs) a.sums[e] = 0;
   if (e < nc) a.counts[e] = 0;
 }
 
 template <int SD>
 hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream_t stream) {
   const int64_t cells = a.n_codebooks * a.n_c;
-  const int64_t clear_blocks = (kReplicas * cells * SD + kThreads - 1) / kThreads;
+  const int64_t clear_blocks = (kReplicas * cells * SD * a.limbs + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(km_clear, dim3(static_cast<uint32_t>(clear_blocks)), dim3(kThreads), 0,
                      stream, a);
   hipError_t err = hipGetLastError();
@@ -212,6 +382,25 @@ hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream
                          ? static_cast<size_t>(a.n_c) * (SD + 1) * sizeof(unsigned long long)
                          : 0;
   const int64_t upd_blocks = (cells * SD + kThreads - 1) / kThreads;
+  if (l.bf16) {
+    for (int it = 0; it < iterations; ++it) {
+      err = encode_mfma_supported(l)
+                ? launch_encode_mfma(a.x, a.codebook, a.group_map, const_cast<uint32_t *>(a.idx),
+                                     l, plain_codes(l), stream)
+                : launch_encode(a.x, a.codebook, a.group_map, const_cast<uint32_t *>(a.idx), l,
+                                plain_codes(l), stream);
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL(km_accumulate_bf16<SD>, dim3(static_cast<uint32_t>(tiles)),
+                         dim3(kAccThreads), 0, stream, a);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL(km_update_bf16<SD>, dim3(static_cast<uint32_t>(upd_blocks)),
+                         dim3(kThreads), 0, stream, a);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+  }
   // up to 512 fp16 centroids the encode adds the member sums itself
   const bool fused = encode_mfma_kmeans_supported(l);
   for (int it = 0; it < iterations; ++it) {
@@ -245,9 +434,10 @@ hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream
 
 }  // namespace
 
-size_t kmeans_workspace_bytes(int sub_dim, int n_centroids, int64_t n_codebooks) {
+size_t kmeans_workspace_bytes(int sub_dim, int n_centroids, int64_t n_codebooks, bool bf16) {
+  const int limbs = bf16 ? kLimbs : 1;
   return static_cast<size_t>(kReplicas) * n_codebooks * n_centroids *
-         (sub_dim * sizeof(unsigned long long) + sizeof(unsigned int));
+         (sub_dim * limbs * sizeof(unsigned long long) + sizeof(unsigned int));
 }
 
 int64_t kmeans_grid(const Layout &l) {
@@ -263,8 +453,9 @@ hipError_t launch_kmeans(const void *x, void *codebook, const int32_t *group_map
   a.codebook = static_cast<uint16_t *>(codebook);
   a.group_map = group_map;
   a.sums = static_cast<unsigned long long *>(workspace);
+  a.limbs = l.bf16 ? kLimbs : 1;
   a.counts = reinterpret_cast<unsigned int *>(a.sums + kReplicas * l.n_codebooks * l.n_centroids *
-                                                           l.sub_dim);
+                                                           l.sub_dim * a.limbs);
   a.n = l.n;
   a.cb_stride = l.codebook_stride;
   a.n_codebooks = l.n_codebooks;

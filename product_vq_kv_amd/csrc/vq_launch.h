@@ -52,6 +52,8 @@ hipError_t launch_encode_mfma(const void *x, const void *codebook, const int32_t
 // and counts [n_codebooks][n_c]; a workgroup adds into copy (index mod
 // kKmReplicas).
 constexpr int kKmReplicas = 8;
+// 32-bit limbs of an exact bf16 member sum (multiples of 2^-133 below 2^285)
+constexpr int kKmBf16Limbs = 9;
 struct KmSums {
   unsigned long long *sums;
   unsigned int *counts;
@@ -84,9 +86,10 @@ struct AttnLayout {
   float softmax_scale;
 };
 
-// K-means calibration (fp16): `iterations` Lloyd steps, codebook updated in
-// place, final assignment in out_idx; workspace = exact member sums + counts.
-size_t kmeans_workspace_bytes(int sub_dim, int n_centroids, int64_t n_codebooks);
+// K-means calibration (fp16 or bf16): `iterations` Lloyd steps, codebook
+// updated in place, final assignment in out_idx; workspace = exact member
+// sums (one int64 per component for fp16, kKmBf16Limbs for bf16) + counts.
+size_t kmeans_workspace_bytes(int sub_dim, int n_centroids, int64_t n_codebooks, bool bf16);
 int64_t kmeans_grid(const Layout &l);
 hipError_t launch_kmeans(const void *x, void *codebook, const int32_t *group_map, uint32_t *out_idx,
                          const Layout &l, int iterations, void *workspace, hipStream_t stream);

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert vq.lib.vq_abi_version() == 5
+    assert vq.lib.vq_abi_version() == 6
     for code in (0, -1, -2, -3, -4, -5, 99):
         assert isinstance(vq.lib.vq_status_str(code), bytes)
     assert vq.lib.vq_status_str(-3) == b"misaligned pointer"
@@ -249,13 +249,18 @@ def km(**over):
 
 
 def test_kmeans_workspace_size():
-    # 8 replicas of the exact int64 member sums and uint32 counts per (slot, centroid)
-    assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4) == 8 * 4 * 256 * (8 * 8 + 4)
-    assert vq.lib.vq_kmeans_workspace_bytes(3, 256, 4) == 0
+    # 8 replicas of the exact member sums (one int64 per component for fp16,
+    # 9 limbs for bf16) and uint32 counts per (slot, centroid)
+    assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4, 0) == 8 * 4 * 256 * (8 * 8 + 4)
+    assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4, 1) == 8 * 4 * 256 * (8 * 9 * 8 + 4)
+    assert vq.lib.vq_kmeans_workspace_bytes(4, 4096, 1, 1) == 8 * 4096 * (4 * 9 * 8 + 4)
+    assert vq.lib.vq_kmeans_workspace_bytes(3, 256, 4, 0) == 0
+    assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4, 2) == 0
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(dt=1), UNSUPPORTED), (dict(sd=2), UNSUPPORTED), (dict(n_c=0), INVALID),
+    (dict(dt=2), UNSUPPORTED), (dict(sd=2), UNSUPPORTED), (dict(n_c=0), INVALID),
+    (dict(dt=1, wsb=8 * 256 * (8 * 8 + 4)), INVALID),    # an fp16-sized workspace for bf16
     (dict(it=-1), INVALID), (dict(x=None), INVALID), (dict(out=None), INVALID),
     (dict(ws=None), INVALID), (dict(wsb=16), INVALID), (dict(x=FAKE + 8), MISALIGNED),
     (dict(out=FAKE + 2), MISALIGNED), (dict(ws=FAKE + 4), MISALIGNED),

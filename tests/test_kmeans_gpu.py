@@ -1,7 +1,12 @@
 """GPU parity of K-means calibration (vq_kmeans) against the CPU oracle.
 
-Every update is the exact member mean rounded once to fp16 on both sides, so
-the codebooks and assignments must be bit-identical after every iteration.
+Every update is the exact member mean rounded once to the element type (fp16
+or bf16) on both sides, so the codebooks and assignments must be
+bit-identical after every iteration.  bf16 cases cover both sub-dims, LDS-
+and global-sized codebooks, the direct kernel, slots and maps, members whose
+exponents span the whole bf16 range (sums across every limb, with carries),
+subnormal and non-finite components, and 2^18 sub-vectors of the
+large-codebook workload (4,096 centroids with duplicate rows).
 Cases cover sub_dim 4 and 8, LDS and global accumulation (n_centroids above
 512), the matrix-core and direct assignment kernels (up to 5000 centroids),
 several slots with group maps and bad slots, workgroups spanning several
@@ -35,7 +40,7 @@ def gpu_kmeans(wl, iterations):
     cb = cb3[0] if wl.n_codebooks == 1 else cb3
     idx = vq.kmeans(x, cb, iterations, group_len=wl.group_len, group_map=gmap)
     torch.cuda.synchronize()
-    full = cb3.reshape(wl.n_codebooks, -1).cpu().numpy().view(np.uint16)
+    full = cb3.reshape(wl.n_codebooks, -1).view(torch.int16).cpu().numpy().view(np.uint16)
     return full, idx.cpu().numpy().view(np.uint32)
 
 
@@ -48,7 +53,7 @@ def slots_of(cb_flat, wl):
 def assert_kmeans_parity(wl, iterations):
     got_cb, got_idx = gpu_kmeans(wl, iterations)
     want_cb, want_idx, counts = K.kmeans(wl.x, wl.codebook, wl.sub_dim, wl.n_centroids,
-                                         iterations, threads=16, **wl.kwargs())
+                                         iterations, dtype=wl.dtype, threads=16, **wl.kwargs())
     want = slots_of(want_cb, wl)
     moved = int(np.sum(want != slots_of(wl.codebook, wl)))
     print(f"[parity] {wl.name} x{iterations}: {moved} codebook elements moved, "
@@ -144,3 +149,54 @@ def test_kmeans_full_cache_sampled_slots():
         np.testing.assert_array_equal(got_idx[rows], want_idx)
         np.testing.assert_array_equal(got_cb[s], want_cb)
         print(f"[parity] full cache slot {s}: identical", flush=True)
+
+
+BF16_CASES = [
+    # (seed, n, sd, n_c, iterations, extras)
+    (21, 3000, 8, 7, 3, {}),
+    (22, 5000, 4, 64, 3, dict(scale=1e20)),
+    (23, 20000, 8, 256, 3, dict(scale=1e-20)),
+    (24, 9000, 4, 600, 2, {}),
+    (25, 3000, 8, 5000, 1, {}),                # direct assignment kernel
+    (26, 9000, 8, 32, 2, dict(n_codebooks=4, group_len=2048, use_map=True)),
+    (27, 40000, 4, 513, 2, dict(dup_frac=0.05)),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES,
+                         ids=[f"b{c[0]}_n{c[1]}_sd{c[2]}_nc{c[3]}" for c in BF16_CASES])
+def test_kmeans_bf16_matches_oracle(case):
+    seed, n, sd, n_c, iters, extra = case
+    wl = W.random_case(400 + seed, n, sd, n_c, W.BF16, **extra)
+    print(f"[case] {wl.name} {extra}", flush=True)
+    assert_kmeans_parity(wl, iters)
+
+
+def test_kmeans_bf16_members_across_the_exponent_range():
+    """Clusters whose members span 2^-133 .. 2^127 with both signs: the sums
+    fill every limb and carry between them; one cluster's members cancel to
+    a subnormal mean, another's sum passes 2^127 before the division."""
+    rng = np.random.default_rng(431)
+    n = 60000
+    mag = np.ldexp(rng.uniform(1.0, 2.0, (n, 8)), rng.integers(-133, 128, (n, 8)))
+    x = np.where(rng.random((n, 8)) < 0.5, -mag, mag)
+    x[: n // 3, :] = np.ldexp(rng.uniform(1.0, 2.0, (n // 3, 8)), 126)   # fp32 distances overflow
+    x[n // 3: n // 3 + 50, 0] = np.ldexp(1.0, -133) * rng.integers(1, 4, 50)
+    bits = W.to_bf16_bits(x).reshape(-1, 8)
+    bits[rng.random((n, 8)) < 0.001] = 0x7F80                   # +inf components add 0
+    init = W.to_bf16_bits(np.ldexp(rng.standard_normal((16, 8)), rng.integers(-100, 100, (16, 8))))
+    wl = W.Workload("bf16 exponent range", bits, init.reshape(-1), 8, 16, W.BF16, 128, 1, n)
+    print(f"[case] {wl.name}: {n} rows", flush=True)
+    assert_kmeans_parity(wl, 3)
+
+
+def test_kmeans_bf16_large_codebook_subset():
+    """2^18 sub-vectors of the large-codebook workload: 4,096 bf16 centroids
+    of sub_dim 8 with about 5% exact duplicate rows (duplicates never gain
+    members: ties go to the lowest index)."""
+    full = W.config(5)
+    rows = 1 << 18
+    wl = W.Workload(full.name + ", first 2^18 rows", full.x[:rows].copy(), full.codebook,
+                    full.sub_dim, full.n_centroids, full.dtype, full.codebook_stride, 1, rows)
+    print(f"[case] {wl.name}", flush=True)
+    assert_kmeans_parity(wl, 2)

@@ -44,6 +44,8 @@ supplies the parity sample.
   kmeans  ``vq_kmeans``: 5 Lloyd iterations per call on the Falcon3-7B keys
          (1,048,576 sub-vectors, 256 centroids, sub_dim 4); fp32 vector
          roofline on the assignment's algorithmic flops.
+  kmeans_bf16  the same on the large-codebook workload (1,048,576 bf16
+         sub-vectors, 4,096 centroids of sub_dim 8).
 Every row is timed after a short GPU warm-up: its launches are enqueued
 behind a short spin kernel, so the events measure the launches back to back
 (``kernel_ms_per_launch``) however fast the host enqueues; ``host_ms_per_call``
@@ -76,7 +78,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CONFIG_TAGS = {1: "encode_tiny", 2: "encode_llama8b", 3: "encode_falcon3", 4: "encode_full_cache",
                5: "encode_large_codebook"}
 ROW_TAGS = {"fused": "encode_fused_falcon3", "attention": "attention_falcon3_decode",
-            "kmeans": "kmeans_falcon3"}
+            "kmeans": "kmeans_falcon3", "kmeans_bf16": "kmeans_bf16_large_codebook"}
 # rows of each config the oracle checks in the bench (the tests check all)
 PARITY_ROWS = {1: 2048, 2: 1 << 18, 4: 1 << 18, 5: 1 << 14}
 
@@ -406,16 +408,19 @@ def leg_attention(args, dev, stream):
     }
 
 
-def leg_kmeans(args, dev, stream):
-    """K-means calibration (Lloyd) on the Falcon3-7B keys."""
+def leg_kmeans(args, dev, stream, cfg: int = 3, tag: str = "kmeans"):
+    """K-means calibration (Lloyd) on the Falcon3-7B keys (fp16), or on the
+    large-codebook workload (bf16, 4,096 centroids; its parity is checked by
+    the GPU tests, the oracle being too slow for a bench sample)."""
     import numpy as np
     import torch
     import workloads as W
     import product_vq_kv_amd as vq
-    wl = W.config(3)
-    log(f"row kmeans: {wl.name}, {KMEANS_ITERATIONS} iterations per call")
-    x = torch.from_numpy(wl.x.view(np.int16)).view(torch.float16).to(dev)
-    cb0 = torch.from_numpy(wl.codebook.view(np.int16)).view(torch.float16).to(dev)
+    wl = W.config(cfg)
+    log(f"row {tag}: {wl.name}, {KMEANS_ITERATIONS} iterations per call")
+    tdt = torch.float16 if wl.dtype == W.F16 else torch.bfloat16
+    x = torch.from_numpy(wl.x.view(np.int16)).view(tdt).to(dev)
+    cb0 = torch.from_numpy(wl.codebook.view(np.int16)).view(tdt).to(dev)
     cb = cb0.clone()
     idx = torch.empty(wl.n, dtype=torch.uint32, device=dev)
     wsb = vq.kmeans_workspace_bytes(wl.sub_dim, wl.n_centroids, 1, wl.dtype)
@@ -429,7 +434,7 @@ def leg_kmeans(args, dev, stream):
     flops = 3.0 * wl.sub_dim * wl.n_centroids * wl.n
     achieved = flops / it_s / 1e12
     parity = None
-    if args.cpu_sample > 0:
+    if args.cpu_sample > 0 and wl.n_centroids <= 256:
         # from the initial codebook, one call of the library against the oracle
         from oracle import kmeans as K
         cb.copy_(cb0)
@@ -437,12 +442,12 @@ def leg_kmeans(args, dev, stream):
         torch.cuda.synchronize()
         want_cb, want_idx, _ = K.kmeans(wl.x, wl.codebook, wl.sub_dim, wl.n_centroids,
                                         KMEANS_ITERATIONS, threads=host_threads())
-        got_cb = cb.cpu().numpy().view(np.uint16)
+        got_cb = cb.view(torch.int16).cpu().numpy().view(np.uint16)
         parity = dict(iterations=KMEANS_ITERATIONS,
                       codebook_equal=int(np.sum(got_cb == want_cb)), codebook_size=int(want_cb.size),
                       assignment_equal=int(np.sum(idx.cpu().numpy().view(np.uint32) == want_idx)),
                       rows=int(wl.n))
-    tag = ROW_TAGS["kmeans"]
+    tag = ROW_TAGS[tag]
     return {
         "workload": wl.name + f", Lloyd x{KMEANS_ITERATIONS} per call",
         "value": wl.n * KMEANS_ITERATIONS / launch_s,
@@ -458,7 +463,9 @@ def leg_kmeans(args, dev, stream):
     }
 
 
-ROW_LEGS = {"fused": leg_fused, "attention": leg_attention, "kmeans": leg_kmeans}
+ROW_LEGS = {"fused": leg_fused, "attention": leg_attention, "kmeans": leg_kmeans,
+            "kmeans_bf16": lambda args, dev, stream: leg_kmeans(args, dev, stream, 5,
+                                                                "kmeans_bf16")}
 ROW_LEGS.update({f"config{c}": leg_config(c) for c in (1, 2, 4, 5)})
 
 
@@ -476,7 +483,7 @@ def main() -> int:
                     help="also run a plain device copy of known size (counter scaling)")
     ap.add_argument("--configs", default="config1,config2,config4,config5",
                     help="comma-separated encode workloads to add as rows ('' = none)")
-    ap.add_argument("--rows", default="fused,attention,kmeans",
+    ap.add_argument("--rows", default="fused,attention,kmeans,kmeans_bf16",
                     help="comma-separated adjacent rows to time after the headline ('' = none)")
     ap.add_argument("--attention-batches", default="64,128",
                     help="extra sequence counts the attention row is timed at ('' = none)")

@@ -164,7 +164,7 @@ vq_status vq_encode_packed(const void *x, const void *codebook, int64_t n, int32
  *                 ties to even); a centroid without members keeps its value.
  * Exact means: every finite fp16 value is an integer multiple of 2^-24 and
  * every finite bf16 value one of 2^-133, so member sums are exact integers
- * (int64 for fp16, 9 limbs of 32 bits for bf16) and the mean is rounded once,
+ * (int64 for fp16, 8 int64 limbs of weight 2^(32 j) for bf16) and the mean is rounded once,
  * in integer arithmetic.  A non-finite component adds 0 to its sum (its row
  * still counts as a member).  The codebook is updated in place; out_idx holds
  * the assignment of the last iteration (made against the codebook before its

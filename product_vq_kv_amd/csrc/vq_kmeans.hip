@@ -20,10 +20,11 @@
 // one address), which the update adds up.
 // bf16: every finite value is an integer multiple of 2^-133 below 2^261, so a
 // member sum is an integer below 2^285.  It is kept as kLimbs signed int64
-// limbs of 32 bits each (limb j weighs 2^(32 j)); a member's 8-bit
-// significand lands in at most two limbs (two 64-bit global atomics), and a
-// limb stays below 2^55 in magnitude for up to 2^23 members.  The update
-// propagates the carries into one 320-bit integer and divides it by the count.
+// limbs, limb j weighing 2^(32 j): a member whose value is m 2^p units (m <
+// 2^8) adds m 2^(p mod 32) < 2^39 to limb p / 32 with one 64-bit global
+// atomic, so a limb stays below 2^23 * 2^39 = 2^62 in magnitude for up to
+// 2^23 members (limbs carry past 32 bits).  The update propagates the carries
+// into one 320-bit integer and divides it by the count.
 // Integer addition is associative, so the result does not depend on the order
 // of the additions, and the rounding of sum / count is done exactly in
 // integer arithmetic.
@@ -43,7 +44,7 @@ constexpr int kRowsPerThread = 4;
 constexpr int kRowsPerTile = kAccThreads * kRowsPerThread;  // rows per accumulate workgroup
 constexpr int kLdsMaxCentroids = 512;   // beyond: accumulate straight to global
 constexpr int kReplicas = kKmReplicas;  // copies of the sums the flush is spread over
-constexpr int kLimbs = kKmBf16Limbs;    // 32-bit limbs of an exact bf16 member sum
+constexpr int kLimbs = kKmBf16Limbs;    // int64 limbs (weight 2^(32 j)) of a bf16 member sum
 
 // x * 2^24 as an exact integer (fp16 x; non-finite values count as 0): a
 // normal value (1024 + m) 2^(e - 25) gives (1024 + m) 2^(e - 1), a
@@ -215,8 +216,8 @@ __global__ void __launch_bounds__(kAccThreads) km_accumulate(const KmArgs a) {
 
 // bf16 member sums of one tile of rows (one group, so one slot), straight to
 // the global limbs: component bits (sign, exponent field E, fraction F) are
-// (128 + F) 2^(E - 1) units of 2^-133 when E > 0 and F units when E = 0; the
-// at most 9 significant bits land in limbs p / 32 and p / 32 + 1.
+// m 2^p units of 2^-133 with m = 128 + F, p = E - 1 when E > 0 and m = F,
+// p = 0 when E = 0; m 2^(p mod 32) goes to limb p / 32.
 template <int SD>
 __global__ void __launch_bounds__(kAccThreads) km_accumulate_bf16(const KmArgs a) {
   const int64_t tile = blockIdx.x;
@@ -265,10 +266,7 @@ __global__ void __launch_bounds__(kAccThreads) km_accumulate_bf16(const KmArgs a
       const uint32_t p = (E == 0) ? 0u : E - 1u;
       const uint64_t v = static_cast<uint64_t>(m) << (p & 31u);
       const bool neg = (bits & 0x8000u) != 0;
-      unsigned long long *limb = gs + (static_cast<int64_t>(c) * SD + i) * kLimbs + (p >> 5);
-      const uint64_t lo = v & 0xFFFFFFFFull, hi = v >> 32;
-      if (lo) atomicAdd(limb, neg ? 0ull - lo : lo);
-      if (hi) atomicAdd(limb + 1, neg ? 0ull - hi : hi);
+      atomicAdd(gs + (static_cast<int64_t>(c) * SD + i) * kLimbs + (p >> 5), neg ? 0ull - v : v);
     }
     atomicAdd(&gc[c], 1u);
   }
@@ -287,8 +285,9 @@ __global__ void __launch_bounds__(kThreads) km_update_bf16(const KmArgs a) {
 #pragma unroll
     for (int r = 0; r < kReplicas; ++r) cnt += a.counts[r * cells + e];
     if (cnt > 0) {
-      // limb sums over the replicas (each below 2^58 in magnitude), then the
-      // carries into 10 words of a 320-bit two's complement integer
+      // limb sums over the replicas (together below 2^62 in magnitude: the
+      // members are split between the replicas), then the carries into 10
+      // words of a 320-bit two's complement integer
       uint32_t W[10];
       int64_t carry = 0;
 #pragma unroll
@@ -301,7 +300,11 @@ __global__ void __launch_bounds__(kThreads) km_update_bf16(const KmArgs a) {
         W[j] = static_cast<uint32_t>(t);
         carry = t >> 32;  // arithmetic: floor(t / 2^32)
       }
-      W[9] = static_cast<uint32_t>(carry);
+#pragma unroll
+      for (int j = kLimbs; j < 10; ++j) {  // the carry's words, sign-extended
+        W[j] = static_cast<uint32_t>(carry);
+        carry >>= 32;
+      }
       const bool neg = carry < 0;
       if (neg) {  // magnitude: invert and add one
         uint64_t c1 = 1;

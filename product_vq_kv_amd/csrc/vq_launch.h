@@ -52,8 +52,9 @@ hipError_t launch_encode_mfma(const void *x, const void *codebook, const int32_t
 // and counts [n_codebooks][n_c]; a workgroup adds into copy (index mod
 // kKmReplicas).
 constexpr int kKmReplicas = 8;
-// 32-bit limbs of an exact bf16 member sum (multiples of 2^-133 below 2^285)
-constexpr int kKmBf16Limbs = 9;
+// int64 limbs (weights 2^(32 j)) of an exact bf16 member sum (multiples of
+// 2^-133 below 2^285)
+constexpr int kKmBf16Limbs = 8;
 struct KmSums {
   unsigned long long *sums;
   unsigned int *counts;

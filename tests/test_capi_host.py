@@ -250,10 +250,10 @@ def km(**over):
 
 def test_kmeans_workspace_size():
     # 8 replicas of the exact member sums (one int64 per component for fp16,
-    # 9 limbs for bf16) and uint32 counts per (slot, centroid)
+    # 8 limbs for bf16) and uint32 counts per (slot, centroid)
     assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4, 0) == 8 * 4 * 256 * (8 * 8 + 4)
-    assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4, 1) == 8 * 4 * 256 * (8 * 9 * 8 + 4)
-    assert vq.lib.vq_kmeans_workspace_bytes(4, 4096, 1, 1) == 8 * 4096 * (4 * 9 * 8 + 4)
+    assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4, 1) == 8 * 4 * 256 * (8 * 8 * 8 + 4)
+    assert vq.lib.vq_kmeans_workspace_bytes(4, 4096, 1, 1) == 8 * 4096 * (4 * 8 * 8 + 4)
     assert vq.lib.vq_kmeans_workspace_bytes(3, 256, 4, 0) == 0
     assert vq.lib.vq_kmeans_workspace_bytes(8, 256, 4, 2) == 0
 

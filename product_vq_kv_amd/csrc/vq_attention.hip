@@ -916,7 +916,7 @@ hipError_t launch_attn_t(AttnArgs a, hipStream_t stream) {
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  a.n_chunks = std::max(1, (a.S + kChunk - 1) / kChunk);
+  a.n_chunks = std::max(1, static_cast<int>((static_cast<int64_t>(a.S) + kChunk - 1) / kChunk));
   hipLaunchKernelGGL(kern, dim3(a.n_chunks, a.Hkv, a.B), dim3(kThreads), lds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -938,7 +938,7 @@ hipError_t launch_attn_m(AttnArgs a, hipStream_t stream) {
     const int g = a.Hq / a.Hkv;
     auto kern = g <= 4 ? attn_mfma_partial<SDK, SDV, BF16, D, 4>
                        : attn_mfma_partial<SDK, SDV, BF16, D, kMaxGroup>;
-    a.n_chunks = std::max(1, (a.S + kMChunk - 1) / kMChunk);
+    a.n_chunks = attention_chunks(a.S);
     hipLaunchKernelGGL(kern, dim3(a.n_chunks, a.Hkv, a.B), dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -997,7 +997,10 @@ hipError_t attention_static_scratch(void **ptr) {
   return hipSuccess;
 }
 
-int attention_chunks(int max_kv_len) { return std::max(1, (max_kv_len + kMChunk - 1) / kMChunk); }
+int attention_chunks(int max_kv_len) {
+  // 64-bit: max_kv_len may be close to INT32_MAX
+  return std::max(1, static_cast<int>((static_cast<int64_t>(max_kv_len) + kMChunk - 1) / kMChunk));
+}
 
 size_t attention_lds_bytes(int sdk, int sdv, int D, int g) {
   if (sdk == 4) return sdv == 4 ? attn_lds_bytes<4, 4>(D, g) : attn_lds_bytes<4, 8>(D, g);

@@ -213,9 +213,8 @@ vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
   if (per_slot > (int64_t(1) << 23)) return VQ_ERR_UNSUPPORTED;
   if (n == 0 || iterations == 0) return VQ_OK;
   if (!x || !out_idx || !workspace) return VQ_ERR_INVALID_ARG;
-  if (workspace_bytes <
-      vqk::kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks, dtype == VQ_BF16))
-    return VQ_ERR_INVALID_ARG;
+  const size_t need = vqk::kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks, dtype == VQ_BF16);
+  if (need == 0 || workspace_bytes < need) return VQ_ERR_INVALID_ARG;  // 0: size overflows
   if (reinterpret_cast<uintptr_t>(x) % (2 * sub_dim) != 0 ||
       reinterpret_cast<uintptr_t>(out_idx) % 4 != 0 ||
       reinterpret_cast<uintptr_t>(workspace) % 8 != 0)
@@ -223,8 +222,7 @@ vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
   if (vqk::encode_grid(l) > kMaxGrid || vqk::encode_mfma_grid(l) > kMaxGrid ||
       vqk::kmeans_grid(l) > kMaxGrid || n_codebooks * n_centroids * sub_dim / 32 + 1 > kMaxGrid ||
       // the clear kernel: one thread per int64 word of the sums
-      vqk::kmeans_workspace_bytes(sub_dim, n_centroids, n_codebooks, dtype == VQ_BF16) / 8 / 256 +
-              1 > kMaxGrid)
+      static_cast<int64_t>(need / 8 / 256) + 1 > kMaxGrid)
     return VQ_ERR_INVALID_ARG;
   (void)hipGetLastError();
   return device_result(vqk::launch_kmeans(x, codebook, group_map, out_idx, l, iterations,
@@ -234,8 +232,13 @@ vq_status vq_kmeans(const void *x, void *codebook, int64_t n, int32_t sub_dim,
 size_t vq_attention_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim,
                                     int32_t max_kv_len) {
   if (batch < 0 || n_q_heads < 0 || head_dim < 0 || max_kv_len < 0) return 0;
-  return static_cast<size_t>(batch) * n_q_heads * vqk::attention_chunks(max_kv_len) *
-         (static_cast<size_t>(head_dim) + 2) * sizeof(float);
+  uint64_t r = 0;
+  if (__builtin_mul_overflow(static_cast<uint64_t>(batch), static_cast<uint64_t>(n_q_heads), &r) ||
+      __builtin_mul_overflow(r, static_cast<uint64_t>(vqk::attention_chunks(max_kv_len)), &r) ||
+      __builtin_mul_overflow(r, (static_cast<uint64_t>(head_dim) + 2) * sizeof(float), &r) ||
+      r > static_cast<uint64_t>(INT64_MAX))
+    return 0;  // does not fit: the decode calls reject such sizes
+  return static_cast<size_t>(r);
 }
 
 vq_status vq_attention_decode(const void *q, const uint8_t *k_codes, const uint8_t *v_codes,
@@ -253,8 +256,8 @@ vq_status vq_attention_decode(const void *q, const uint8_t *k_codes, const uint8
                                        softmax_scale, out, &l);
   if (st != VQ_OK || batch == 0) return st;
   if (!workspace) return VQ_ERR_INVALID_ARG;
-  if (workspace_bytes < vq_attention_workspace_bytes(batch, n_q_heads, head_dim, max_kv_len))
-    return VQ_ERR_INVALID_ARG;
+  const size_t need = vq_attention_workspace_bytes(batch, n_q_heads, head_dim, max_kv_len);
+  if (need == 0 || workspace_bytes < need) return VQ_ERR_INVALID_ARG;  // 0: size overflows
   if (reinterpret_cast<uintptr_t>(workspace) % 4) return VQ_ERR_MISALIGNED;
   l.workspace = static_cast<float *>(workspace);
   (void)hipGetLastError();
@@ -275,9 +278,9 @@ vq_status vq_attention_decode_static(const void *q, const uint8_t *k_codes,
                                        k_sub_dim, v_sub_dim, n_centroids, dtype, window,
                                        softmax_scale, out, &l);
   if (st != VQ_OK || batch == 0) return st;
-  if (vq_attention_workspace_bytes(batch, n_q_heads, head_dim, max_kv_len) >
-      VQ_ATTN_STATIC_SCRATCH_BYTES)
-    return VQ_ERR_TOO_LARGE;
+  const size_t need = vq_attention_workspace_bytes(batch, n_q_heads, head_dim, max_kv_len);
+  if (need == 0) return VQ_ERR_INVALID_ARG;  // the size overflows
+  if (need > VQ_ATTN_STATIC_SCRATCH_BYTES) return VQ_ERR_TOO_LARGE;
   void *scratch = nullptr;
   (void)hipGetLastError();
   const hipError_t e = vqk::attention_static_scratch(&scratch);

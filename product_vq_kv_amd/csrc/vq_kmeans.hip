@@ -439,8 +439,14 @@ hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream
 
 size_t kmeans_workspace_bytes(int sub_dim, int n_centroids, int64_t n_codebooks, bool bf16) {
   const int limbs = bf16 ? kLimbs : 1;
-  return static_cast<size_t>(kReplicas) * n_codebooks * n_centroids *
-         (sub_dim * limbs * sizeof(unsigned long long) + sizeof(unsigned int));
+  const uint64_t cell = sub_dim * limbs * sizeof(unsigned long long) + sizeof(unsigned int);
+  uint64_t r = 0;
+  // 0 when the size does not fit in 63 bits (the caller rejects it)
+  if (n_codebooks < 1 || n_centroids < 1 ||
+      __builtin_mul_overflow(static_cast<uint64_t>(n_codebooks), static_cast<uint64_t>(n_centroids), &r) ||
+      __builtin_mul_overflow(r, cell * kReplicas, &r) || r > static_cast<uint64_t>(INT64_MAX))
+    return 0;
+  return static_cast<size_t>(r);
 }
 
 int64_t kmeans_grid(const Layout &l) {

@@ -179,6 +179,17 @@ def attn(**over):
                                       a["scale"], a["out"], a["ws"], a["wsb"], a["stream"])
 
 
+def test_workspace_sizes_that_overflow_are_rejected():
+    """Sizes whose byte counts do not fit 63 bits give 0, and the calls
+    reject them instead of accepting a wrapped (small) workspace."""
+    big = (1 << 31) - 1
+    assert vq.lib.vq_attention_workspace_bytes(65535, 32768, 256, big) == 0
+    assert vq.lib.vq_attention_workspace_bytes(2, 12, 256, big) == 2 * 12 * (big // 256 + 1) * 258 * 4
+    assert vq.lib.vq_kmeans_workspace_bytes(8, 65536, (1 << 62), 1) == 0
+    assert attn(B=65535, Hq=32768, Hkv=32768, D=256, S=big, wsb=1 << 20) == INVALID
+    assert attn_static(B=65535, Hq=32768, Hkv=32768, D=256, S=big) == INVALID
+
+
 def test_attention_workspace_size():
     # one (D + 2)-float partial per (sequence, query head, 256-token chunk)
     assert vq.lib.vq_attention_workspace_bytes(2, 12, 256, 100) == 2 * 12 * 1 * 258 * 4

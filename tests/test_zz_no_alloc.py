@@ -6,6 +6,9 @@ static per-GPU scratch replaces the workspace), and both must be within the
 derived error bound of the float64 oracle.  Two calls in a row, the second
 on a smaller input, so the second reads a scratch buffer the first left
 dirty; the device's free memory must not change across a static call.
+Captured in a HIP graph (through torch's graph API), the call must give
+the eager result on every replay, with new queries copied in and other
+eager work between the replays.
 """
 import numpy as np
 import pytest
@@ -89,3 +92,28 @@ def test_static_scratch_rejects_inputs_beyond_its_size():
                                        t["v_codes"].data_ptr(), t["k_codebook"].data_ptr(),
                                        t["v_codebook"].data_ptr(), None, None, 1024, 8, 1, 256,
                                        4096, 4, 4, 64, W.F16, 0, 0.0625, out.data_ptr(), None)
+
+
+def test_static_entry_point_captured_in_a_graph():
+    wl = W.attention_case(56, 6, 12, 4, 256, 1800, 4, 4, 256, W.F16, lens="mixed")
+    t = _dev(wl)
+    B, Hq, Hkv, D, S = wl.shape
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)
+    args = (t["q"], t["k_codes"], t["v_codes"], t["k_codebook"], t["v_codebook"])
+    kw = dict(k_scale=t["k_scale"], kv_len=t["kv_len"])
+    vq.attention_decode_static(*args, **kw, out=out)      # resolves the scratch address
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        vq.attention_decode_static(*args, **kw, out=out)
+    rng = np.random.default_rng(56)
+    for rep in range(3):
+        qn = torch.from_numpy(rng.standard_normal((B, Hq, D)).astype(np.float16)).to(DEV)
+        t["q"].copy_(qn)                                   # eager work between replays
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = vq.attention_decode(*args, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs from the eager call"
+    print("[graph] 3 replays equal to the eager call", flush=True)

@@ -13,15 +13,21 @@
 //   accumulation of the m = sub_dim + 1 nonzero terms errs by at most
 //   eta_m (sum |terms|), eta_m = 2 (m + 1) u, u = 2^-24 (one rounding of at
 //   most 2u per addition, in any order; measured below 5u on gfx950).  Each
-//   lane owns 16 of the 32 rows of a block (its "group"); the group minimum
-//   of M minus a(g) b(x), with a(g) >= kappa max_{c in g} |c| and b(x) >= |x|,
+//   lane holds 16 of the 32 rows of a block: one "group" of 16 rows, or, for
+//   codebooks of up to 256 centroids, two groups of 8.  The group minimum of
+//   M minus a(g) b(x), with a(g) >= kappa max_{c in g} |c| and b(x) >= |x|,
 //   bounds every centroid of the group from below:
 //       L(g) <= s(c) = |c|^2/2 - x.c   for all c in g,
 //   and |x - c|^2 = |x|^2 + 2 s(c), so ranking by s is ranking by distance.
 //   Per sub-vector the lanes keep the smallest group bound m1, its group g1
-//   and the second smallest group bound m2.
-// Stage 2 (exact): the 16 rows of g1 are evaluated in the fixed fp32
-//   arithmetic above (8 rows on each lane of the pair that shares the
+//   and the second smallest group bound m2.  With 8-row groups (at most 16
+//   per lane) the index of g1 rides in the 4 low mantissa bits of the bound
+//   itself, so one min and one med3 keep all three: writing those bits moves
+//   a bound by less than 2^-19 of its magnitude plus 15 subnormal steps, and
+//   the bounds of this form are built with that much more slack (C shrunk
+//   and kappa grown by 2^-19 (1 + 2^-10) more, one more 2^-140 off C).
+// Stage 2 (exact): the rows of g1 are evaluated in the fixed fp32
+//   arithmetic above (8 or 4 rows on each lane of the pair that shares the
 //   sub-vector).  With D the smallest such distance, the oracle's winner c*
 //   satisfies s(c*) <= U = (D (1 + 2 gamma) - |x|^2_low) / 2, gamma = (sub_dim
 //   + 2) u (rounding bound of the fp32 distance), so its group's bound is
@@ -95,7 +101,23 @@ struct Consts {
   // the rounding of the constants themselves.
   static constexpr float kUA = 0.5f * (1.0f + kGamma2) * (1.0f + 8.0f * kU);
   static constexpr float kUB = 0.5f * (1.0f - (SD + 2) * kU) * (1.0f - 8.0f * kU);
+  // Small codebooks carry the group index in the 4 low bits of a bound,
+  // which moves it by at most 15 ulps: less than 2^-19 = 32 u of its
+  // magnitude for a normal bound, at most 15 2^-149 otherwise.  The bound is
+  // built with 32 u (1 + 2^-10) more relative slack in both C and kappa
+  // (which covers 32 u (1 + eta) of |C| + |x||c| + a'b', the largest the
+  // bound can be), and one more kTau of absolute slack in C.
+  static constexpr float kEtaIdx = kEta + 32.0f * kU * 1.0009765625f;
+  static constexpr float kKappaIdx = 1.125f * kEtaIdx;
+  static constexpr float kInvKappaIdxUp = (1.0f / kKappaIdx) * 1.0000152587890625f;
+  static constexpr float kHalfShrinkIdx = 0.5f * (1.0f - kEtaIdx - 9.5367431640625e-07f);
 };
+
+// Codebooks of up to kSmallMaxCentroids (8 blocks of 32 rows) use groups of
+// 8 rows and keep the group index in the bound itself (SMALL); larger ones
+// use groups of 16 rows and keep the index in a register of its own.
+constexpr int kSmallMaxCentroids = 256;
+constexpr uint32_t kIdxMask = 15u;  // 2 groups per block and lane, <= 8 blocks
 
 // Sub_dim 4 leaves K slots of the matrix-core dot empty; they carry C and
 // the error term instead ("folded").  Plain keys (K = 8): A = [-c, C_hi,
@@ -297,6 +319,17 @@ __device__ __forceinline__ float min16(const f32x16 &v) {
   return fminf(fminf(a, v[14]), v[15]);
 }
 
+// Minimum of the 8 values v[LO] .. v[LO + 7], at most FLT_MAX (an infinite
+// minimum, a group of marked rows only, becomes FLT_MAX: still a lower
+// bound, and finite, so that writing index bits into it cannot make a NaN).
+template <int LO>
+__device__ __forceinline__ float min8(const f32x16 &v) {
+  float a = __builtin_fminf(__builtin_fminf(v[LO], v[LO + 1]), kFltMax);
+  a = fminf(fminf(a, v[LO + 2]), v[LO + 3]);
+  a = fminf(fminf(a, v[LO + 4]), v[LO + 5]);
+  return fminf(fminf(a, v[LO + 6]), v[LO + 7]);
+}
+
 // The two lanes of a pair are l and l + 32 (h = 0, 1): they sit in the two
 // 32-lane halves of the wave.  v_permlane32_swap trades the upper half of one
 // register with the lower half of another on the VALU; with both operands
@@ -332,7 +365,8 @@ __device__ __forceinline__ float pair_sum(float v) {
 //                           padded (K = 8; lane half h reads halves 4h..4h+3);
 //   cval [n_cpad] float     C operand: shrunk |c|^2/2, +inf for padding and
 //                           duplicate rows;
-//   gan  [n_cpad/16] float  per 16-row group: kappa max |c| (rounded up);
+//   gan  [groups] float     per group (16 rows, or 8 when n_cpad <= 256):
+//                           kappa max |c| (rounded up);
 //   c32                     the centroids in fp32 (ROWS32 only), row r at
 //                           c32_offset(r): 16 bytes of padding after every
 //                           4 rows and after every 32, so that the rows the
@@ -355,7 +389,10 @@ struct Lds {
   uint32_t *hash;
   int *flags;
   float *scale;
-  static constexpr int gan_len(int n_cpad) { return (n_cpad / 16 + 3) & ~3; }
+  // (8-row groups only where n_cpad <= kSmallMaxCentroids)
+  static constexpr int gan_len(int n_cpad) {
+    return ((n_cpad <= kSmallMaxCentroids ? n_cpad / 8 : n_cpad / 16) + 3) & ~3;
+  }
   // floats of the c32 region, and the float offset of row r in it
   static constexpr int c32_len(int n_cpad) {
     return ROWS32 ? SD * n_cpad + 4 * (n_cpad / 4 + n_cpad / 32 + 1) : 0;
@@ -378,8 +415,15 @@ struct Lds {
   }
 };
 
-// Group (16 rows) of row r: block r/32, half ((r%32)/4)%2.
-__device__ __forceinline__ int group_of(int r) { return 2 * (r >> 5) + ((r >> 2) & 1); }
+// In the matrix-core result the lane of half hh holds rows 32 b + 8 j + 4 hh
+// + i (j, i = 0..3) of block b.  Group of row r = 32 b + 16 q + 8 j' + 4 hh
+// + i: 2 b + hh (16 rows: the lane's 16 values), or with SMALL 4 b + 2 q + hh
+// (8 rows: the lane's first 8 values, q = 0, or its last 8, q = 1).
+template <bool SMALL>
+__device__ __forceinline__ int group_of(int r) {
+  return SMALL ? 4 * (r >> 5) + 2 * ((r >> 4) & 1) + ((r >> 2) & 1)
+               : 2 * (r >> 5) + ((r >> 2) & 1);
+}
 
 // Row i (0..3) of the 4-row set starting at c0 (a multiple of 4) as fp32,
 // from the fp32 copy (the set is contiguous there) or widened from the
@@ -410,14 +454,17 @@ __device__ __forceinline__ void centroid(const Lds<SD, ROWS32> &s, int c, float 
   centroid_in_set<SD, BF16, ROWS32>(s, c & ~3, c & 3, v);
 }
 
-// Maximum over the 16 lanes that hold the rows of one group (lanes that agree
-// on bits 2 and 5 of the lane index: rows b*32 + 8j + 4hh + i, i, j = 0..3).
+// Maximum over the lanes that hold the rows of one group, where lane l of a
+// staging pass holds row base + l: the lanes that agree on bits 2 and 5 of
+// the lane index (16 rows), and on bit 4 too with SMALL (8 rows).
 // Non-negative floats order like their bit patterns.
+template <bool SMALL>
 __device__ __forceinline__ float group_max(float v) {
   int b = __float_as_int(v);
   b = max(b, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));   // lane ^ 1
   b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));   // lane ^ 2
   b = max(b, __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false));  // lane ^ 8
+  if constexpr (SMALL) return __int_as_float(b);
   const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);     // lane ^ 16
   return __int_as_float(max(static_cast<int>(r[0]), static_cast<int>(r[1])));
 }
@@ -426,7 +473,7 @@ __device__ __forceinline__ float group_max(float v) {
 // Returns true when some centroid has a non-finite or huge norm: then every
 // sub-vector of the slot takes the full exact scan.  One barrier, after the
 // rows are written; duplicate rows are marked after it.
-template <int SD, int NT, bool BF16, bool ROWS32, int BLOCK, bool FOLD, bool AROWS>
+template <int SD, int NT, bool BF16, bool ROWS32, int BLOCK, bool FOLD, bool AROWS, bool SMALL>
 __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_cpad,
                                const Lds<SD, ROWS32> &s, int hash_slots,
                                const float *__restrict__ scale, int scale_len, bool &fold_ok) {
@@ -463,13 +510,13 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
       if (!(n2c <= kNormCap)) {
         flag = 1;
       } else {
-        cv = n2c * K::kHalfShrink - 2.0f * kTau;
-        an = sqrt_up(n2c) * K::kKappa;
+        cv = SMALL ? n2c * K::kHalfShrinkIdx - 3.0f * kTau : n2c * K::kHalfShrink - 2.0f * kTau;
+        an = sqrt_up(n2c) * (SMALL ? K::kKappaIdx : K::kKappa);
       }
     }
-    an = group_max(an);
+    an = group_max<SMALL>(an);
     if (r < n_cpad) {
-      if ((lane & 0x1B) == 0) s.gan[group_of(r)] = an;
+      if ((lane & (SMALL ? 0x0B : 0x1B)) == 0) s.gan[group_of<SMALL>(r)] = an;
       if constexpr (FOLD) {  // halves 4, 5 carry C, half 6 carries -a' (SD == 4)
         // C beyond the element type: the slot takes the unfolded form, which
         // adds C in fp32 and multiplies these halves by 0, so they must be
@@ -597,6 +644,26 @@ __device__ __forceinline__ void exact8(const Lds<SD, ROWS32> &s, const float (&x
   for (int j = 6; j >= 0; --j) bk = (d[j] == best) ? (j & 3) + ((j & 4) << 1) : bk;
 }
 
+// The 4 rows c0 .. c0 + 3 (c0 a multiple of 4) that one lane evaluates in the
+// exact stage for an 8-row group.  best and bk are set as by exact8 (bk =
+// offset 0..3).
+template <int SD, bool BF16, bool ROWS32, bool MASK>
+__device__ __forceinline__ void exact_rows4(const Lds<SD, ROWS32> &s, const float (&xv)[SD], int c0,
+                                            int n_c, float &best, int &bk) {
+  float d[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float cv[SD];
+    centroid_in_set<SD, BF16, ROWS32>(s, c0, j, cv);
+    d[j] = sqdist<SD>(xv, cv);
+    if (MASK) d[j] = (c0 + j < n_c) ? d[j] : __builtin_inff();
+  }
+  best = __builtin_fminf(__builtin_fminf(__builtin_fminf(d[0], d[1]), d[2]), d[3]);
+  bk = 3;
+#pragma unroll
+  for (int j = 2; j >= 0; --j) bk = (d[j] == best) ? j : bk;
+}
+
 // Strict-< minimum of the exact distance over the 4 consecutive rows c0 ..
 // c0 + 3 (c0 a multiple of 4, c0 + 3 < n_cpad: padding rows are staged too),
 // visited in ascending order; the index recorded for row c0 + i is k0 + i.
@@ -617,14 +684,16 @@ __device__ __forceinline__ void exact4(const Lds<SD, ROWS32> &s, const float (&x
   }
 }
 
-// All 16 rows of group grp (rows b*32 + 8j + 4hh + i, grp = 2b + hh), in
-// ascending order, into (best, bi) by strict <.
-template <int SD, bool BF16, bool ROWS32>
+// All rows of group grp (see group_of), in ascending order, into (best, bi)
+// by strict <.
+template <int SD, bool BF16, bool ROWS32, bool SMALL>
 __device__ __forceinline__ void exact_group(const Lds<SD, ROWS32> &s, const float (&xv)[SD],
                                             int grp, int n_c, float &best, int &bi) {
-  const int r0 = (grp >> 1) * 32 + 4 * (grp & 1);
+  const int r0 = SMALL ? (grp >> 2) * 32 + ((grp >> 1) & 1) * 16 + 4 * (grp & 1)
+                       : (grp >> 1) * 32 + 4 * (grp & 1);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) exact4<SD, BF16, ROWS32, true>(s, xv, r0 + 8 * j, r0 + 8 * j, n_c, best, bi);
+  for (int j = 0; j < (SMALL ? 2 : 4); ++j)
+    exact4<SD, BF16, ROWS32, true>(s, xv, r0 + 8 * j, r0 + 8 * j, n_c, best, bi);
 }
 
 // Combine (distance, index) over the two lanes of a pair: smaller distance,
@@ -736,7 +805,7 @@ __device__ __forceinline__ void add_unit_sums(const UnitSums<SD, T> &us, int64_t
 
 // One unit: the wave encodes T columns of 32 sub-vectors, rows ubase ..
 // ubase + 32 T - 1 (raw words from load_unit_x).
-template <int SD, int T, bool BF16, bool ROWS32, bool SCALED, bool ACC, bool POW2>
+template <int SD, int T, bool BF16, bool ROWS32, bool SCALED, bool ACC, bool POW2, bool SMALL>
 __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t gend, int n_c,
                             int n_cpad, const Lds<SD, ROWS32> &s, bool exact_tile, bool fold,
                             const Smooth sm, int sub0, int code_bits, uint8_t *__restrict__ out,
@@ -753,7 +822,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
   float bn[T];   // upper bound of |x| (plus the split residual when smoothed)
   float nx2[T];  // plain keys: fp32 |x|^2 as the exact stage computes it
   float m1[T], m2[T];
-  int g1[T];
+  int g1[T];  // 16-row groups only; SMALL keeps the index in m1's low bits
   uint32_t codes[T];
   // smoothed keys: sub-slot of this lane's column 0 (sub0 = ubase mod n_sub)
   const int m0 = SCALED ? sub_mod<POW2>(sub0 + col, sm) : 0;
@@ -817,7 +886,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       const bool ex = !(nv2 <= kNormCap) || exact_tile;
       full_bits |= (ex ? 1u : 0u) << t;
       bn[t] = ex ? 0.0f
-                 : __builtin_fmaf(esum, K::kInvKappaUp, sqrt_up(nv2)) * kBnUp;
+                 : __builtin_fmaf(esum, SMALL ? K::kInvKappaIdxUp : K::kInvKappaUp, sqrt_up(nv2)) * kBnUp;
       // components 0 .. E-1 come from lane h = 0, E .. SD-1 from lane h = 1
       if constexpr (SD == 4) {
         // folded (K = 16): lane 0 of the pair holds [hi, lo], lane 1 the
@@ -888,12 +957,30 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
 
   // accumulator input of block blk: C from LDS, or zero when C is folded
   const f32x16 zero16 = {};
-  // lower bound of this lane's group of block blk for column t (recomputed)
-  auto group_bound = [&](int blk, int t) {
+  // lower bounds of this lane's groups of block blk for column t
+  // (recomputed): lo for group 2 blk + h, or with SMALL lo for 4 blk + h and
+  // hi for 4 blk + 2 + h
+  auto group_bounds = [&](int blk, int t, float &lo, float &hi) {
     const OpT aop = a_operand(blk);
-    if (kFold<SD, SCALED> && fold) return min16(mfma<BF16>(aop, bop[t], zero16));
-    const float an = s.gan[2 * blk + h];
-    return __builtin_fmaf(-an, bn[t], min16(mfma<BF16>(aop, bop[t], c_operand(blk))));
+    if constexpr (SMALL) {
+      if (kFold<SD, SCALED> && fold) {
+        const f32x16 a = mfma<BF16>(aop, bop[t], zero16);
+        lo = min8<0>(a);
+        hi = min8<8>(a);
+      } else {
+        const f32x16 a = mfma<BF16>(aop, bop[t], c_operand(blk));
+        lo = __builtin_fmaf(-s.gan[4 * blk + h], bn[t], min8<0>(a));
+        hi = __builtin_fmaf(-s.gan[4 * blk + 2 + h], bn[t], min8<8>(a));
+      }
+    } else {
+      hi = __builtin_inff();
+      if (kFold<SD, SCALED> && fold) {
+        lo = min16(mfma<BF16>(aop, bop[t], zero16));
+      } else {
+        lo = __builtin_fmaf(-s.gan[2 * blk + h], bn[t],
+                            min16(mfma<BF16>(aop, bop[t], c_operand(blk))));
+      }
+    }
   };
 
   // ---- stage 1: group lower bounds on the matrix cores ---------------------
@@ -903,23 +990,59 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
   // bound are loaded one block ahead.  Otherwise one accumulator is reused.
   auto stage1 = [&](auto folded) {
     constexpr bool F = decltype(folded)::value;
+    constexpr int kGpb = SMALL ? 4 : 2;  // groups per block
     OpT aop = a_operand(0);
-    float an = F ? 0.0f : s.gan[h];
+    float an0 = F ? 0.0f : s.gan[h];
+    float an1 = (F || !SMALL) ? 0.0f : s.gan[2 + h];
     for (int blk = 0; blk < nblk; ++blk) {
       const OpT a_cur = aop;
-      const float an_cur = an;
+      const float an0_cur = an0, an1_cur = an1;
       const f32x16 cop = F ? zero16 : c_operand(blk);
       if constexpr (F) {
         aop = a_operand(min(blk + 1, nblk - 1));
       } else if (blk + 1 < nblk) {
         aop = a_operand(blk + 1);
-        an = s.gan[2 * blk + 2 + h];
+        an0 = s.gan[kGpb * (blk + 1) + h];
+        if constexpr (SMALL) an1 = s.gan[kGpb * (blk + 1) + 2 + h];
       }
-      const int grp = 2 * blk + h;
+      // 16-row groups: group 2 blk + h, its index kept in g1
       auto track = [&](int t, float mb) {
         m2[t] = __builtin_amdgcn_fmed3f(m1[t], m2[t], mb);
-        g1[t] = (mb < m1[t]) ? grp : g1[t];
+        g1[t] = (mb < m1[t]) ? 2 * blk + h : g1[t];
         m1[t] = __builtin_amdgcn_fmed3f(m1[t], mb, kNegMax);
+      };
+      // 8-row groups: group 2 k + h with k = 2 blk + q, and k written into
+      // the 4 low bits of the bound (see Consts); equal keys then hold equal
+      // k, and min and med3 carry the index along with the bound
+      auto track_key = [&](int t, float mb, uint32_t k) {
+        const float key = __uint_as_float((__float_as_uint(mb) & ~kIdxMask) | k);
+        m2[t] = __builtin_amdgcn_fmed3f(m1[t], m2[t], key);
+        m1[t] = __builtin_amdgcn_fmed3f(m1[t], key, kNegMax);
+      };
+      // the bounds of this lane's groups from a product: lo (and hi, SMALL)
+      auto reduce = [&](int t, const f32x16 &a, float &lo, float &hi) {
+        if constexpr (SMALL) {
+          lo = min8<0>(a);
+          hi = min8<8>(a);
+          if constexpr (!F) {
+            lo = __builtin_fmaf(-an0_cur, bn[t], lo);
+            hi = __builtin_fmaf(-an1_cur, bn[t], hi);
+          }
+        } else {
+          lo = F ? min16(a) : __builtin_fmaf(-an0_cur, bn[t], min16(a));
+        }
+      };
+      // (the index of the upper group is made a scalar of its own: folded into
+      // the other's, it costs a second VALU instruction per key)
+      const uint32_t k_lo = 2u * blk;
+      const uint32_t k_hi = __builtin_amdgcn_readfirstlane(k_lo + 1u);
+      auto track_all = [&](int t, float lo, float hi) {
+        if constexpr (SMALL) {
+          track_key(t, lo, k_lo);
+          track_key(t, hi, k_hi);
+        } else {
+          track(t, lo);
+        }
       };
       if constexpr (F) {
         // the error term is in the product: the group minimum is the bound
@@ -928,14 +1051,17 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
         if constexpr (T > 1) acc[1] = mfma<BF16>(a_cur, bop[1], cop);
         unroll<T>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
-          const float mb = min16(acc[t & 1]);
+          float lo, hi;
+          reduce(t, acc[t & 1], lo, hi);
           if constexpr (t + 2 < T) acc[t & 1] = mfma<BF16>(a_cur, bop[t + 2], cop);
-          track(t, mb);
+          track_all(t, lo, hi);
         });
       } else {
         unroll<T>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
-          track(t, __builtin_fmaf(-an_cur, bn[t], min16(mfma<BF16>(a_cur, bop[t], cop))));
+          float lo, hi;
+          reduce(t, mfma<BF16>(a_cur, bop[t], cop), lo, hi);
+          track_all(t, lo, hi);
         });
       }
     }
@@ -977,24 +1103,46 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     // smallest of {a0, b0, a1, b1} is med3(a0, a1, min(b0, b1))
     const PairVals pa = pair_vals(__float_as_uint(m1[t]));
     const PairVals pb = pair_vals(__float_as_uint(m2[t]));
-    const PairVals pg = pair_vals(static_cast<uint32_t>(g1[t]));
     const float a0 = __uint_as_float(pa.first), a1 = __uint_as_float(pa.second);
-    const bool take1 = a1 < a0 || (a1 == a0 && static_cast<int>(pg.second) < static_cast<int>(pg.first));
-    const int cg1 = static_cast<int>(take1 ? pg.second : pg.first);
+    int cg1;
+    if constexpr (SMALL) {
+      // lane h's group is 2 k + h; equal keys hold equal k, and then lane
+      // 0's group is the lower one
+      const bool take1 = a1 < a0;
+      cg1 = take1 ? 2 * static_cast<int>(pa.second & kIdxMask) + 1
+                  : 2 * static_cast<int>(pa.first & kIdxMask);
+    } else {
+      const PairVals pg = pair_vals(static_cast<uint32_t>(g1[t]));
+      const bool take1 =
+          a1 < a0 || (a1 == a0 && static_cast<int>(pg.second) < static_cast<int>(pg.first));
+      cg1 = static_cast<int>(take1 ? pg.second : pg.first);
+    }
     const float cm2 = __builtin_amdgcn_fmed3f(
         a0, a1,
         __builtin_amdgcn_fmed3f(__uint_as_float(pb.first), __uint_as_float(pb.second), kNegMax));
-    // rows of group cg1 (block b, half hh): b*32 + 8j + 4hh + i; this lane
-    // takes j = 2h and 2h + 1 in ascending order, so every row of lane 0
-    // precedes every row of lane 1
+    // the rows of group cg1 (see group_of) split over the pair so that every
+    // row of lane 0 precedes every row of lane 1: 16-row groups, rows b*32 +
+    // 8j + 4hh + i with j = 2h, 2h + 1; 8-row groups, rows 32 b + 16 q + 8 h
+    // + 4 hh + i
     float best = __builtin_inff();
     int bk = 0;
-    if (n_c & 31) {  // uniform: the last block has padding rows
-      exact8<SD, BF16, ROWS32, true>(s, xv, cg1, h, n_c, best, bk);
+    int bi;
+    if constexpr (SMALL) {
+      const int c0 = (cg1 >> 2) * 32 + ((cg1 >> 1) & 1) * 16 + 8 * h + 4 * (cg1 & 1);
+      if (n_c & 31) {  // uniform: the last block has padding rows
+        exact_rows4<SD, BF16, ROWS32, true>(s, xv, c0, n_c, best, bk);
+      } else {
+        exact_rows4<SD, BF16, ROWS32, false>(s, xv, c0, n_c, best, bk);
+      }
+      bi = c0 + bk;
     } else {
-      exact8<SD, BF16, ROWS32, false>(s, xv, cg1, h, n_c, best, bk);
+      if (n_c & 31) {
+        exact8<SD, BF16, ROWS32, true>(s, xv, cg1, h, n_c, best, bk);
+      } else {
+        exact8<SD, BF16, ROWS32, false>(s, xv, cg1, h, n_c, best, bk);
+      }
+      bi = (cg1 >> 1) * 32 + 16 * h + 4 * (cg1 & 1) + bk;
     }
-    int bi = (cg1 >> 1) * 32 + 16 * h + 4 * (cg1 & 1) + bk;
     {
       const PairVals pd = pair_vals(__float_as_uint(best));
       const PairVals pi = pair_vals(static_cast<uint32_t>(bi));
@@ -1026,25 +1174,37 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     if (__any(amb)) {
       int q0 = -1, q1 = -1;
       bool over = false;
-      for (int blk = 0; blk < nblk; ++blk) {
-        const float mb = group_bound(blk, t);
-        const int grp = 2 * blk + h;
+      // this lane's groups of block blk, in ascending row order: 2 blk + h,
+      // or 4 blk + h and 4 blk + 2 + h
+      constexpr int kGpb = SMALL ? 4 : 2;
+      auto keep = [&](float mb, int grp) {
         if (amb && mb <= U) {
           over = over || q1 >= 0;
           q1 = (q0 >= 0 && q1 < 0) ? grp : q1;
           q0 = (q0 < 0) ? grp : q0;
         }
+      };
+      for (int blk = 0; blk < nblk; ++blk) {
+        float lo, hi;
+        group_bounds(blk, t, lo, hi);
+        keep(lo, kGpb * blk + h);
+        if constexpr (SMALL) keep(hi, kGpb * blk + 2 + h);
       }
       float fb = __builtin_inff();
       int fi = 0x7fffffff;
-      if (q0 >= 0) exact_group<SD, BF16, ROWS32>(s, xv, q0, n_c, fb, fi);
+      if (q0 >= 0) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, q0, n_c, fb, fi);
       if (__any(q1 >= 0)) {
-        if (q1 >= 0) exact_group<SD, BF16, ROWS32>(s, xv, q1, n_c, fb, fi);
+        if (q1 >= 0) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, q1, n_c, fb, fi);
       }
       if (__any(over)) {
         for (int blk = 0; blk < nblk; ++blk) {
-          const float mb = group_bound(blk, t);
-          if (over && mb <= U) exact_group<SD, BF16, ROWS32>(s, xv, 2 * blk + h, n_c, fb, fi);
+          float lo, hi;
+          group_bounds(blk, t, lo, hi);
+          if (over && lo <= U) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, kGpb * blk + h, n_c, fb, fi);
+          if constexpr (SMALL) {
+            if (over && hi <= U)
+              exact_group<SD, BF16, ROWS32, SMALL>(s, xv, kGpb * blk + 2 + h, n_c, fb, fi);
+          }
         }
       }
       pair_min(fb, fi, h);
@@ -1119,7 +1279,8 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
 // take units from a counter in LDS: a wave that runs ahead takes more units,
 // so all waves of the CU finish close together (the issue arbiter favours
 // the oldest waves, which would otherwise finish far ahead of the others).
-template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED, bool ACC, bool POW2>
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED, bool ACC, bool POW2,
+          bool SMALL>
 __global__ void __launch_bounds__(BLOCK, 1)
 encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ codebook,
                    int64_t n, int n_c, int64_t cb_stride, int64_t n_codebooks, int64_t group_len,
@@ -1186,7 +1347,7 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     if (!bad) {
       // its barrier also publishes the counter
       exact_tile = stage_codebook<SD, kTerms<SD, SCALED>, BF16, ROWS32, BLOCK, kFold<SD, SCALED>,
-                                  kARows>(
+                                  kARows, SMALL>(
           codebook + slot * cb_stride, n_c, n_cpad, s, hash_slots,
           (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len, fold);
     } else {
@@ -1219,10 +1380,10 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
                                      : static_cast<uint32_t>(rel % sm.n_sub);
             sub0 = mod_small(seg_sub0 + static_cast<int>(off), sm.n_sub, sm.inv_n_sub);
           }
-          encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, POW2>(
+          encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, POW2, SMALL>(
               xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, sub0, code_bits, out, us);
         } else {
-          encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, false>(
+          encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, false, SMALL>(
               xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, 0, code_bits, out, us);
         }
       }
@@ -1262,8 +1423,8 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
   } while (seg < u_last);
 }
 
-template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED, bool ACC = false,
-          bool POW2 = false>
+template <int SD, int T, int BLOCK, bool BF16, bool ROWS32, bool SCALED, bool ACC, bool POW2,
+          bool SMALL>
 hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_map, void *out,
                     const Layout &l, const Codes &codes, hipStream_t stream, int64_t cus,
                     const KmSums &acc = KmSums{nullptr, nullptr}) {
@@ -1278,7 +1439,9 @@ hipError_t launch_t(const void *x, const void *codebook, const int32_t *group_ma
   const size_t lds =
       Lds<SD, ROWS32>::bytes(n_cpad, hash_slots, SCALED ? codes.head_dim : 0, arows_len) +
       (ACC ? static_cast<size_t>(l.n_centroids) * (SD * 8 + 4) : 0);
-  auto kern = encode_mfma_kernel<SD, T, BLOCK, BF16, ROWS32, SCALED, ACC, POW2>;
+  static_assert(!SMALL || ROWS32, "small codebooks keep the fp32 rows");
+  if (SMALL && l.n_centroids > kSmallMaxCentroids) return hipErrorInvalidValue;
+  auto kern = encode_mfma_kernel<SD, T, BLOCK, BF16, ROWS32, SCALED, ACC, POW2, SMALL>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1329,9 +1492,12 @@ hipError_t launch_sd_p(const void *x, const void *codebook, const int32_t *group
                        const Layout &l, const Codes &codes, hipStream_t stream) {
   const int64_t cus = cu_count();
   if (l.n_centroids > kRows32MaxCentroids)
-    return launch_t<SD, columns<SD, SCALED, false>(), 1024, BF16, false, SCALED, false, POW2>(
+    return launch_t<SD, columns<SD, SCALED, false>(), 1024, BF16, false, SCALED, false, POW2, false>(
         x, codebook, group_map, out, l, codes, stream, cus);
-  return launch_t<SD, columns<SD, SCALED, true>(), 1024, BF16, true, SCALED, false, POW2>(
+  if (l.n_centroids > kSmallMaxCentroids)
+    return launch_t<SD, columns<SD, SCALED, true>(), 1024, BF16, true, SCALED, false, POW2, false>(
+        x, codebook, group_map, out, l, codes, stream, cus);
+  return launch_t<SD, columns<SD, SCALED, true>(), 1024, BF16, true, SCALED, false, POW2, true>(
       x, codebook, group_map, out, l, codes, stream, cus);
 }
 
@@ -1376,11 +1542,16 @@ hipError_t launch_encode_mfma_kmeans(const void *x, const void *codebook,
   static_assert(kKmFusedMaxCentroids <= kRows32MaxCentroids, "the sums follow the fp32 rows");
   const int64_t cus = cu_count();
   const Codes codes = plain_codes(l);
+  const bool small = l.n_centroids <= kSmallMaxCentroids;
   if (l.sub_dim == 4)
-    return launch_t<4, columns<4, false, true>(), 1024, false, true, false, true>(
-        x, codebook, group_map, out, l, codes, stream, cus, acc);
-  return launch_t<8, columns<8, false, true>(), 1024, false, true, false, true>(
-      x, codebook, group_map, out, l, codes, stream, cus, acc);
+    return small ? launch_t<4, columns<4, false, true>(), 1024, false, true, false, true, false, true>(
+                       x, codebook, group_map, out, l, codes, stream, cus, acc)
+                 : launch_t<4, columns<4, false, true>(), 1024, false, true, false, true, false, false>(
+                       x, codebook, group_map, out, l, codes, stream, cus, acc);
+  return small ? launch_t<8, columns<8, false, true>(), 1024, false, true, false, true, false, true>(
+                     x, codebook, group_map, out, l, codes, stream, cus, acc)
+               : launch_t<8, columns<8, false, true>(), 1024, false, true, false, true, false, false>(
+                     x, codebook, group_map, out, l, codes, stream, cus, acc);
 }
 
 int64_t encode_mfma_grid(const Layout &l) {

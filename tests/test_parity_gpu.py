@@ -177,13 +177,15 @@ def test_non_finite_values_odd_codebook(n_c):
     assert rep.equal == rep.rows
 
 
-@pytest.mark.parametrize("sd,dt", [(4, W.F16), (8, W.BF16)])
-def test_near_tied_centroids_across_groups(sd, dt):
-    # centroids in pairs one or two ulps apart, placed in different 16-row
-    # groups, and sub-vectors sitting between them: most columns are ambiguous
-    # after the matrix-core stage and must be resolved exactly
-    r = np.random.default_rng(38 + sd)
-    n_c = 512
+@pytest.mark.parametrize("sd,dt,n_c", [(4, W.F16, 512), (8, W.BF16, 512), (4, W.F16, 256),
+                                        (8, W.BF16, 256), (4, W.BF16, 200), (8, W.F16, 200)])
+def test_near_tied_centroids_across_groups(sd, dt, n_c):
+    # centroids in pairs one or two ulps apart, placed in different groups
+    # (16 rows; 8 rows, with the group index kept in the bound, at 256
+    # centroids or fewer, 200 with a padded last block), and sub-vectors
+    # sitting between them: most columns are ambiguous after the
+    # matrix-core stage and must be resolved exactly
+    r = np.random.default_rng(38 + sd + n_c)
     base = r.standard_normal((n_c // 2, sd))
     bits = W.to_f16_bits if dt == W.F16 else W.to_bf16_bits
     a = bits(base).reshape(-1, sd)
@@ -200,6 +202,30 @@ def test_near_tied_centroids_across_groups(sd, dt):
                     n_c * sd, 1, 20000)
     rep = assert_parity(wl, gpu_encode(wl))
     assert rep.equal == rep.rows
+
+
+@pytest.mark.parametrize("sd,dt,scale", [(4, W.F16, 1.0), (8, W.BF16, 1.0), (4, W.F16, 300.0),
+                                         (8, W.F16, 1.0)])
+def test_whole_groups_of_duplicate_rows(sd, dt, scale):
+    """A codebook whose rows 8.. repeat rows 0..7: every group but the first
+    holds only rows that can never win (marked at staging), so their bounds
+    are infinite before the group index is written into them; the 8-row
+    groups of small codebooks must keep such bounds finite and out of the
+    way.  scale 300 makes an fp16 slot take the unfolded form."""
+    r = np.random.default_rng(45 + sd)
+    n_c = 256
+    bits = W.to_f16_bits if dt == W.F16 else W.to_bf16_bits
+    head = bits(scale * r.standard_normal((8, sd))).reshape(-1, sd)
+    cb = np.tile(head, (n_c // 8, 1))
+    xf = W.bits_to_f32(head, dt).astype(np.float64)
+    x = xf[r.integers(0, 8, size=12000)] + 0.3 * scale * r.standard_normal((12000, sd))
+    wl = W.Workload("whole duplicate groups", bits(x).reshape(-1, sd), cb.reshape(-1), sd, n_c,
+                    dt, n_c * sd, 1, 12000)
+    print(f"[case] {wl.name} sd {sd} scale {scale}", flush=True)
+    got = gpu_encode(wl)
+    rep = assert_parity(wl, got)
+    assert rep.equal == rep.rows
+    assert int(got.max()) < 8, "a repeated row can never be the first minimum"
 
 
 @pytest.mark.parametrize("sd,scale,dups", [(4, 300.0, 0.0), (4, 150.0, 0.0), (8, 300.0, 0.0),

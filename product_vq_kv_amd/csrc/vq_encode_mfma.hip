@@ -367,7 +367,8 @@ __device__ __forceinline__ float pair_sum(float v) {
 //                           duplicate rows;
 //   gan  [groups] float     per group (16 rows, or 8 when n_cpad <= 256):
 //                           kappa max |c| (rounded up);
-//   c32                     the centroids in fp32 (ROWS32 only), row r at
+//   c32                     the centroids in fp32 (ROWS32 only; +inf in the
+//                           padding rows), row r at
 //                           c32_offset(r): 16 bytes of padding after every
 //                           4 rows and after every 32, so that the rows the
 //                           lanes of a wave read together in the exact stage
@@ -490,9 +491,11 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
   for (int base = wave * 64; base < n_cpad; base += BLOCK) {
     const int r = base + lane;
     uint16_t k8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // padding rows (r >= n_c) keep +inf in the fp32 copy: their exact
+    // distance is +inf, so the exact stage needs no row mask there
     float v[SD];
 #pragma unroll
-    for (int i = 0; i < SD; ++i) v[i] = 0.0f;
+    for (int i = 0; i < SD; ++i) v[i] = __builtin_inff();
     float cv = __builtin_inff();
     float an = 0.0f;
     if (r < n_c) {
@@ -552,6 +555,7 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
   int all = 0;
 #pragma unroll
   for (int w = 0; w < BLOCK / 64; ++w) all |= s.flags[w];
+  all = __builtin_amdgcn_readfirstlane(all);  // uniform: the flags live in scalar registers
   const bool exact = (all & 1) != 0;
   fold_ok = FOLD && (all & 2) == 0;
   if (!exact) {
@@ -602,7 +606,7 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
 // distance and the offset (0..3, 8..11) of its first row, the result of a
 // strict-< scan from (+inf, 0) whenever that minimum is finite.  With MASK,
 // rows >= n_c (the padding of the last block) are excluded; without it every
-// row is < n_c.
+// row is < n_c, or a padding row of the fp32 copy (exact distance +inf).
 template <int SD, bool BF16, bool ROWS32, bool MASK>
 __device__ __forceinline__ void exact8(const Lds<SD, ROWS32> &s, const float (&xv)[SD], int grp,
                                        int h, int n_c, float &best, int &bk) {
@@ -658,7 +662,10 @@ __device__ __forceinline__ void exact_rows4(const Lds<SD, ROWS32> &s, const floa
     d[j] = sqdist<SD>(xv, cv);
     if (MASK) d[j] = (c0 + j < n_c) ? d[j] : __builtin_inff();
   }
-  best = __builtin_fminf(__builtin_fminf(__builtin_fminf(d[0], d[1]), d[2]), d[3]);
+  // (distances are >= 0, +inf or NaN; a NaN sends the column to the full
+  // scan, and for the others med3 with -FLT_MAX is min without the NaN
+  // quieting copy)
+  best = __builtin_fminf(__builtin_fminf(__builtin_amdgcn_fmed3f(d[0], d[1], kNegMax), d[2]), d[3]);
   bk = 3;
 #pragma unroll
   for (int j = 2; j >= 0; --j) bk = (d[j] == best) ? j : bk;
@@ -693,7 +700,7 @@ __device__ __forceinline__ void exact_group(const Lds<SD, ROWS32> &s, const floa
                        : (grp >> 1) * 32 + 4 * (grp & 1);
 #pragma unroll
   for (int j = 0; j < (SMALL ? 2 : 4); ++j)
-    exact4<SD, BF16, ROWS32, true>(s, xv, r0 + 8 * j, r0 + 8 * j, n_c, best, bi);
+    exact4<SD, BF16, ROWS32, !ROWS32>(s, xv, r0 + 8 * j, r0 + 8 * j, n_c, best, bi);
 }
 
 // Combine (distance, index) over the two lanes of a pair: smaller distance,
@@ -816,6 +823,9 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
   const int h = lane >> 5;  // half of the block's rows / K slots this lane holds
   const int col = lane & 31;
   const int nblk = n_cpad / 32;
+  // the last block has padding rows (uniform); with the fp32 copy their
+  // exact distance is +inf and no mask is needed
+  const bool padded = !ROWS32 && __builtin_amdgcn_readfirstlane(n_c & 31) != 0;
 
   OpT bop[T];    // this lane's K slots of its column
   uint2 xw[T];   // smoothed keys: the raw words stage 2 rebuilds x~ from
@@ -1109,8 +1119,8 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       // lane h's group is 2 k + h; equal keys hold equal k, and then lane
       // 0's group is the lower one
       const bool take1 = a1 < a0;
-      cg1 = take1 ? 2 * static_cast<int>(pa.second & kIdxMask) + 1
-                  : 2 * static_cast<int>(pa.first & kIdxMask);
+      const uint32_t key = take1 ? pa.second : pa.first;
+      cg1 = 2 * static_cast<int>(key & kIdxMask) + (take1 ? 1 : 0);
     } else {
       const PairVals pg = pair_vals(static_cast<uint32_t>(g1[t]));
       const bool take1 =
@@ -1129,14 +1139,14 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     int bi;
     if constexpr (SMALL) {
       const int c0 = (cg1 >> 2) * 32 + ((cg1 >> 1) & 1) * 16 + 8 * h + 4 * (cg1 & 1);
-      if (n_c & 31) {  // uniform: the last block has padding rows
+      if (padded) {
         exact_rows4<SD, BF16, ROWS32, true>(s, xv, c0, n_c, best, bk);
       } else {
         exact_rows4<SD, BF16, ROWS32, false>(s, xv, c0, n_c, best, bk);
       }
       bi = c0 + bk;
     } else {
-      if (n_c & 31) {
+      if (padded) {
         exact8<SD, BF16, ROWS32, true>(s, xv, cg1, h, n_c, best, bk);
       } else {
         exact8<SD, BF16, ROWS32, false>(s, xv, cg1, h, n_c, best, bk);
@@ -1161,7 +1171,9 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     // s(c*) <= (best (1 + 2 gamma) - |x|^2) / 2 <= U
     const float U = __builtin_fmaf(best, K::kUA, __builtin_fmaf(n2x, -K::kUB, kTau));
     const bool full = ((full_bits >> t) & 1u) || !(best < __builtin_inff());
-    const bool amb = !full && !(cm2 > U);
+    // amb = !full && !(cm2 > U), as one compare: a column that is not full
+    // has finite U and a cm2 that is not NaN, and a NaN fails <=
+    const bool amb = (full ? __builtin_nanf("") : cm2) <= U;
     codes[t] = static_cast<uint32_t>(bi);
 
     // ambiguous: every group whose bound can reach U contains the oracle's
@@ -1171,7 +1183,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     // their own kept groups side by side.  A lane with more than two takes a
     // second pass over all of its qualifying groups, which come after the
     // kept two.
-    if (__any(amb)) {
+    if (__builtin_amdgcn_ballot_w64(amb) != 0) {
       int q0 = -1, q1 = -1;
       bool over = false;
       // this lane's groups of block blk, in ascending row order: 2 blk + h,
@@ -1184,12 +1196,14 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
           q0 = (q0 < 0) ? grp : q0;
         }
       };
-      for (int blk = 0; blk < nblk; ++blk) {
+      // (nblk >= 1: bottom-tested loops, whose entry needs no test)
+      int blk = 0;
+      do {
         float lo, hi;
         group_bounds(blk, t, lo, hi);
         keep(lo, kGpb * blk + h);
         if constexpr (SMALL) keep(hi, kGpb * blk + 2 + h);
-      }
+      } while (++blk < nblk);
       float fb = __builtin_inff();
       int fi = 0x7fffffff;
       if (q0 >= 0) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, q0, n_c, fb, fi);
@@ -1197,7 +1211,8 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
         if (q1 >= 0) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, q1, n_c, fb, fi);
       }
       if (__any(over)) {
-        for (int blk = 0; blk < nblk; ++blk) {
+        blk = 0;
+        do {
           float lo, hi;
           group_bounds(blk, t, lo, hi);
           if (over && lo <= U) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, kGpb * blk + h, n_c, fb, fi);
@@ -1205,14 +1220,14 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
             if (over && hi <= U)
               exact_group<SD, BF16, ROWS32, SMALL>(s, xv, kGpb * blk + 2 + h, n_c, fb, fi);
           }
-        }
+        } while (++blk < nblk);
       }
       pair_min(fb, fi, h);
       codes[t] = amb ? static_cast<uint32_t>(fi) : codes[t];
     }
     // non-finite or huge values (or no distance below +inf): full exact
     // strict-< scan, split by parity; index 0 when nothing beats +inf
-    if (__any(full)) {
+    if (__builtin_amdgcn_ballot_w64(full) != 0) {
       float fb = __builtin_inff();
       int fi = 0x7fffffff;
       // same trip count on both lanes of a pair; lane h takes rows r0 + h

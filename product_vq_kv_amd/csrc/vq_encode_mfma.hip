@@ -477,7 +477,8 @@ __device__ __forceinline__ float group_max(float v) {
 template <int SD, int NT, bool BF16, bool ROWS32, int BLOCK, bool FOLD, bool AROWS, bool SMALL>
 __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_cpad,
                                const Lds<SD, ROWS32> &s, int hash_slots,
-                               const float *__restrict__ scale, int scale_len, bool &fold_ok) {
+                               const float *__restrict__ scale, int scale_len, bool last_waves,
+                               bool &fold_ok) {
   using K = Consts<SD, NT>;
   constexpr uint32_t kEmpty = 0xFFFFFFFFu;
   const int tid = threadIdx.x;
@@ -487,8 +488,14 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
   for (int i = tid; i < scale_len; i += BLOCK) s.scale[i] = scale ? scale[i] : 1.0f;
   int flag = 0, nofold = 0;
   // whole waves per pass (n_cpad is a multiple of 32, so a group never
-  // straddles the end), which keeps the group maximum's lane exchanges uniform
-  for (int base = wave * 64; base < n_cpad; base += BLOCK) {
+  // straddles the end), which keeps the group maximum's lane exchanges
+  // uniform.  With fewer units than waves (last_waves) the last waves of
+  // the workgroup stage the rows and mark the duplicates below, so that the
+  // first waves, which take the units, start right after the barrier;
+  // otherwise the first waves do it (the issue arbiter favours them, and
+  // the last waves would end late).
+  const int rwave = last_waves ? BLOCK / 64 - 1 - wave : wave;
+  for (int base = rwave * 64; base < n_cpad; base += BLOCK) {
     const int r = base + lane;
     uint16_t k8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     // padding rows (r >= n_c) keep +inf in the fp32 copy: their exact
@@ -573,7 +580,7 @@ __device__ bool stage_codebook(const uint16_t *__restrict__ cb, int n_c, int n_c
     // rows' x, y words (all the comparisons read at sub_dim 4) are never
     // written.
     const uint32_t mask = static_cast<uint32_t>(hash_slots - 1);
-    for (int r = tid; r < n_c; r += BLOCK) {
+    for (int r = last_waves ? BLOCK - 1 - tid : tid; r < n_c; r += BLOCK) {
       const uint4 q = s.rows[r];
       const uint32_t hv = hash_row<SD>(q);
       const uint32_t key = ((hv >> 13) << 12) | static_cast<uint32_t>(r);
@@ -1178,49 +1185,65 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
 
     // ambiguous: every group whose bound can reach U contains the oracle's
     // winner if any does; those groups are recomputed exactly.  The bounds
-    // are recomputed on the matrix cores and each lane keeps the first two
-    // of its groups (its half of every block) that qualify; lanes evaluate
-    // their own kept groups side by side.  A lane with more than two takes a
-    // second pass over all of its qualifying groups, which come after the
-    // kept two.
+    // are recomputed on the matrix cores.  8-row groups: each lane marks its
+    // qualifying groups in a mask and evaluates them in ascending order.
+    // 16-row groups: each lane keeps the first two of its groups (its half
+    // of every block) that qualify; lanes evaluate their own kept groups side
+    // by side, and a lane with more than two takes a second pass over all of
+    // its qualifying groups, which come after the kept two.
     if (__builtin_amdgcn_ballot_w64(amb) != 0) {
-      int q0 = -1, q1 = -1;
-      bool over = false;
-      // this lane's groups of block blk, in ascending row order: 2 blk + h,
-      // or 4 blk + h and 4 blk + 2 + h
-      constexpr int kGpb = SMALL ? 4 : 2;
-      auto keep = [&](float mb, int grp) {
-        if (amb && mb <= U) {
-          over = over || q1 >= 0;
-          q1 = (q0 >= 0 && q1 < 0) ? grp : q1;
-          q0 = (q0 < 0) ? grp : q0;
-        }
-      };
-      // (nblk >= 1: bottom-tested loops, whose entry needs no test)
-      int blk = 0;
-      do {
-        float lo, hi;
-        group_bounds(blk, t, lo, hi);
-        keep(lo, kGpb * blk + h);
-        if constexpr (SMALL) keep(hi, kGpb * blk + 2 + h);
-      } while (++blk < nblk);
       float fb = __builtin_inff();
       int fi = 0x7fffffff;
-      if (q0 >= 0) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, q0, n_c, fb, fi);
-      if (__any(q1 >= 0)) {
-        if (q1 >= 0) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, q1, n_c, fb, fi);
-      }
-      if (__any(over)) {
-        blk = 0;
+      if constexpr (SMALL) {
+        // at most 16 groups per lane: bit k of qmask marks group 2 k + h
+        // (k = 2 blk + q, ascending rows); the blocks are unrolled so that
+        // their products issue back to back, and the lane then visits its
+        // qualifying groups in ascending order
+        uint32_t qmask = 0;
+        unroll<kSmallMaxCentroids / 32>([&](auto bc) {
+          constexpr int blk = decltype(bc)::value;
+          if (blk < nblk) {
+            float lo, hi;
+            group_bounds(blk, t, lo, hi);
+            qmask |= (amb && lo <= U) ? (1u << (2 * blk)) : 0u;
+            qmask |= (amb && hi <= U) ? (2u << (2 * blk)) : 0u;
+          }
+        });
+        while (qmask != 0) {
+          const int k = __builtin_ctz(qmask);
+          qmask &= qmask - 1;
+          exact_group<SD, BF16, ROWS32, SMALL>(s, xv, 2 * k + h, n_c, fb, fi);
+        }
+      } else {
+        int q0 = -1, q1 = -1;
+        bool over = false;
+        // this lane's groups of block blk, 2 blk + h, in ascending row order
+        auto keep = [&](float mb, int grp) {
+          if (amb && mb <= U) {
+            over = over || q1 >= 0;
+            q1 = (q0 >= 0 && q1 < 0) ? grp : q1;
+            q0 = (q0 < 0) ? grp : q0;
+          }
+        };
+        // (nblk >= 1: bottom-tested loops, whose entry needs no test)
+        int blk = 0;
         do {
           float lo, hi;
           group_bounds(blk, t, lo, hi);
-          if (over && lo <= U) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, kGpb * blk + h, n_c, fb, fi);
-          if constexpr (SMALL) {
-            if (over && hi <= U)
-              exact_group<SD, BF16, ROWS32, SMALL>(s, xv, kGpb * blk + 2 + h, n_c, fb, fi);
-          }
+          keep(lo, 2 * blk + h);
         } while (++blk < nblk);
+        if (q0 >= 0) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, q0, n_c, fb, fi);
+        if (__any(q1 >= 0)) {
+          if (q1 >= 0) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, q1, n_c, fb, fi);
+        }
+        if (__any(over)) {
+          blk = 0;
+          do {
+            float lo, hi;
+            group_bounds(blk, t, lo, hi);
+            if (over && lo <= U) exact_group<SD, BF16, ROWS32, SMALL>(s, xv, 2 * blk + h, n_c, fb, fi);
+          } while (++blk < nblk);
+        }
       }
       pair_min(fb, fi, h);
       codes[t] = amb ? static_cast<uint32_t>(fi) : codes[t];
@@ -1364,7 +1387,8 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
       exact_tile = stage_codebook<SD, kTerms<SD, SCALED>, BF16, ROWS32, BLOCK, kFold<SD, SCALED>,
                                   kARows, SMALL>(
           codebook + slot * cb_stride, n_c, n_cpad, s, hash_slots,
-          (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len, fold);
+          (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len,
+          units_per_wg < kWaves, fold);
     } else {
       __syncthreads();
     }

@@ -1536,6 +1536,15 @@ hipError_t launch_sd_p(const void *x, const void *codebook, const int32_t *group
   if (l.n_centroids > kSmallMaxCentroids)
     return launch_t<SD, columns<SD, SCALED, true>(), 1024, BF16, true, SCALED, false, POW2, false>(
         x, codebook, group_map, out, l, codes, stream, cus);
+  if constexpr (!SCALED) {
+    // fewer 4-column units than CUs: one column per unit, so that the work
+    // spreads over 4 times as many waves (a unit runs on one wave, alone on
+    // its CU, and its latency is the launch's)
+    const int64_t span = l.group_len < l.n ? l.group_len : l.n;
+    if ((span + 127) / 128 * l.n_groups < cus)
+      return launch_t<SD, 1, 1024, BF16, true, false, false, false, true>(
+          x, codebook, group_map, out, l, codes, stream, cus);
+  }
   return launch_t<SD, columns<SD, SCALED, true>(), 1024, BF16, true, SCALED, false, POW2, true>(
       x, codebook, group_map, out, l, codes, stream, cus);
 }
@@ -1594,9 +1603,9 @@ hipError_t launch_encode_mfma_kmeans(const void *x, const void *codebook,
 }
 
 int64_t encode_mfma_grid(const Layout &l) {
-  // upper bound on the workgroups of any plan above (one 64-row unit each)
+  // upper bound on the workgroups of any plan above (one 32-row unit each)
   const int64_t span = l.group_len < l.n ? l.group_len : l.n;
-  return (span + 63) / 64 * l.n_groups;
+  return (span + 31) / 32 * l.n_groups;
 }
 
 hipError_t launch_encode_mfma(const void *x, const void *codebook, const int32_t *group_map,

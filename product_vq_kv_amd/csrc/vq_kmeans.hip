@@ -12,25 +12,27 @@
 // fp16: every value is an integer multiple of 2^-24, so member sums are exact
 // int64 (|sum| < 2^40 * n).  Up to 512 centroids the encode itself adds every
 // sub-vector to its centroid's sums (fp64 LDS atomics, exact for the at most
-// 8192 rows a workgroup adds before it flushes, see vq_encode_mfma.hip);
-// otherwise km_accumulate reads the rows and codes back and adds them in LDS
-// with 64-bit integer atomics (or straight to global memory above 512
-// centroids).  Either way the per-workgroup sums are flushed with 64-bit
-// global atomics into one of kReplicas copies (fewer workgroups contend for
-// one address), which the update adds up.
+// 8192 rows a workgroup adds before it flushes, see vq_encode_mfma.hip).
 // bf16: every finite value is an integer multiple of 2^-133 below 2^261, so a
 // member sum is an integer below 2^285.  It is kept as kLimbs signed int64
 // limbs, limb j weighing 2^(32 j): a member whose value is m 2^p units (m <
-// 2^8) adds m 2^(p mod 32) < 2^39 to limb p / 32 with one 64-bit global
-// atomic, so a limb stays below 2^23 * 2^39 = 2^62 in magnitude for up to
-// 2^23 members (limbs carry past 32 bits).  The update propagates the carries
-// into one 320-bit integer and divides it by the count.
+// 2^8) adds m 2^(p mod 32) < 2^39 to limb p / 32, so a limb stays below
+// 2^23 * 2^39 = 2^62 in magnitude for up to 2^23 members (limbs carry past
+// 32 bits).  The update propagates the carries into one 320-bit integer and
+// divides it by the count.
+// Otherwise (bf16, or fp16 above 512 centroids) km_accumulate reads the rows
+// and codes back: a workgroup takes a tile of rows of one group and a range
+// of centroids whose sums fit in LDS, adds the members in that range with
+// 64-bit LDS atomics, and flushes the nonzero sums with 64-bit global atomics.
+// The flushes go into one of kReplicas copies (fewer workgroups contend for
+// one address), which the update adds up.
 // Integer addition is associative, so the result does not depend on the order
 // of the additions, and the rounding of sum / count is done exactly in
 // integer arithmetic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "vq_launch.h"
@@ -41,8 +43,9 @@ namespace {
 constexpr int kThreads = 256;        // update and clear workgroups
 constexpr int kAccThreads = 1024;    // accumulate workgroups
 constexpr int kRowsPerThread = 4;
-constexpr int kRowsPerTile = kAccThreads * kRowsPerThread;  // rows per accumulate workgroup
-constexpr int kLdsMaxCentroids = 512;   // beyond: accumulate straight to global
+constexpr int kRowsPerBatch = kAccThreads * kRowsPerThread;  // rows per accumulate round
+constexpr int64_t kAccMaxTileRows = 1 << 16;  // rows per accumulate workgroup at most
+constexpr size_t kAccLdsBytes = 144 * 1024;   // LDS of an accumulate workgroup at most
 constexpr int kReplicas = kKmReplicas;  // copies of the sums the flush is spread over
 constexpr int kLimbs = kKmBf16Limbs;    // int64 limbs (weight 2^(32 j)) of a bf16 member sum
 
@@ -139,137 +142,94 @@ struct KmArgs {
   int64_t n, cb_stride, n_codebooks, group_len, tiles_per_group;
   int sd, n_c;
   int limbs;  // 1 (fp16) or kLimbs (bf16) int64 words per (slot, centroid, component)
+  int64_t tile_rows;  // rows per accumulate workgroup (a multiple of kAccThreads * kRowsPerThread)
+  int range;          // centroids per accumulate workgroup (their sums fit in LDS)
 };
 
-// Member sums and counts of one tile of rows (one group, so one slot).
-template <int SD>
+// Member sums of one tile of rows (one group, so one slot) for one range of
+// centroids [c0, c0 + range), in LDS, then flushed.  A component with bits
+// (sign, exponent field E, fraction F) adds, for fp16, its exact value in
+// units of 2^-24 to its one word; for bf16 it is m 2^p units of 2^-133 with
+// m = 128 + F, p = E - 1 when E > 0 and m = F, p = 0 when E = 0, and m 2^(p
+// mod 32) goes to limb p / 32.  Non-finite components add 0.  A workgroup
+// adds at most kAccMaxTileRows rows, so an LDS word stays below 2^16 2^40 =
+// 2^56 (fp16) or 2^16 2^39 (bf16) in magnitude.
+template <int SD, bool BF16>
 __global__ void __launch_bounds__(kAccThreads) km_accumulate(const KmArgs a) {
-  extern __shared__ unsigned long long lsum[];  // [n_c][SD] then counts [n_c] (as u64)
+  constexpr int L = BF16 ? kLimbs : 1;   // words per (centroid, component)
+  extern __shared__ unsigned long long tab[];  // [range][SD][L], then counts [range] (u32)
   const int64_t tile = blockIdx.x;
   const int64_t g = tile / a.tiles_per_group;
   const int64_t gstart = g * a.group_len;
   const int64_t gend = min(gstart + a.group_len, a.n);
-  const int64_t tbase = gstart + (tile - g * a.tiles_per_group) * kRowsPerTile;
+  const int64_t tbase = gstart + (tile - g * a.tiles_per_group) * a.tile_rows;
   if (tbase >= gend) return;  // whole workgroup
   const int64_t slot = a.group_map ? static_cast<int64_t>(a.group_map[g]) : g;
   if (slot < 0 || slot >= a.n_codebooks) return;  // whole workgroup: no centroid to train
-  const int64_t tend = min(tbase + kRowsPerTile, gend);
-  const int64_t cells = a.n_codebooks * a.n_c;
-  const int rep = static_cast<int>(blockIdx.x % kReplicas);
-  unsigned long long *gs = a.sums + rep * cells * SD + slot * a.n_c * SD;
-  unsigned int *gc = a.counts + rep * cells + slot * a.n_c;
-  const bool use_lds = a.n_c <= kLdsMaxCentroids;
-  unsigned long long *lcnt = lsum + a.n_c * SD;
-  if (use_lds) {
-    for (int e = threadIdx.x; e < a.n_c * (SD + 1); e += kAccThreads) lsum[e] = 0;
-    __syncthreads();
-  }
-  // every load first (unconditional, from clamped rows), then the additions
+  const int64_t tend = min(tbase + a.tile_rows, gend);
+  const int c0 = static_cast<int>(blockIdx.y) * a.range;
+  const int nr = min(a.range, a.n_c - c0);  // centroids of this range (>= 1)
+  unsigned int *cnt = reinterpret_cast<unsigned int *>(tab + static_cast<int64_t>(a.range) * SD * L);
+  for (int e = threadIdx.x; e < nr * SD * L; e += kAccThreads) tab[e] = 0;
+  for (int e = threadIdx.x; e < nr; e += kAccThreads) cnt[e] = 0;
+  __syncthreads();
   using Row = std::conditional_t<SD == 4, uint2, uint4>;
-  uint32_t code[kRowsPerThread];
-  Row xr[kRowsPerThread];
+  const Row *xrows = reinterpret_cast<const Row *>(a.x);
+  for (int64_t b0 = tbase + threadIdx.x; b0 < tend; b0 += kAccThreads * kRowsPerThread) {
+    // every load of the batch first: the codes, then the rows (a row outside
+    // the range loads the tile's first row instead, one shared address)
+    uint32_t rel[kRowsPerThread];
+    Row xr[kRowsPerThread];
 #pragma unroll
-  for (int k = 0; k < kRowsPerThread; ++k) {
-    const int64_t r = min(tbase + threadIdx.x + k * kAccThreads, tend - 1);
-    code[k] = a.idx[r];
-    xr[k] = reinterpret_cast<const Row *>(a.x)[r];
-  }
-#pragma unroll
-  for (int k = 0; k < kRowsPerThread; ++k) {
-    const int64_t r = tbase + threadIdx.x + k * kAccThreads;
-    const uint32_t c = code[k];
-    if (r >= tend || c >= static_cast<uint32_t>(a.n_c)) continue;
-    uint32_t w[SD / 2];
-    if constexpr (SD == 4) {
-      w[0] = xr[k].x;
-      w[1] = xr[k].y;
-    } else {
-      w[0] = xr[k].x;
-      w[1] = xr[k].y;
-      w[2] = xr[k].z;
-      w[3] = xr[k].w;
+    for (int k = 0; k < kRowsPerThread; ++k) {
+      const int64_t r = min(b0 + static_cast<int64_t>(k) * kAccThreads, tend - 1);
+      rel[k] = a.idx[r] - static_cast<uint32_t>(c0);  // in range: < nr (unsigned)
     }
 #pragma unroll
-    for (int i = 0; i < SD; ++i) {
-      const uint16_t bits = static_cast<uint16_t>((i & 1) ? (w[i >> 1] >> 16) : w[i >> 1]);
-      const unsigned long long u = static_cast<unsigned long long>(units(bits));
-      if (use_lds) {
-        atomicAdd(&lsum[c * SD + i], u);
-      } else {
-        atomicAdd(&gs[c * SD + i], u);
+    for (int k = 0; k < kRowsPerThread; ++k) {
+      const int64_t r = b0 + static_cast<int64_t>(k) * kAccThreads;
+      const bool in = r < tend && rel[k] < static_cast<uint32_t>(nr);
+      xr[k] = xrows[in ? r : tbase];
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) {
+      const int64_t r = b0 + static_cast<int64_t>(k) * kAccThreads;
+      if (r >= tend || rel[k] >= static_cast<uint32_t>(nr)) continue;
+      uint32_t w[SD / 2];
+      w[0] = xr[k].x;
+      w[1] = xr[k].y;
+      if constexpr (SD == 8) {
+        w[2] = xr[k].z;
+        w[3] = xr[k].w;
       }
-    }
-    if (use_lds) {
-      atomicAdd(&lcnt[c], 1ull);
-    } else {
-      atomicAdd(&gc[c], 1u);
+      unsigned long long *t = tab + static_cast<int64_t>(rel[k]) * SD * L;
+#pragma unroll
+      for (int i = 0; i < SD; ++i) {
+        const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
+        if constexpr (BF16) {
+          const uint32_t E = (bits >> 7) & 0xFFu, F = bits & 0x7Fu;
+          const uint32_t m = (E == 0) ? F : (128u | F);
+          if (E == 255u || m == 0) continue;  // non-finite adds 0
+          const uint32_t p = (E == 0) ? 0u : E - 1u;
+          const uint64_t v = static_cast<uint64_t>(m) << (p & 31u);
+          atomicAdd(t + i * L + (p >> 5), (bits & 0x8000u) ? 0ull - v : v);
+        } else {
+          const unsigned long long u = static_cast<unsigned long long>(units(static_cast<uint16_t>(bits)));
+          if (u) atomicAdd(t + i, u);
+        }
+      }
+      atomicAdd(cnt + rel[k], 1u);
     }
   }
-  if (use_lds) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < a.n_c * SD; e += kAccThreads)
-      if (lsum[e]) atomicAdd(&gs[e], lsum[e]);
-    for (int c = threadIdx.x; c < a.n_c; c += kAccThreads)
-      if (lcnt[c]) atomicAdd(&gc[c], static_cast<unsigned int>(lcnt[c]));
-  }
-}
-
-// bf16 member sums of one tile of rows (one group, so one slot), straight to
-// the global limbs: component bits (sign, exponent field E, fraction F) are
-// m 2^p units of 2^-133 with m = 128 + F, p = E - 1 when E > 0 and m = F,
-// p = 0 when E = 0; m 2^(p mod 32) goes to limb p / 32.
-template <int SD>
-__global__ void __launch_bounds__(kAccThreads) km_accumulate_bf16(const KmArgs a) {
-  const int64_t tile = blockIdx.x;
-  const int64_t g = tile / a.tiles_per_group;
-  const int64_t gstart = g * a.group_len;
-  const int64_t gend = min(gstart + a.group_len, a.n);
-  const int64_t tbase = gstart + (tile - g * a.tiles_per_group) * kRowsPerTile;
-  if (tbase >= gend) return;  // whole workgroup
-  const int64_t slot = a.group_map ? static_cast<int64_t>(a.group_map[g]) : g;
-  if (slot < 0 || slot >= a.n_codebooks) return;  // whole workgroup: no centroid to train
-  const int64_t tend = min(tbase + kRowsPerTile, gend);
+  __syncthreads();
   const int64_t cells = a.n_codebooks * a.n_c;
   const int rep = static_cast<int>(blockIdx.x % kReplicas);
-  unsigned long long *gs = a.sums + (rep * cells + slot * a.n_c) * SD * kLimbs;
-  unsigned int *gc = a.counts + rep * cells + slot * a.n_c;
-  using Row = std::conditional_t<SD == 4, uint2, uint4>;
-  uint32_t code[kRowsPerThread];
-  Row xr[kRowsPerThread];
-#pragma unroll
-  for (int k = 0; k < kRowsPerThread; ++k) {
-    const int64_t r = min(tbase + threadIdx.x + k * kAccThreads, tend - 1);
-    code[k] = a.idx[r];
-    xr[k] = reinterpret_cast<const Row *>(a.x)[r];
-  }
-#pragma unroll
-  for (int k = 0; k < kRowsPerThread; ++k) {
-    const int64_t r = tbase + threadIdx.x + k * kAccThreads;
-    const uint32_t c = code[k];
-    if (r >= tend || c >= static_cast<uint32_t>(a.n_c)) continue;
-    uint32_t w[SD / 2];
-    if constexpr (SD == 4) {
-      w[0] = xr[k].x;
-      w[1] = xr[k].y;
-    } else {
-      w[0] = xr[k].x;
-      w[1] = xr[k].y;
-      w[2] = xr[k].z;
-      w[3] = xr[k].w;
-    }
-#pragma unroll
-    for (int i = 0; i < SD; ++i) {
-      const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-      const uint32_t E = (bits >> 7) & 0xFFu, F = bits & 0x7Fu;
-      const uint32_t m = (E == 0) ? F : (128u | F);
-      if (E == 255u || m == 0) continue;  // non-finite adds 0
-      const uint32_t p = (E == 0) ? 0u : E - 1u;
-      const uint64_t v = static_cast<uint64_t>(m) << (p & 31u);
-      const bool neg = (bits & 0x8000u) != 0;
-      atomicAdd(gs + (static_cast<int64_t>(c) * SD + i) * kLimbs + (p >> 5), neg ? 0ull - v : v);
-    }
-    atomicAdd(&gc[c], 1u);
-  }
+  unsigned long long *gs = a.sums + ((rep * cells + slot * a.n_c + c0) * SD) * L;
+  unsigned int *gc = a.counts + rep * cells + slot * a.n_c + c0;
+  for (int e = threadIdx.x; e < nr * SD * L; e += kAccThreads)
+    if (tab[e]) atomicAdd(gs + e, tab[e]);
+  for (int e = threadIdx.x; e < nr; e += kAccThreads)
+    if (cnt[e]) atomicAdd(gc + e, cnt[e]);
 }
 
 // New bf16 centroids from the limbs, one thread per (slot, centroid,
@@ -372,6 +332,35 @@ __global__ void __launch_bounds__(kThreads) km_clear(const KmArgs a) {
   if (e < nc) a.counts[e] = 0;
 }
 
+// LDS of an accumulate workgroup: the sums of `range` centroids, then their
+// counts.
+size_t acc_lds_bytes(int sd, int limbs, int range) {
+  return static_cast<size_t>(range) * (sd * limbs * sizeof(unsigned long long) + sizeof(unsigned int));
+}
+
+// Centroids per accumulate workgroup: all of them when their sums fit, else
+// the largest power of two that does.
+int acc_range(int sd, int limbs, int n_c) {
+  if (acc_lds_bytes(sd, limbs, n_c) <= kAccLdsBytes) return n_c;
+  int r = 1;
+  while (acc_lds_bytes(sd, limbs, 2 * r) <= kAccLdsBytes) r *= 2;
+  return r;
+}
+
+// Rows per accumulate workgroup: about one workgroup per CU over all tiles
+// and ranges, in whole rounds of kRowsPerBatch, at most kAccMaxTileRows.
+int64_t acc_tile_rows(int64_t span, int64_t n_groups, int ranges) {
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t target = (span * n_groups * ranges + cus - 1) / cus;
+  int64_t rows = (target + kRowsPerBatch - 1) / kRowsPerBatch * kRowsPerBatch;
+  const int64_t span_rounded = (span + kRowsPerBatch - 1) / kRowsPerBatch * kRowsPerBatch;
+  rows = std::min(rows, std::min(kAccMaxTileRows, span_rounded));
+  return std::max<int64_t>(rows, kRowsPerBatch);
+}
+
 template <int SD>
 hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream_t stream) {
   const int64_t cells = a.n_codebooks * a.n_c;
@@ -381,9 +370,15 @@ hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t tiles = a.tiles_per_group * ((a.n + a.group_len - 1) / a.group_len);
-  const size_t lds = a.n_c <= kLdsMaxCentroids
-                         ? static_cast<size_t>(a.n_c) * (SD + 1) * sizeof(unsigned long long)
-                         : 0;
+  const int ranges = (a.n_c + a.range - 1) / a.range;
+  const dim3 acc_grid(static_cast<uint32_t>(tiles), static_cast<uint32_t>(ranges));
+  const size_t lds = acc_lds_bytes(SD, a.limbs, a.range);
+  auto acc = l.bf16 ? km_accumulate<SD, true> : km_accumulate<SD, false>;
+  if (lds > 65536) {
+    err = hipFuncSetAttribute(reinterpret_cast<const void *>(acc),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (err != hipSuccess) return err;
+  }
   const int64_t upd_blocks = (cells * SD + kThreads - 1) / kThreads;
   if (l.bf16) {
     for (int it = 0; it < iterations; ++it) {
@@ -393,8 +388,7 @@ hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream
                 : launch_encode(a.x, a.codebook, a.group_map, const_cast<uint32_t *>(a.idx), l,
                                 plain_codes(l), stream);
       if (err != hipSuccess) return err;
-      hipLaunchKernelGGL(km_accumulate_bf16<SD>, dim3(static_cast<uint32_t>(tiles)),
-                         dim3(kAccThreads), 0, stream, a);
+      hipLaunchKernelGGL(acc, acc_grid, dim3(kAccThreads), lds, stream, a);
       err = hipGetLastError();
       if (err != hipSuccess) return err;
       hipLaunchKernelGGL(km_update_bf16<SD>, dim3(static_cast<uint32_t>(upd_blocks)),
@@ -423,8 +417,7 @@ hipError_t launch_km(const KmArgs &a, const Layout &l, int iterations, hipStream
               : launch_encode(a.x, a.codebook, a.group_map, const_cast<uint32_t *>(a.idx), l,
                               plain_codes(l), stream);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(km_accumulate<SD>, dim3(static_cast<uint32_t>(tiles)), dim3(kAccThreads),
-                       lds, stream, a);
+    hipLaunchKernelGGL(acc, acc_grid, dim3(kAccThreads), lds, stream, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(km_update<SD>, dim3(static_cast<uint32_t>(upd_blocks)), dim3(kThreads), 0,
@@ -450,8 +443,10 @@ size_t kmeans_workspace_bytes(int sub_dim, int n_centroids, int64_t n_codebooks,
 }
 
 int64_t kmeans_grid(const Layout &l) {
+  // upper bound on the accumulate workgroups along x (tiles of at least
+  // kRowsPerBatch rows)
   const int64_t span = l.group_len < l.n ? l.group_len : l.n;
-  return (span + kRowsPerTile - 1) / kRowsPerTile * l.n_groups;
+  return (span + kRowsPerBatch - 1) / kRowsPerBatch * l.n_groups;
 }
 
 hipError_t launch_kmeans(const void *x, void *codebook, const int32_t *group_map, uint32_t *out_idx,
@@ -470,9 +465,11 @@ hipError_t launch_kmeans(const void *x, void *codebook, const int32_t *group_map
   a.n_codebooks = l.n_codebooks;
   a.group_len = l.group_len;
   const int64_t span = l.group_len < l.n ? l.group_len : l.n;
-  a.tiles_per_group = (span + kRowsPerTile - 1) / kRowsPerTile;
   a.sd = l.sub_dim;
   a.n_c = l.n_centroids;
+  a.range = acc_range(l.sub_dim, a.limbs, l.n_centroids);
+  a.tile_rows = acc_tile_rows(span, l.n_groups, (l.n_centroids + a.range - 1) / a.range);
+  a.tiles_per_group = (span + a.tile_rows - 1) / a.tile_rows;
   return l.sub_dim == 4 ? launch_km<4>(a, l, iterations, stream)
                         : launch_km<8>(a, l, iterations, stream);
 }

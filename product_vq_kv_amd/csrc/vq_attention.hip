@@ -105,6 +105,7 @@ struct AttnArgs {
   float *ws;                // [B][Hq][n_chunks][D + 2]
   float *out;               // [B][Hq][D]
   int B, Hq, Hkv, D, S, n_c, window, n_chunks;
+  int n_wg;                 // workgroups of the streaming partial launch
   float qmul;               // softmax_scale * log2(e)
 };
 
@@ -854,28 +855,25 @@ attn_mfma_partial(const AttnArgs a) {
   }
 }
 
-// Merge the chunk partials of one (sequence, query head): thread d.  Chunks
-// are taken 16 at a time: lanes 0..15 load their (m, l) pairs and the
-// threads their 16 o values, every load in flight (clamped indices); each
-// batch is merged against the running maximum.  An empty chunk has m = -inf
-// (weight 0), l = 0 and o = 0.
-__global__ void __launch_bounds__(kThreads)
-attn_combine(const AttnArgs a) {
+// Merge `count` partials of one (sequence, query head), `cstride` floats
+// apart: thread d.  Partials are taken 16 at a time: lanes 0..15 load their
+// (m, l) pairs and the threads their 16 o values, every load in flight
+// (clamped indices); each batch is merged against the running maximum.  An
+// empty partial has m = -inf (weight 0), l = 0 and o = 0.
+__device__ __forceinline__ void merge_partials(const float *part, int count, int64_t cstride,
+                                               int D, float *out) {
   constexpr int kBatch = 16;
   __shared__ float bm[kBatch], bl[kBatch];
-  const int bh = blockIdx.x;
-  const int D = a.D, d = threadIdx.x, dc = min(d, D - 1);
-  const int64_t part_stride = D + 2;
-  const float *part = a.ws + static_cast<int64_t>(bh) * a.n_chunks * part_stride;
+  const int d = threadIdx.x, dc = min(d, D - 1);
   float M = kNegInf, l = 0.0f, acc = 0.0f;
-  for (int c0 = 0; c0 < a.n_chunks; c0 += kBatch) {  // uniform
+  for (int c0 = 0; c0 < count; c0 += kBatch) {  // uniform
     float oc[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) oc[j] = part[min(c0 + j, a.n_chunks - 1) * part_stride + dc];
+    for (int j = 0; j < kBatch; ++j) oc[j] = part[min(c0 + j, count - 1) * cstride + dc];
     if (d < kBatch) {
-      const float *pc = part + min(c0 + d, a.n_chunks - 1) * part_stride;
+      const float *pc = part + min(c0 + d, count - 1) * cstride;
       const float mj = pc[D], lj = pc[D + 1];
-      bm[d] = c0 + d < a.n_chunks ? mj : kNegInf;
+      bm[d] = c0 + d < count ? mj : kNegInf;
       bl[d] = lj;
     }
     __syncthreads();
@@ -902,7 +900,630 @@ attn_combine(const AttnArgs a) {
       M = Mb;
     }
   }
-  if (d < D) a.out[static_cast<int64_t>(bh) * D + d] = M == kNegInf ? 0.0f : acc / l;
+  if (d < D) out[d] = M == kNegInf ? 0.0f : acc / l;
+}
+
+// Merge of the chunked form: the n_chunks partials of (sequence, query head)
+// blockIdx.x.
+__global__ void __launch_bounds__(kThreads)
+attn_combine(const AttnArgs a) {
+  const int bh = blockIdx.x;
+  const int64_t part_stride = a.D + 2;
+  merge_partials(a.ws + static_cast<int64_t>(bh) * a.n_chunks * part_stride, a.n_chunks,
+                 part_stride, a.D, a.out + static_cast<int64_t>(bh) * a.D);
+}
+
+// ---- streaming form (matrix cores, balanced token ranges) -----------------
+// The chunked form above gives every (sequence, kv head, 256-token chunk) a
+// workgroup of its own: all of them are resident at once, so their loads,
+// scores, softmax and value sums run in lockstep, and each writes a partial.
+// Here the attended tokens of all (sequence, kv head) segments are cut into
+// 64-token slices, laid end to end in (sequence, kv head, slice) order, and
+// workgroup i of G takes slices [U i / G, U (i+1) / G) of the U in total
+// (every workgroup reads the lengths and finds its range itself).  A
+// workgroup works through the segment parts in its range; for each it stages
+// the codebooks and the split query rows once, then its 4 waves take the
+// part's slices in turn, each with a running softmax of its own (running
+// maximum and sum per head, value sums rescaled when the maximum rises), the
+// next slice's key codes (registers) and value codes (LDS, asynchronous)
+// in flight while the current one is computed, and no barrier between
+// slices.  At the end of a part the waves merge through LDS and write one
+// partial per head into slot i + sigma (sigma = b Hkv + h: the slots of the
+// (workgroup, segment) pairs along the range increase strictly, so they are
+// distinct); the first and the last workgroup of each segment are recorded
+// for the merge launch.  The arithmetic per slice is that of the chunked
+// form: the query split exactly into element-type parts, scores
+// and value sums on v_mfma_f32_16x16x32, weights p 2^14 split the same way.
+constexpr int kSlice = 64;        // tokens per wave step
+// Fourth word of a raw buffer resource on this target (untyped 32-bit data).
+constexpr int kBufferWord3 = 0x00020000;
+// Workgroups per CU the registers are budgeted for: 3, or 2 when the value
+// sums take more than 8 accumulator blocks (bf16 or 8 heads per kv head at
+// head_dim 256).
+template <bool BF16, int D, int GC>
+constexpr int kStreamPerCu = ((BF16 ? 4 : 2) * GC * 4 + 15) / 16 * (D / 64) > 8 ? 2 : 3;
+
+// Attended slices of sequence b: tokens [first, L).
+__device__ __forceinline__ int seq_slices(const AttnArgs &a, int b, int &first, int &L) {
+  int len = a.kv_len ? a.kv_len[b] : a.S;
+  len = min(max(len, 0), a.S);
+  first = a.window > 0 ? max(0, len - a.window) : 0;
+  L = len;
+  return (len - first + kSlice - 1) / kSlice;
+}
+
+// Inclusive prefix sum of v over the workgroup (kThreads threads); `total`
+// gets the sum of all.  `sc` holds kThreads / 64 words of LDS.
+__device__ __forceinline__ int64_t block_scan(int64_t v, int64_t *sc, int64_t &total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) sc[w] = v;
+  __syncthreads();
+  int64_t off = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < kThreads / 64; ++k) {
+    off += k < w ? sc[k] : 0;
+    total += sc[k];
+  }
+  __syncthreads();  // sc is refilled by the next call
+  return v + off;
+}
+
+// Waits until every LDS operation of the wave has completed.
+__device__ __forceinline__ void wait_lgkm_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int SDK, int SDV, bool BF16, int D, int GC>
+__global__ void __launch_bounds__(kThreads, (kStreamPerCu<BF16, D, GC>))
+attn_stream_partial(const AttnArgs a) {
+  constexpr int NSK = D / SDK, NSV = D / SDV;
+  constexpr int QB = NSK / 4;          // key-code bytes per lane quarter (4, 8 or 16)
+  constexpr int NQW = QB / 4;          // their 32-bit words
+  constexpr int NI = D / 32;           // score instructions per 16 tokens
+  constexpr int P = BF16 ? 4 : 2;      // element-type parts of a split fp32 value
+  constexpr int HPL = 4 / P;           // heads per lane in the score layout
+  constexpr int NR = GC * P;           // rows (head, part) at most
+  constexpr int ZR = NR;               // the all-zero row
+  constexpr int VP = NSV / 16;         // 16-byte pieces per value-code row
+  constexpr int NCG = NSV / 16;        // 16-sub-space column groups of the value sum
+  constexpr int NRB = (NR * 4 + 15) / 16;  // 16-row blocks (head, part, element)
+  constexpr int CB = kSlice * NSV;     // value-code bytes of one slice
+  constexpr int QS = D + 8;            // row stride of the query parts (halves)
+  constexpr int PS = kSlice + 8;       // row stride of the weights (halves)
+  constexpr float kPScale = 16384.0f;  // weights in (0, 1] are split as p 2^14
+  static_assert(SDV == 4 && QB % 4 == 0 && NSV % 16 == 0 && NR <= 16, "shape");
+
+  __shared__ uint4 ktab_s[256 * SDK / 8];         // key codebook, element bits
+  __shared__ uint4 vtab_s[256 * SDV / 8];         // value codebook, element bits
+  __shared__ uint4 qrow_s[(NR + 1) * QS / 8];     // query parts, rows (head, part); zero row
+  __shared__ uint4 prow_s[4][(NR + 1) * PS / 8];  // per wave: weights, rows (head, part); zero row
+  __shared__ uint4 vbuf_s[4][CB / 16];            // per wave: value codes of the next slice
+  __shared__ float red[3 * GC * D];               // waves 1..3: scaled value sums
+  __shared__ float wm[4][GC], wl[4][GC];          // per wave: running maximum, sum
+  __shared__ float walpha[4][GC];                 // per wave: rescale factors
+  __shared__ int qexp[GC];                        // E of each head
+  __shared__ int64_t scan_s[kThreads / 64];
+  __shared__ int found_b, found_first, found_len;
+  __shared__ int64_t found_seq0;
+
+  const int g = a.Hq / a.Hkv;
+  const int nrows = g * P;             // rows (head, part) in use
+  const int wg = blockIdx.x, G = gridDim.x;
+  uint16_t *ktab = reinterpret_cast<uint16_t *>(ktab_s);
+  uint16_t *vtab = reinterpret_cast<uint16_t *>(vtab_s);
+  uint16_t *qp = reinterpret_cast<uint16_t *>(qrow_s);
+
+  // the zero rows (read for the rows past g P of the matrix operands)
+  for (int e = NR * QS / 8 + threadIdx.x; e < (NR + 1) * QS / 8; e += kThreads)
+    qrow_s[e] = make_uint4(0, 0, 0, 0);
+  for (int e = NR * PS / 8 + (threadIdx.x & 63); e < (NR + 1) * PS / 8; e += 64)
+    prow_s[threadIdx.x >> 6][e] = make_uint4(0, 0, 0, 0);
+
+  // ---- this workgroup's slice range --------------------------------------
+  // (one pass over the lengths when they fit one round of threads: the
+  // prefix sums that give the total also locate s_begin)
+  int64_t U, s_begin, s_end;
+  if (threadIdx.x == 0) {
+    found_b = a.B;  // (not found: no part runs)
+    found_seq0 = 0;
+    found_first = found_len = 0;
+  }
+  if (a.B <= kThreads) {
+    const int bb = threadIdx.x;
+    int f = 0, L = 0;
+    const int64_t v = bb < a.B ? seq_slices(a, bb, f, L) : 0;
+    int64_t tot;
+    const int64_t incl = block_scan(v, scan_s, tot);
+    U = tot * a.Hkv;
+    s_begin = U * wg / G;
+    s_end = U * (wg + 1) / G;
+    if (s_begin >= s_end) return;  // uniform
+    const int64_t lo = (incl - v) * a.Hkv, hi = incl * a.Hkv;
+    if (v > 0 && lo <= s_begin && s_begin < hi) {
+      found_b = bb;
+      found_seq0 = lo;
+      found_first = f;
+      found_len = L;
+    }
+    __syncthreads();
+  } else {
+    int64_t mine = 0;
+    for (int b = threadIdx.x; b < a.B; b += kThreads) {
+      int f, L;
+      mine += seq_slices(a, b, f, L);
+    }
+    (void)block_scan(mine, scan_s, U);
+    U *= a.Hkv;
+    s_begin = U * wg / G;
+    s_end = U * (wg + 1) / G;
+    if (s_begin >= s_end) return;  // uniform
+    int64_t run = 0;
+    for (int base = 0; base < a.B; base += kThreads) {  // uniform
+      const int bb = base + static_cast<int>(threadIdx.x);
+      int f = 0, L = 0;
+      const int64_t v = bb < a.B ? static_cast<int64_t>(a.Hkv) * seq_slices(a, bb, f, L) : 0;
+      int64_t tot;
+      const int64_t incl = block_scan(v, scan_s, tot);
+      if (v > 0 && run + incl - v <= s_begin && s_begin < run + incl) {
+        found_b = bb;
+        found_seq0 = run + incl - v;
+        found_first = f;
+        found_len = L;
+      }
+      run += tot;
+      __syncthreads();
+      if (run > s_begin) break;
+    }
+  }
+  // uniform values (scalar registers): the part loop and the buffer
+  // resources derived from them are the same for every lane
+  int b = __builtin_amdgcn_readfirstlane(found_b);
+  const int b_found = b;
+  const int first_found = __builtin_amdgcn_readfirstlane(found_first);
+  const int len_found = __builtin_amdgcn_readfirstlane(found_len);
+  int64_t seq0;
+  {
+    const uint64_t s0 = static_cast<uint64_t>(found_seq0);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(s0));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(s0 >> 32));
+    seq0 = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+  }
+  int *tab_first = reinterpret_cast<int *>(
+      a.ws + static_cast<int64_t>(G + a.B * a.Hkv - 1) * g * (D + 2));
+  int *tab_last = tab_first + a.B * a.Hkv;
+
+  int64_t pos = s_begin;
+  while (pos < s_end && b < a.B) {  // uniform: one segment part per pass
+    int first = first_found, L = len_found;
+    const int ns = b == b_found ? (L - first + kSlice - 1) / kSlice : seq_slices(a, b, first, L);
+    const int64_t span = static_cast<int64_t>(a.Hkv) * ns;
+    if (pos >= seq0 + span) {
+      seq0 += span;
+      ++b;
+      continue;
+    }
+    const int64_t r = pos - seq0;
+    const int h = static_cast<int>(r / ns);
+    const int j0 = static_cast<int>(r - static_cast<int64_t>(h) * ns);
+    const int j1 = static_cast<int>(min<int64_t>(ns, s_end - seq0 - static_cast<int64_t>(h) * ns));
+    pos = seq0 + static_cast<int64_t>(h) * ns + j1;
+    const int sigma = b * a.Hkv + h;
+    // the thread index, opaque to the optimizer per part: values derived from
+    // it are computed where they are used instead of being kept in registers
+    // across all parts
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int col = lane & 15, kg = lane >> 4;
+    uint16_t *pp = reinterpret_cast<uint16_t *>(prow_s[w]);
+    uint4 *vb = vbuf_s[w];
+
+    __syncthreads();  // the previous part's readers of the tables and of red are done
+    if (tid == 0) {
+      if (j0 == 0) tab_first[sigma] = wg;
+      if (j1 == ns) tab_last[sigma] = wg;
+    }
+    // the codes of segment (b, h) through buffer resources (base and size in
+    // scalar registers, 32-bit offsets per lane)
+    const int64_t row0 = (static_cast<int64_t>(b) * a.Hkv + h) * a.S;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(a.k_codes + row0 * NSK), 0, a.S * NSK, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(a.v_codes + row0 * NSV), 0, a.S * NSV, kBufferWord3);
+    // key codes of slice j into kw (lane: quarter kg of token 16 G + col);
+    // clamped token indices
+    auto load_keys = [&](int j, uint32_t(&kw)[4][NQW]) {
+      const int t0 = first + j * kSlice;
+#pragma unroll
+      for (int G4 = 0; G4 < 4; ++G4) {
+        const int off = min(t0 + 16 * G4 + col, L - 1) * NSK + kg * QB;
+        if constexpr (NQW == 4) {
+          const auto q = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+          kw[G4][0] = q[0];
+          kw[G4][1] = q[1];
+          kw[G4][2] = q[2];
+          kw[G4][3] = q[3];
+        } else if constexpr (NQW == 2) {
+          const auto q = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
+          kw[G4][0] = q[0];
+          kw[G4][1] = q[1];
+        } else {
+          kw[G4][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, off, 0, 0);
+        }
+      }
+    };
+    // value codes of slice j into the wave's buffer (slot e = 64 q + lane:
+    // token e / VP, piece (e % VP) ^ ((token / 2) mod VP), so that the rows of
+    // tokens 2 apart, read together by the value sum, start on different
+    // banks); clamped token indices
+    auto copy_values = [&](int j) {
+      const int t0 = first + j * kSlice;
+      wait_lgkm_all();  // earlier reads of the buffer have completed
+#pragma unroll
+      for (int q = 0; q < VP; ++q) {
+        const int e = 64 * q + lane;
+        const int tc = e / VP, pc = e % VP;
+        const int off = min(t0 + tc, L - 1) * NSV + 16 * (pc ^ ((tc >> 1) & (VP - 1)));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void *)(vb + 64 * q), 16, off, 0, 0, 0);
+      }
+    };
+    // Every step issues the same memory operations in the same order (the
+    // key codes of the next slice after the scores, its value codes after the
+    // value sum; past the wave's last slice the loads repeat that slice), so
+    // the waits the compiler places count only what each use needs.
+    // ---- codebooks of kv head h, query parts of its g heads: their loads
+    // go out before the first slice's codes (they are few and cached) ------
+    const int n_c = a.n_c;
+    uint16_t kvr[SDK], vvr[SDV];
+    {
+      const uint16_t *kcb = a.k_cb + static_cast<int64_t>(h) * n_c * SDK;
+      const uint16_t *vcb = a.v_cb + static_cast<int64_t>(h) * n_c * SDV;
+#pragma unroll
+      for (int k = 0; k < SDK; ++k) kvr[k] = kcb[min(tid + kThreads * k, n_c * SDK - 1)];
+#pragma unroll
+      for (int k = 0; k < SDV; ++k) vvr[k] = vcb[min(tid + kThreads * k, n_c * SDV - 1)];
+    }
+    constexpr int JH = GC > 4 ? 2 : 1;
+    uint16_t qv[JH][D / 64];
+    float ks[D / 64];
+#pragma unroll
+    for (int jh = 0; jh < JH; ++jh) {
+      const int hq = h * g + min(w + 4 * jh, g - 1);
+      const uint16_t *qrow = a.q + (static_cast<int64_t>(b) * a.Hq + hq) * D;
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) qv[jh][k] = qrow[lane + 64 * k];
+    }
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k)
+      ks[k] = a.k_scale ? a.k_scale[static_cast<int64_t>(h) * D + lane + 64 * k] : 1.0f;
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t kw[4][NQW];
+    int j = j0 + w;
+    if (j < j1) {
+      load_keys(j, kw);
+      copy_values(j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < SDK; ++k) {
+      const int e = tid + kThreads * k;
+      ktab[e] = (e < n_c * SDK) ? kvr[k] : static_cast<uint16_t>(0);
+    }
+#pragma unroll
+    for (int k = 0; k < SDV; ++k) {
+      const int e = tid + kThreads * k;
+      vtab[e] = (e < n_c * SDV) ? vvr[k] : static_cast<uint16_t>(0);
+    }
+#pragma unroll
+    for (int jh = 0; jh < JH; ++jh) {
+      const int hs = w + 4 * jh;
+      if (hs < g) {  // uniform per wave
+        uint16_t *rows = qp + static_cast<int64_t>(hs) * P * QS;
+        float x[D / 64];
+        float mx = 0.0f;
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) {
+          float v = widen<BF16>(qv[jh][k]);
+          if (a.k_scale) v = v / ks[k];
+          v = v * a.qmul;
+          x[k] = v;
+          mx = fmaxf(mx, __builtin_fabsf(v));
+        }
+        mx = row_max16(mx);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        int E = 0;
+        if (mx > 0.0f && mx <= 3.4028234663852886e38f) {
+          int ex;
+          (void)frexpf(mx, &ex);  // mx = f 2^ex, f in [0.5, 1)
+          E = 14 - ex;            // max |q~| 2^E in [2^13, 2^14)
+        }
+        if (lane == 0) qexp[hs] = E;
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) {
+          const int d = lane + 64 * k;
+          float rr = ldexpf(x[k], E);
+#pragma unroll
+          for (int q = 0; q < P; ++q) {  // rr - part is exact in fp32
+            const uint16_t pb = narrow_rn<BF16>(rr);
+            rows[q * QS + d] = pb;
+            rr = rr - widen<BF16>(pb);
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // A operand of the scores: row col of the query parts (the zero row past
+    // g P), quarter kg
+    uint4 areg[NI];
+    {
+      const uint16_t *arow = qp + (col < nrows ? col : ZR) * QS + kg * (D / 4);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) areg[i] = *reinterpret_cast<const uint4 *>(arow + 8 * i);
+    }
+    int ex[HPL];
+#pragma unroll
+    for (int jj = 0; jj < HPL; ++jj) ex[jj] = qexp[min(kg * HPL + jj, g - 1)];
+    float m_run[HPL], l_run[HPL];
+#pragma unroll
+    for (int jj = 0; jj < HPL; ++jj) {
+      m_run[jj] = kNegInf;
+      l_run[jj] = 0.0f;
+    }
+    // Value sum, rows (head, part, element): in block rb lane (col, kg) holds
+    // rows 16 rb + 4 kg .. + 3 = elements 0..3 of weight row 4 rb + kg, for
+    // sub-space 16 cg + col.  Its A operand is row 16 rb + col, i.e. weight row
+    // (16 rb + col) / 4 placed at element e = col % 4 of its two tokens: word
+    // e / 2 (first token) and 2 + e / 2 (second), half e % 2 (selectors).
+    f32x4 vacc[NCG][NRB];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) vacc[cg][rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int ea = col & 3;
+    const uint32_t zsel = 0x0C0C0C0Cu;
+    const uint32_t lo_sel = (ea & 1) ? 0x01000C0Cu : 0x0C0C0100u;  // first token's half
+    const uint32_t hi_sel = (ea & 1) ? 0x03020C0Cu : 0x0C0C0302u;  // second token's half
+    const uint32_t sel0 = (ea >> 1) == 0 ? lo_sel : zsel, sel1 = (ea >> 1) == 1 ? lo_sel : zsel;
+    const uint32_t sel2 = (ea >> 1) == 0 ? hi_sel : zsel, sel3 = (ea >> 1) == 1 ? hi_sel : zsel;
+    int prow_off[NRB];  // the weight row of A row 16 rb + col (the zero row past g P)
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int hp = (16 * rb + col) >> 2;
+      prow_off[rb] = (hp < nrows ? hp : ZR) * PS + 2 * kg;
+    }
+    const uint8_t *codes = reinterpret_cast<const uint8_t *>(vb) + 2 * kg * NSV + col;
+    const int swz = kg & (VP - 1);
+
+    const uint2 *ktab2 = reinterpret_cast<const uint2 *>(ktab_s);
+    const uint4 *ktab4 = reinterpret_cast<const uint4 *>(ktab_s);
+    const uint2 *vtab2 = reinterpret_cast<const uint2 *>(vtab_s);
+    // one 64-token slice: scores, running softmax, value sum
+    auto slice = [&](int js) {
+      const int t0 = first + js * kSlice;
+      float sreg[4][HPL];
+#pragma unroll
+      for (int G4 = 0; G4 < 4; ++G4) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          uint4 bop;
+          if constexpr (SDK == 4) {
+            const uint32_t wd = kw[G4][i >> 1];
+            const uint32_t c0 = (wd >> (16 * (i & 1))) & 0xFFu;
+            const uint32_t c1 = (wd >> (16 * (i & 1) + 8)) & 0xFFu;
+            const uint2 r0 = ktab2[c0], r1 = ktab2[c1];
+            bop = make_uint4(r0.x, r0.y, r1.x, r1.y);
+          } else {
+            const uint32_t c = (kw[G4][i >> 2] >> (8 * (i & 3))) & 0xFFu;
+            bop = ktab4[c];
+          }
+          acc = mfma16<BF16>(areg[i], bop, acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one 16-token group's gathers live at a time
+        const bool valid = t0 + 16 * G4 + col < L;
+        if constexpr (P == 2) {
+          sreg[G4][0] = valid ? ldexpf(acc[0] + acc[1], -ex[0]) : kNegInf;
+          sreg[G4][1] = valid ? ldexpf(acc[2] + acc[3], -ex[1]) : kNegInf;
+        } else {
+          sreg[G4][0] = valid ? ldexpf(((acc[3] + acc[2]) + acc[1]) + acc[0], -ex[0]) : kNegInf;
+        }
+      }
+      // the key codes are consumed: the next slice's go into the same registers
+      load_keys(min(js + 4, j1 - 1), kw);
+      __builtin_amdgcn_sched_barrier(0);
+      // running maximum per head; rescale the sums when it rises
+      float alpha[HPL];
+      bool grow = false;
+#pragma unroll
+      for (int jj = 0; jj < HPL; ++jj) {
+        float m = fmaxf(fmaxf(sreg[0][jj], sreg[1][jj]), fmaxf(sreg[2][jj], sreg[3][jj]));
+        m = row_max16(m);
+        const float mn = fmaxf(m_run[jj], m);
+        alpha[jj] = (mn == m_run[jj]) ? 1.0f : exp2f(m_run[jj] - mn);
+        grow = grow || mn != m_run[jj];
+        m_run[jj] = mn;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow)) {  // uniform
+#pragma unroll
+        for (int jj = 0; jj < HPL; ++jj) {
+          l_run[jj] *= alpha[jj];
+          if (col == 0 && kg * HPL + jj < GC) walpha[w][kg * HPL + jj] = alpha[jj];
+        }
+        // value rows of block rb: weight row 4 rb + kg, head (4 rb + kg) / P
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const float f = walpha[w][min((4 * rb + kg) / P, GC - 1)];
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) vacc[cg][rb][rr] *= f;
+        }
+      }
+      // weights p 2^14, split, as rows (head, part) x 64 tokens
+#pragma unroll
+      for (int jj = 0; jj < HPL; ++jj) {
+        const int hh = kg * HPL + jj;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int G4 = 0; G4 < 4; ++G4) {
+          const float sv = sreg[G4][jj];
+          const float pv = (sv == kNegInf) ? 0.0f : exp2f(sv - m_run[jj]);
+          lsum += pv;
+          if (hh < g) {
+            float rr = pv * kPScale;
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+              const uint16_t pb = narrow_rn<BF16>(rr);
+              pp[(hh * P + q) * PS + 16 * G4 + col] = pb;
+              rr = rr - widen<BF16>(pb);
+            }
+          }
+        }
+        l_run[jj] += row_sum16(lsum);
+      }
+      // value sum over 8-token groups: lane (col, kg) gathers the rows of
+      // sub-space 16 cg + col for tokens 8 k8 + 2 kg, + 1 (one B operand,
+      // elements in order); the A operand places the weights by element
+#pragma unroll
+      for (int k8 = 0; k8 < kSlice / 8; ++k8) {
+        uint4 aop[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const uint32_t pv = *reinterpret_cast<const uint32_t *>(pp + prow_off[rb] + 8 * k8);
+          aop[rb] = make_uint4(__builtin_amdgcn_perm(0u, pv, sel0), __builtin_amdgcn_perm(0u, pv, sel1),
+                               __builtin_amdgcn_perm(0u, pv, sel2), __builtin_amdgcn_perm(0u, pv, sel3));
+        }
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          const uint8_t *cc = codes + 8 * k8 * NSV + ((cg ^ swz) << 4);
+          const uint2 r0 = vtab2[cc[0]], r1 = vtab2[cc[NSV]];
+          const uint4 bop = make_uint4(r0.x, r0.y, r1.x, r1.y);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) vacc[cg][rb] = mfma16<BF16>(aop[rb], bop, vacc[cg][rb]);
+        }
+      }
+      // the value codes are consumed: the next slice's go into the buffer
+      copy_values(min(js + 4, j1 - 1));
+    };
+
+    while (j < j1) {  // uniform per wave
+      slice(j);
+      j += 4;
+    }
+    wait_vm_all();  // the repeated loads past the last slice have landed
+
+    // ---- merge the waves, write the part's partial -------------------------
+    if (col == 0) {
+#pragma unroll
+      for (int jj = 0; jj < HPL; ++jj) {
+        const int hh = kg * HPL + jj;
+        if (hh < g) {
+          wm[w][hh] = m_run[jj];
+          wl[w][hh] = l_run[jj];
+        }
+      }
+    }
+    __syncthreads();
+    // o of weight row 4 rb + kg (head (4 rb + kg) / P), elements 0..3 of
+    // sub-space 16 cg + col: scaled to the part's maximum, parts summed across
+    // the lanes that hold them (kg differs in its low log2(P) bits)
+    float o[NRB][NCG][4];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int hc = min((4 * rb + kg) / P, g - 1);
+      const float M = fmaxf(fmaxf(wm[0][hc], wm[1][hc]), fmaxf(wm[2][hc], wm[3][hc]));
+      const float mine_m = wm[w][hc];
+      const float f = (mine_m == kNegInf) ? 0.0f : exp2f(mine_m - M) * (1.0f / kPScale);
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = vacc[cg][rb][e];
+          v = v + __shfl_xor(v, 16);
+          if constexpr (P == 4) v = v + __shfl_xor(v, 32);
+          o[rb][cg][e] = v * f;
+        }
+    }
+    // lanes holding part 0 of a head in range write it
+    const bool owner = (kg & (P - 1)) == 0;
+    if (w > 0 && owner) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int hh = (4 * rb + kg) / P;
+        if (hh < g) {
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              red[((w - 1) * GC + hh) * D + (cg * 16 + col) * 4 + e] = o[rb][cg][e];
+        }
+      }
+    }
+    __syncthreads();
+    float *slot = a.ws + static_cast<int64_t>(wg + sigma) * g * (D + 2);
+    if (w == 0 && owner) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int hh = (4 * rb + kg) / P;
+        if (hh < g) {
+          float *dst = slot + hh * (D + 2);
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg) {
+            const int d0 = (cg * 16 + col) * 4;
+            float s4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              s4[e] = ((o[rb][cg][e] + red[hh * D + d0 + e]) + red[(GC + hh) * D + d0 + e]) +
+                      red[(2 * GC + hh) * D + d0 + e];
+            *reinterpret_cast<float4 *>(dst + d0) = make_float4(s4[0], s4[1], s4[2], s4[3]);
+          }
+        }
+      }
+    }
+    if (tid < g) {
+      const float M = fmaxf(fmaxf(wm[0][tid], wm[1][tid]), fmaxf(wm[2][tid], wm[3][tid]));
+      float l = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) l += wm[v][tid] == kNegInf ? 0.0f : wl[v][tid] * exp2f(wm[v][tid] - M);
+      slot[tid * (D + 2) + D] = M;
+      slot[tid * (D + 2) + D + 1] = l;
+    }
+  }
+}
+
+// Merge of the streaming form: the partials of (sequence, query head)
+// blockIdx.x sit in slots i + sigma for the workgroups i from the first to
+// the last one recorded for its segment sigma; a sequence with no attended
+// token gets zeros.
+__global__ void __launch_bounds__(kThreads)
+attn_stream_combine(const AttnArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq, hq = bh - b * a.Hq;
+  const int g = a.Hq / a.Hkv, h = hq / g, jh = hq - h * g;
+  float *out = a.out + static_cast<int64_t>(bh) * a.D;
+  int first, L;
+  if (seq_slices(a, b, first, L) == 0) {
+    if (threadIdx.x < a.D) out[threadIdx.x] = 0.0f;
+    return;
+  }
+  const int G = a.n_wg;
+  const int sigma = b * a.Hkv + h;
+  const int *tab_first = reinterpret_cast<const int *>(
+      a.ws + static_cast<int64_t>(G + a.B * a.Hkv - 1) * g * (a.D + 2));
+  // (clamped: the indices are always in range when the partial launch ran)
+  const int i0 = min(max(tab_first[sigma], 0), G - 1);
+  const int i1 = min(max(tab_first[a.B * a.Hkv + sigma], i0), G - 1);
+  const int64_t cstride = static_cast<int64_t>(g) * (a.D + 2);
+  merge_partials(a.ws + (static_cast<int64_t>(i0 + sigma) * g + jh) * (a.D + 2), i1 - i0 + 1,
+                 cstride, a.D, out);
 }
 
 template <int SDK, int SDV, bool BF16>
@@ -930,12 +1551,57 @@ constexpr bool mfma_shape(int sdk, int sdv, int d) {
   return (d == 64 || d == 128 || d == 256) && (d / sdk) % 16 == 0 && (d / sdv) % 16 == 0;
 }
 
+// Workgroups of the streaming form for this call: per_cu per CU, few enough
+// that the partials (slots up to G + B Hkv - 1) and the segment table fit in
+// the workspace the chunked form is sized for (attention_chunks(S) partials
+// per sequence and query head).  0 = the chunked form runs instead: the
+// streaming form pays a longer fixed latency per workgroup (length scan,
+// staging, merge in sequence), which only a long enough range of slices per
+// workgroup amortizes; below kStreamMinSlices slices per workgroup (counted
+// on max_kv_len, the lengths being on the device) the chunked form is the
+// faster one.
+constexpr int64_t kStreamMinSlices = 32;
+int stream_workgroups(const AttnArgs &a, int per_cu) {
+  const int g = a.Hq / a.Hkv;
+  const int64_t segs = static_cast<int64_t>(a.B) * a.Hkv;
+  const int64_t row = static_cast<int64_t>(g) * (a.D + 2);  // floats per slot
+  const int64_t avail = static_cast<int64_t>(a.B) * a.Hq * attention_chunks(a.S) * (a.D + 2);
+  const int64_t gmax = (avail - 2 * segs) / row - segs + 1;
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  const int64_t G = static_cast<int64_t>(per_cu) * cus;
+  const int64_t slices = segs * ((static_cast<int64_t>(a.S) + kSlice - 1) / kSlice);
+  if (slices < kStreamMinSlices * G || G > gmax) return 0;
+  return static_cast<int>(G);
+}
+
 template <int SDK, int SDV, bool BF16, int D>
 hipError_t launch_attn_m(AttnArgs a, hipStream_t stream) {
   if constexpr (!mfma_shape(SDK, SDV, D)) {
     return hipErrorInvalidValue;
   } else {
     const int g = a.Hq / a.Hkv;
+    // the streaming form (value sub-dim 4) holds one block of query rows:
+    // g P <= 16
+    if constexpr (SDV == 4) {
+      const bool small = BF16 || g <= 4;
+      constexpr int GC8 = BF16 ? 4 : kMaxGroup;
+      a.n_wg = (g * (BF16 ? 4 : 2) <= 16)
+                   ? stream_workgroups(a, small ? kStreamPerCu<BF16, D, 4> : kStreamPerCu<BF16, D, GC8>)
+                   : 0;
+      if (a.n_wg > 0) {
+        auto kern = small ? attn_stream_partial<SDK, SDV, BF16, D, 4>
+                          : attn_stream_partial<SDK, SDV, BF16, D, GC8>;
+        hipLaunchKernelGGL(kern, dim3(a.n_wg), dim3(kThreads), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_stream_combine, dim3(a.B * a.Hq), dim3(kThreads), 0, stream, a);
+        return hipGetLastError();
+      }
+    }
     auto kern = g <= 4 ? attn_mfma_partial<SDK, SDV, BF16, D, 4>
                        : attn_mfma_partial<SDK, SDV, BF16, D, kMaxGroup>;
     a.n_chunks = attention_chunks(a.S);
@@ -1026,6 +1692,7 @@ hipError_t launch_attention(const AttnLayout &l, hipStream_t stream) {
   a.n_c = l.n_centroids;
   a.window = l.window;
   a.n_chunks = 0;
+  a.n_wg = 0;
   a.qmul = l.softmax_scale * 1.4426950408889634f;
   const bool mfma = mfma_shape(l.k_sub_dim, l.v_sub_dim, l.head_dim) &&
                     reinterpret_cast<uintptr_t>(l.k_codes) % 16 == 0 &&

@@ -12,7 +12,9 @@ is reported too and is typically ~1e-7 of M.  Cases cover both code sub-dims
 for keys and values, fp16 and bf16, smoothed and plain keys, grouped-query
 groups 1..8, head_dim 16..256, multi-chunk and ragged lengths (empty and
 one-token sequences), windows, codes past the codebook, a dirty workspace,
-the Falcon3-7B decode workload at full size, and that workload with the
+sizes that run the streaming form (balanced token ranges, running softmax,
+up to 2048 sequences), the Falcon3-7B decode workload at full size (32 and
+128 sequences: the chunked and the streaming form), and that workload with the
 tokens next to every 256-token chunk boundary carrying the attention (so a
 dropped, repeated or misweighted boundary token is far outside the bound).
 """
@@ -96,10 +98,28 @@ CASES = [
     (8, 2, 16, 2, 64, 1100, 4, 8, 100, W.F16, dict(lens="ragged", skew=0.8)),
     (9, 1, 1, 1, 256, 4096, 4, 4, 256, W.BF16, dict()),
     (10, 6, 4, 1, 96, 520, 8, 8, 33, W.F16, dict(lens="ragged", window=513)),
+    # more sequences than a workgroup has threads, 8 query heads per kv head,
+    # sub_dim 8 bf16 keys and values
+    (11, 300, 8, 2, 64, 300, 4, 4, 64, W.F16, dict(lens="ragged")),
+    (12, 4, 16, 2, 128, 1000, 4, 4, 256, W.F16, dict(lens="mixed", window=300)),
+    (13, 7, 4, 4, 256, 777, 8, 8, 256, W.BF16, dict(lens="ragged")),
+    (14, 3, 8, 2, 256, 3000, 4, 8, 128, W.F16, dict(lens="mixed", smooth=False)),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"t{c[0]}_D{c[4]}_S{c[5]}" for c in CASES])
+# Sizes at which the streaming form runs (at least 32 slices of 64 tokens per
+# workgroup, counted on max_kv_len): more sequences than a workgroup has
+# threads (the length scan takes several rounds) with empty and one-token
+# sequences, bf16 with sub_dim 8 keys, 8 query heads per kv head with a window.
+STREAM_CASES = [
+    (31, 2048, 2, 1, 64, 1024, 4, 4, 256, W.F16, dict(lens="ragged")),
+    (32, 640, 8, 2, 128, 2048, 8, 4, 256, W.BF16, dict(lens="ragged")),
+    (33, 260, 16, 2, 256, 2048, 4, 4, 256, W.F16, dict(lens="mixed", window=1500)),
+]
+
+
+@pytest.mark.parametrize("case", CASES + STREAM_CASES,
+                         ids=[f"t{c[0]}_B{c[1]}_D{c[4]}_S{c[5]}" for c in CASES + STREAM_CASES])
 def test_attention_matches_oracle(case):
     seed, B, Hq, Hkv, D, S, sdk, sdv, n_c, dt, extra = case
     window = extra.pop("window", 0)
@@ -117,13 +137,22 @@ def test_codes_past_the_codebook_read_zero_rows():
     assert_attention_parity(wl)
 
 
-def test_softmax_scale_and_identical_results_across_workspaces():
-    wl = W.attention_case(21, 2, 6, 3, 64, 900, 8, 8, 256, W.F16, lens="mixed")
+@pytest.mark.parametrize("sd", [8, 4])
+def test_softmax_scale_and_identical_results_across_workspaces(sd):
+    wl = W.attention_case(21, 2, 6, 3, 64, 900, sd, sd, 256, W.F16, lens="mixed")
     wl.softmax_scale = 0.3
     assert_attention_parity(wl)
     a = gpu_attention(wl, dirty_workspace=True)
     b = gpu_attention(wl, dirty_workspace=False)
     assert np.array_equal(a, b)
+
+
+def test_codes_past_the_codebook_read_zero_rows_matrix_core_shape():
+    wl = W.attention_case(23, 3, 8, 2, 128, 700, 4, 4, 77, W.F16, lens="ragged")
+    r = np.random.default_rng(23)
+    wl.k_codes[r.random(wl.k_codes.shape) < 0.05] = 255
+    wl.v_codes[r.random(wl.v_codes.shape) < 0.05] = 130
+    assert_attention_parity(wl)
 
 
 def test_all_sequences_empty():
@@ -132,8 +161,9 @@ def test_all_sequences_empty():
     assert np.all(gpu_attention(wl) == 0)
 
 
-def test_falcon_decode_workload_full_size():
-    wl = W.falcon_decode_attention()
+@pytest.mark.parametrize("B", [32, 128])
+def test_falcon_decode_workload_full_size(B):
+    wl = W.falcon_decode_attention(B=B)
     print(f"[case] {wl.name}", flush=True)
     assert_attention_parity(wl)
 

@@ -79,6 +79,9 @@ CONFIG_TAGS = {1: "encode_tiny", 2: "encode_llama8b", 3: "encode_falcon3", 4: "e
                5: "encode_large_codebook"}
 ROW_TAGS = {"fused": "encode_fused_falcon3", "attention": "attention_falcon3_decode",
             "kmeans": "kmeans_falcon3", "kmeans_bf16": "kmeans_bf16_large_codebook"}
+# sequence counts of the attention row with a profile of their own (the
+# streaming form runs at 128)
+ATTENTION_BATCH_TAGS = {128: "attention_falcon3_decode_b128"}
 # rows of each config the oracle checks in the bench (the tests check all)
 PARITY_ROWS = {1: 2048, 2: 1 << 18, 4: 1 << 18, 5: 1 << 14}
 
@@ -389,7 +392,10 @@ def leg_attention(args, dev, stream):
         _, ls = time_row(lambda: vq.attention_decode_raw(*callb), steps, stream, warm_s=0.02)
         batches[str(nb)] = dict(kernel_ms_per_launch=ls * 1e3,
                                 algorithmic_gb_per_s=bytes_b / ls / 1e9,
-                                frac=bytes_b / ls / 1e9 / HBM_PEAK_GBS)
+                                frac=bytes_b / ls / 1e9 / HBM_PEAK_GBS,
+                                algorithmic_bytes_per_launch=bytes_b)
+        if nb in ATTENTION_BATCH_TAGS:
+            batches[str(nb)]["traffic"] = traffic_bytes_per_launch(ATTENTION_BATCH_TAGS[nb])
     tag = ROW_TAGS["attention"]
     return {
         "workload": wl.name,

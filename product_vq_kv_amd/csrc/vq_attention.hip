@@ -24,6 +24,10 @@
 //     folded into q~;
 //   * the value sum maps lanes to (value sub-space, token group): a lane reads
 //     one value-codebook row per token and feeds all g heads with it.
+// For head_dim 64, 128 and 256 the scores and the value sum run on the
+// matrix cores instead (attn_mfma_partial).  Large batches take a streaming
+// form (attn_stream_partial): balanced ranges of 64-token slices per
+// workgroup, a running softmax per wave and one partial per segment part.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -743,6 +743,8 @@ attn_mfma_partial(const AttnArgs a) {
       }
     }
   }
+  // every wave's value-code copies have landed before any wave reads them
+  wait_vm_all();
   __syncthreads();
 
   // ---- value sum on the matrix cores: wave w takes sub-spaces 16 (w % WG)
@@ -980,6 +982,10 @@ __device__ __forceinline__ int64_t block_scan(int64_t v, int64_t *sc, int64_t &t
 
 // Waits until every LDS operation of the wave has completed.
 __device__ __forceinline__ void wait_lgkm_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Waits until at most 4 vector memory operations of the wave are in flight
+// (vmcnt(4)): the 4 key-code loads of the next slice.
+__device__ __forceinline__ void wait_vm_keys() { __builtin_amdgcn_s_waitcnt(0x0F74); }
 
 template <int SDK, int SDV, bool BF16, int D, int GC>
 __global__ void __launch_bounds__(kThreads, (kStreamPerCu<BF16, D, GC>))
@@ -1342,6 +1348,12 @@ attn_stream_partial(const AttnArgs a) {
       }
       // the key codes are consumed: the next slice's go into the same registers
       load_keys(min(js + 4, j1 - 1), kw);
+      __builtin_amdgcn_sched_barrier(0);
+      // This slice's value codes (the copy issued one step earlier, before
+      // those 4 key loads) must have landed in LDS before the value sum reads
+      // them; the compiler does not track the copy's LDS writes, so the wait
+      // is explicit: at most the 4 key loads may still be in flight.
+      wait_vm_keys();
       __builtin_amdgcn_sched_barrier(0);
       // running maximum per head; rescale the sums when it rises
       float alpha[HPL];

@@ -8,7 +8,9 @@ on a smaller input, so the second reads a scratch buffer the first left
 dirty; the device's free memory must not change across a static call.
 Captured in a HIP graph (through torch's graph API), the call must give
 the eager result on every replay, with new queries copied in and other
-eager work between the replays.
+eager work between the replays.  Both decode forms are covered: the chunked
+one, and the streaming one at 128 Falcon3-7B sequences (its partials and
+segment table in the same scratch).
 """
 import numpy as np
 import pytest
@@ -52,17 +54,25 @@ def _check_against_oracle(wl, got):
     assert np.all(np.abs(got - ref) <= bound)
 
 
+def _workload(case):
+    if case == "falcon128":  # runs the streaming form
+        return W.falcon_decode_attention(B=128)
+    seed, B, Hq, Hkv, D, S, sdk, sdv, n_c, dt, lens = case
+    return W.attention_case(seed, B, Hq, Hkv, D, S, sdk, sdv, n_c, dt, lens=lens)
+
+
 @pytest.mark.parametrize("first,second", [
     # (seed, B, Hq, Hkv, D, S, sdk, sdv, n_c, dtype, lens)
     ((51, 8, 12, 4, 256, 3000, 4, 4, 256, W.F16, "mixed"),
      (52, 3, 12, 4, 256, 700, 4, 4, 256, W.F16, "ragged")),
     ((53, 4, 8, 2, 96, 1500, 8, 8, 200, W.BF16, "mixed"),
      (54, 2, 4, 1, 32, 300, 4, 8, 64, W.F16, "ragged")),
-])
+    ("falcon128", (52, 3, 12, 4, 256, 700, 4, 4, 256, W.F16, "ragged")),
+], ids=["chunked", "chunked-lut", "streaming"])
 def test_static_scratch_matches_the_workspace_entry_point(first, second):
     for case in (first, second):
-        seed, B, Hq, Hkv, D, S, sdk, sdv, n_c, dt, lens = case
-        wl = W.attention_case(seed, B, Hq, Hkv, D, S, sdk, sdv, n_c, dt, lens=lens)
+        wl = _workload(case)
+        B, Hq, Hkv, D, S = wl.shape
         print(f"[case] {wl.name}", flush=True)
         t = _dev(wl)
         ref = vq.attention_decode(t["q"], t["k_codes"], t["v_codes"], t["k_codebook"],
@@ -94,8 +104,10 @@ def test_static_scratch_rejects_inputs_beyond_its_size():
                                        4096, 4, 4, 64, W.F16, 0, 0.0625, out.data_ptr(), None)
 
 
-def test_static_entry_point_captured_in_a_graph():
-    wl = W.attention_case(56, 6, 12, 4, 256, 1800, 4, 4, 256, W.F16, lens="mixed")
+@pytest.mark.parametrize("case", [(56, 6, 12, 4, 256, 1800, 4, 4, 256, W.F16, "mixed"),
+                                  "falcon128"], ids=["chunked", "streaming"])
+def test_static_entry_point_captured_in_a_graph(case):
+    wl = _workload(case)
     t = _dev(wl)
     B, Hq, Hkv, D, S = wl.shape
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=DEV)

@@ -1591,6 +1591,9 @@ int stream_workgroups(const AttnArgs &a, int per_cu) {
   const int64_t G = static_cast<int64_t>(per_cu) * cus;
   const int64_t slices = segs * ((static_cast<int64_t>(a.S) + kSlice - 1) / kSlice);
   if (slices < kStreamMinSlices * G || G > gmax) return 0;
+  // a segment's codes are addressed with 32-bit offsets (buffer resources)
+  const int64_t row_bytes = a.D / 4;  // the most code bytes per token (sub_dim 4)
+  if (static_cast<int64_t>(a.S) * row_bytes >= (int64_t{1} << 31)) return 0;
   return static_cast<int>(G);
 }
 

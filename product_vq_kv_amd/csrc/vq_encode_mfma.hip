@@ -1028,14 +1028,6 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
         g1[t] = (mb < m1[t]) ? 2 * blk + h : g1[t];
         m1[t] = __builtin_amdgcn_fmed3f(m1[t], mb, kNegMax);
       };
-      // 8-row groups: group 2 k + h with k = 2 blk + q, and k written into
-      // the 4 low bits of the bound (see Consts); equal keys then hold equal
-      // k, and min and med3 carry the index along with the bound
-      auto track_key = [&](int t, float mb, uint32_t k) {
-        const float key = __uint_as_float((__float_as_uint(mb) & ~kIdxMask) | k);
-        m2[t] = __builtin_amdgcn_fmed3f(m1[t], m2[t], key);
-        m1[t] = __builtin_amdgcn_fmed3f(m1[t], key, kNegMax);
-      };
       // the bounds of this lane's groups from a product: lo (and hi, SMALL)
       auto reduce = [&](int t, const f32x16 &a, float &lo, float &hi) {
         if constexpr (SMALL) {
@@ -1055,8 +1047,23 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       const uint32_t k_hi = __builtin_amdgcn_readfirstlane(k_lo + 1u);
       auto track_all = [&](int t, float lo, float hi) {
         if constexpr (SMALL) {
-          track_key(t, lo, k_lo);
-          track_key(t, hi, k_hi);
+          // 8-row groups: group 2 k + h with k = 2 blk + q, and k written
+          // into the 4 low bits of the bound (see Consts), so keys of
+          // different groups differ and min and med3 carry the index along
+          // with the bound.  Both keys of the block at once: with m1 <= m2
+          // and distinct keys a, b the new smallest is min3(m1, a, b) and the
+          // new second smallest min(m2, med3(m1, a, b)): 3 instructions for 2
+          // keys.  min3 and min are written out because keys with index bits
+          // are not canonical floats to the compiler, which would quiet them
+          // first (the keys are finite, so quieting changes nothing).
+          const float ka = __uint_as_float((__float_as_uint(lo) & ~kIdxMask) | k_lo);
+          const float kb = __uint_as_float((__float_as_uint(hi) & ~kIdxMask) | k_hi);
+          const float mid = __builtin_amdgcn_fmed3f(m1[t], ka, kb);
+          float n1, n2;
+          asm("v_min3_f32 %0, %1, %2, %3" : "=v"(n1) : "v"(m1[t]), "v"(ka), "v"(kb));
+          asm("v_min_f32 %0, %1, %2" : "=v"(n2) : "v"(m2[t]), "v"(mid));
+          m1[t] = n1;
+          m2[t] = n2;
         } else {
           track(t, lo);
         }

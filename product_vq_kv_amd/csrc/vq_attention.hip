@@ -724,7 +724,10 @@ attn_mfma_partial(const AttnArgs a) {
 #pragma unroll
         for (int G = 0; G < 4; ++G) {
           const float sv = sreg[hb][G][j];
-          const float pv = (sv == kNegInf) ? 0.0f : exp2f(sv - M);
+          // v_exp_f32 directly: M is finite (the chunk attends a token) and
+          // a masked score of -inf gives 2^-inf = 0; results below 2^-126
+          // (flushed) are far below the split's resolution of 2^-38
+          const float pv = __builtin_amdgcn_exp2f(sv - M);
           lsum += pv;
           if (hh < g) {
             const int tc = w * kWaveTok + 16 * G + col;
@@ -1391,7 +1394,9 @@ attn_stream_partial(const AttnArgs a) {
 #pragma unroll
         for (int G4 = 0; G4 < 4; ++G4) {
           const float sv = sreg[G4][jj];
-          const float pv = (sv == kNegInf) ? 0.0f : exp2f(sv - m_run[jj]);
+          // v_exp_f32 directly (results below 2^-126 flush to 0, far below
+          // the split's resolution of 2^-38)
+          const float pv = (sv == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(sv - m_run[jj]);
           lsum += pv;
           if (hh < g) {
             float rr = pv * kPScale;

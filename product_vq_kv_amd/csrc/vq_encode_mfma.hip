@@ -370,7 +370,7 @@ __device__ __forceinline__ float pair_sum(float v) {
 //   c32                     the centroids in fp32 (ROWS32 only; +inf in the
 //                           padding rows), row r at
 //                           c32_offset(r): 16 bytes of padding after every
-//                           4 rows and after every 32, so that the rows the
+//                           4 rows and after every 16, so that the rows the
 //                           lanes of a wave read together in the exact stage
 //                           (same position in different groups) fall on
 //                           different LDS banks;
@@ -396,9 +396,9 @@ struct Lds {
   }
   // floats of the c32 region, and the float offset of row r in it
   static constexpr int c32_len(int n_cpad) {
-    return ROWS32 ? SD * n_cpad + 4 * (n_cpad / 4 + n_cpad / 32 + 1) : 0;
+    return ROWS32 ? SD * n_cpad + 4 * (n_cpad / 4 + n_cpad / 16 + 1) : 0;
   }
-  static __device__ __forceinline__ int c32_offset(int r) { return SD * r + 4 * ((r >> 2) + (r >> 5)); }
+  static __device__ __forceinline__ int c32_offset(int r) { return SD * r + 4 * ((r >> 2) + (r >> 4)); }
   __device__ Lds(uint4 *base, int n_cpad, int hash_slots, int arows_len) {
     arows = base;
     rows = base + arows_len;
@@ -619,8 +619,8 @@ __device__ __forceinline__ void exact8(const Lds<SD, ROWS32> &s, const float (&x
                                        int h, int n_c, float &best, int &bk) {
   const int b = grp >> 1, hh = grp & 1;
   const int c0 = b * 32 + h * 16 + hh * 4;
-  // c32_offset(c0), spelled out: the row set's padding is 4 (c0 / 4 + c0 / 32)
-  const float *base = s.c32 + b * (32 * SD + 36) + h * (16 * SD + 16) + hh * (4 * SD + 4);
+  // c32_offset(c0), spelled out: the row set's padding is 4 (c0 / 4 + c0 / 16)
+  const float *base = s.c32 + b * (32 * SD + 40) + h * (16 * SD + 20) + hh * (4 * SD + 4);
   float d[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -656,16 +656,27 @@ __device__ __forceinline__ void exact8(const Lds<SD, ROWS32> &s, const float (&x
 }
 
 // The 4 rows c0 .. c0 + 3 (c0 a multiple of 4) that one lane evaluates in the
-// exact stage for an 8-row group.  best and bk are set as by exact8 (bk =
-// offset 0..3).
+// exact stage for an 8-row group; off = c32_offset(c0) (the caller knows
+// c0 / 16).  best and bk are set as by exact8 (bk = offset 0..3).
 template <int SD, bool BF16, bool ROWS32, bool MASK>
 __device__ __forceinline__ void exact_rows4(const Lds<SD, ROWS32> &s, const float (&xv)[SD], int c0,
-                                            int n_c, float &best, int &bk) {
+                                            int off, int n_c, float &best, int &bk) {
   float d[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float cv[SD];
-    centroid_in_set<SD, BF16, ROWS32>(s, c0, j, cv);
+    if constexpr (ROWS32) {
+#pragma unroll
+      for (int q = 0; q < SD / 4; ++q) {
+        const float4 w = *reinterpret_cast<const float4 *>(s.c32 + off + SD * j + 4 * q);
+        cv[4 * q] = w.x;
+        cv[4 * q + 1] = w.y;
+        cv[4 * q + 2] = w.z;
+        cv[4 * q + 3] = w.w;
+      }
+    } else {
+      centroid_in_set<SD, BF16, ROWS32>(s, c0, j, cv);
+    }
     d[j] = sqdist<SD>(xv, cv);
     if (MASK) d[j] = (c0 + j < n_c) ? d[j] : __builtin_inff();
   }
@@ -1152,11 +1163,15 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     int bk = 0;
     int bi;
     if constexpr (SMALL) {
-      const int c0 = (cg1 >> 2) * 32 + ((cg1 >> 1) & 1) * 16 + 8 * h + 4 * (cg1 & 1);
+      // c0 = 16 k + 8 h + 4 (cg1 mod 2) with k = cg1 / 2, so c0 / 16 = k and
+      // its fp32 row set starts at (SD + 1) c0 + 4 k
+      const int kk = cg1 >> 1;
+      const int c0 = 16 * kk + 8 * h + 4 * (cg1 & 1);
+      const int off = (SD + 1) * c0 + 4 * kk;
       if (padded) {
-        exact_rows4<SD, BF16, ROWS32, true>(s, xv, c0, n_c, best, bk);
+        exact_rows4<SD, BF16, ROWS32, true>(s, xv, c0, off, n_c, best, bk);
       } else {
-        exact_rows4<SD, BF16, ROWS32, false>(s, xv, c0, n_c, best, bk);
+        exact_rows4<SD, BF16, ROWS32, false>(s, xv, c0, off, n_c, best, bk);
       }
       bi = c0 + bk;
     } else {

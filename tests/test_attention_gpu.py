@@ -174,3 +174,32 @@ def test_falcon_decode_boundary_tokens_carry_the_attention():
     wl.name += ", boundary tokens heavy"
     print(f"[case] {wl.name}", flush=True)
     assert_attention_parity(wl)
+
+
+def test_query_and_codebooks_only_2_byte_aligned():
+    """Query and codebooks at addresses 2 bytes past a 16-byte boundary (the
+    contract's minimum alignment) give results identical to aligned ones."""
+    wl = W.attention_case(24, 4, 12, 4, 256, 700, 4, 4, 256, W.F16, lens="ragged")
+    print(f"[case] {wl.name}", flush=True)
+    t = to_dev(wl)
+
+    def shifted(x):  # same values at an address 2 bytes past a 16-byte boundary
+        buf = torch.empty(x.numel() + 8, dtype=x.dtype, device=DEV)
+        v = buf[1:1 + x.numel()].view(x.shape)
+        v.copy_(x)
+        assert v.data_ptr() % 16 == 2 and v.is_contiguous()
+        return v
+
+    def run(q, kcb, vcb):
+        out = vq.attention_decode(q, t["k_codes"], t["v_codes"], kcb, vcb, k_scale=t["k_scale"],
+                                  kv_len=t["kv_len"], window=wl.window,
+                                  softmax_scale=wl.softmax_scale)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64)
+
+    assert t["q"].data_ptr() % 16 == 0 and t["k_codebook"].data_ptr() % 16 == 0
+    aligned = run(t["q"], t["k_codebook"], t["v_codebook"])
+    for q, kcb, vcb in ((shifted(t["q"]), t["k_codebook"], t["v_codebook"]),
+                        (t["q"], shifted(t["k_codebook"]), shifted(t["v_codebook"]))):
+        assert np.array_equal(run(q, kcb, vcb), aligned)
+    assert_attention_parity(wl)

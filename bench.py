@@ -146,6 +146,23 @@ def utilization(tag: str, launch_s: float):
     return out
 
 
+def kernel_counters(tag: str):
+    """Counter-derived figures of the dominant kernel of a multi-launch row
+    from profiles/<tag>_counters.txt (None if stale): busy fractions and
+    instructions per wave, no clock (the row's time spans several launches)."""
+    t = _summary_json(os.path.join(PROFILES, f"{tag}_counters.txt"))
+    if t is None:
+        return None
+    c = t.get("counters", {})
+    waves = t.get("waves") or 1.0
+    out = {k: t[k] for k in ("kernel", "valu_busy", "mfma_busy", "valu_insts_per_wave",
+                             "mfma_insts_per_wave", "lds_conflict_cycles_per_inst") if k in t}
+    if "SQ_INSTS_LDS" in c:
+        out["lds_insts_per_wave"] = c["SQ_INSTS_LDS"] / waves
+    out["source"] = f"profiles/{tag}_counters.txt"
+    return out
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -396,6 +413,7 @@ def leg_attention(args, dev, stream):
                                 algorithmic_bytes_per_launch=bytes_b)
         if nb in ATTENTION_BATCH_TAGS:
             batches[str(nb)]["traffic"] = traffic_bytes_per_launch(ATTENTION_BATCH_TAGS[nb])
+            batches[str(nb)]["partial_kernel_counters"] = kernel_counters(ATTENTION_BATCH_TAGS[nb])
     tag = ROW_TAGS["attention"]
     return {
         "workload": wl.name,
@@ -407,6 +425,7 @@ def leg_attention(args, dev, stream):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic_bytes_per_launch(tag)},
+        "partial_kernel_counters": kernel_counters(tag),
         "algorithmic_bytes_per_launch": algo_bytes,
         "tokens_attended_per_launch": int(np.sum(wl.kv_len)) * Hq,
         "by_batch": batches,

@@ -50,7 +50,10 @@ Every row is timed after a short GPU warm-up: its launches are enqueued
 behind a short spin kernel, so the events measure the launches back to back
 (``kernel_ms_per_launch``) however fast the host enqueues; ``host_ms_per_call``
 is the wall time per call of the same loop.  ``--only ROW`` runs one row
-alone (for profiling its kernel).
+alone (for profiling its kernel).  ``--ab PKG_A PKG_B --ab-row ROW`` compares
+two builds of the library on one row in the same process, in alternating
+rounds of launches (package directories: this one, and a copy built from
+another revision).
 """
 from __future__ import annotations
 
@@ -494,6 +497,80 @@ ROW_LEGS = {"fused": leg_fused, "attention": leg_attention, "kmeans": leg_kmeans
 ROW_LEGS.update({f"config{c}": leg_config(c) for c in (1, 2, 4, 5)})
 
 
+def load_binding(pkg_dir: str, name: str):
+    """The binding module of another build of the library: `pkg_dir` holds a
+    package's __init__.py and the libvq.so built beside it."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(name, os.path.join(pkg_dir, "__init__.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def ab_compare(args, dev, stream) -> dict:
+    """Same-process A/B of two library builds on one row: both are loaded, and
+    rounds of `ab_steps` launches alternate between them (A then B, then B
+    then A, ...), so clock drift between runs does not enter the comparison."""
+    import statistics
+    import numpy as np
+    import torch
+    import workloads as W
+    mods = [load_binding(os.path.abspath(d), f"_vq_ab{i}") for i, d in enumerate(args.ab)]
+    keep = []
+    cases = []  # (label, [launch function per build])
+    row = args.ab_row
+    if row == "attention":
+        for nb in [int(b) for b in (args.attention_batches or "32").split(",") if b]:
+            wl = W.falcon_decode_attention(B=nb)
+            k, call, _ = attention_call(wl, dev, stream)
+            keep.append(k)
+            cases.append((f"{nb} sequences",
+                          [lambda m=m, c=call: m.attention_decode_raw(*c) for m in mods]))
+    elif row.startswith("config"):
+        wl = W.config(int(row[len("config"):]))
+        tdt = torch.float16 if wl.dtype == W.F16 else torch.bfloat16
+        x = torch.from_numpy(wl.x.view(np.int16)).view(tdt).to(dev)
+        cb = torch.from_numpy(wl.codebook.view(np.int16)).view(tdt).to(dev)
+        out = torch.empty(wl.n, dtype=torch.uint32, device=dev)
+        keep.append((x, cb, out))
+        call = (x.data_ptr(), cb.data_ptr(), wl.n, wl.sub_dim, wl.n_centroids, wl.dtype,
+                wl.codebook_stride, wl.n_codebooks, wl.group_len, None, out.data_ptr(),
+                stream.cuda_stream)
+        cases.append((wl.name, [lambda m=m: m.encode_raw(*call) for m in mods]))
+    elif row in ("kmeans", "kmeans_bf16"):
+        wl = W.config(3 if row == "kmeans" else 5)
+        tdt = torch.float16 if wl.dtype == W.F16 else torch.bfloat16
+        x = torch.from_numpy(wl.x.view(np.int16)).view(tdt).to(dev)
+        keep.append(x)
+        fns = []
+        for m in mods:  # each build with its own codebook copy and workspace size
+            cb = torch.from_numpy(wl.codebook.view(np.int16)).view(tdt).to(dev)
+            idx = torch.empty(wl.n, dtype=torch.uint32, device=dev)
+            wsb = m.kmeans_workspace_bytes(wl.sub_dim, wl.n_centroids, 1, wl.dtype)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            keep.append((cb, idx, ws))
+            c = (x.data_ptr(), cb.data_ptr(), wl.n, wl.sub_dim, wl.n_centroids, wl.dtype,
+                 wl.codebook_stride, 1, wl.group_len, None, KMEANS_ITERATIONS, idx.data_ptr(),
+                 ws.data_ptr(), wsb, stream.cuda_stream)
+            fns.append(lambda m=m, c=c: m.kmeans_raw(*c))
+        cases.append((wl.name + f", Lloyd x{KMEANS_ITERATIONS}", fns))
+    else:
+        raise SystemExit(f"--ab-row {row!r}: one of attention, config1..config5, kmeans, kmeans_bf16")
+    res = {}
+    for label, fns in cases:
+        t = [[], []]
+        for r in range(args.ab_rounds):
+            for i in ((0, 1) if r % 2 == 0 else (1, 0)):
+                _, sec = time_row(fns[i], args.ab_steps, stream, warm_s=0.02)
+                t[i].append(sec * 1e6)
+        med = [statistics.median(v) for v in t]
+        res[label] = {"A_us": med[0], "B_us": med[1], "B_over_A": med[1] / med[0],
+                      "rounds_B_faster": sum(1 for a, b in zip(t[0], t[1]) if b < a),
+                      "rounds": args.ab_rounds}
+        log(f"ab {row} {label}: A {med[0]:.3f} us, B {med[1]:.3f} us, B/A {med[1] / med[0]:.4f}")
+    return {"ab": {"row": row, "A": args.ab[0], "B": args.ab[1], "cases": res}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -514,6 +591,14 @@ def main() -> int:
                     help="extra sequence counts the attention row is timed at ('' = none)")
     ap.add_argument("--only", choices=sorted(ROW_LEGS), default=None,
                     help="run only this row's leg and print its object")
+    ap.add_argument("--ab", nargs=2, metavar=("PKG_A", "PKG_B"), default=None,
+                    help="same-process A/B of two builds of the library (each a package "
+                         "directory: __init__.py and the libvq.so built beside it) on --ab-row")
+    ap.add_argument("--ab-row", default="config3",
+                    help="attention (at --attention-batches, default 32), config1..config5, "
+                         "kmeans or kmeans_bf16")
+    ap.add_argument("--ab-rounds", type=int, default=10)
+    ap.add_argument("--ab-steps", type=int, default=300)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -534,6 +619,9 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.ab:
+        print(json.dumps(ab_compare(args, dev, torch.cuda.current_stream(dev))), flush=True)
+        return 0
     if args.only:
         res = ROW_LEGS[args.only](args, dev, torch.cuda.current_stream(dev))
         if args.copy_calibration:

@@ -1396,67 +1396,131 @@ encode_mfma_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     const int seg_sub0 = SCALED ? static_cast<int>(gstart % sm.n_sub) : 0;
     const int64_t slot = group_map ? static_cast<int64_t>(group_map[g]) : g;
     const bool bad = slot < 0 || slot >= n_codebooks;
-    // the first unit of every wave is fixed; its loads overlap the staging
-    int64_t u = seg + wave;
-    uint32_t xw[T][4];
-    if (!bad && u < seg_end) load_unit_x<SD, T>(x, gstart + (u - g_unit0) * kUnit, gend, xw);
-    if (!first_seg) __syncthreads();  // every wave is done with the previous segment
-    first_seg = false;
-    if (threadIdx.x == 0) *counter = kWaves;
-    bool exact_tile = false, fold = false;
-    if (!bad) {
-      // its barrier also publishes the counter
-      exact_tile = stage_codebook<SD, kTerms<SD, SCALED>, BF16, ROWS32, BLOCK, kFold<SD, SCALED>,
-                                  kARows, SMALL>(
-          codebook + slot * cb_stride, n_c, n_cpad, s, hash_slots,
-          (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len,
-          units_per_wg < kWaves, fold);
-    } else {
-      __syncthreads();
-    }
-    while (u < seg_end) {  // uniform per wave
-      const int64_t ubase = gstart + (u - g_unit0) * kUnit;
-      if (bad) {
-        // a bad slot: all-one codes
-        if constexpr (SCALED) {
-#pragma unroll
-          for (int t = 0; t < T; ++t)
-            store_codes32(0xFFFFFFFFu, ubase + t * 32, gend, code_bits, h == 0, out);
+    // Plain keys in 4-column units with 16-row groups (codebooks of more
+    // than 256 centroids, whose units are long: kMixed) take work in pieces
+    // of half a unit: the youngest wave of each SIMD, which the issue
+    // arbiter serves last, takes 2-column pieces and the others whole units
+    // (two pieces), so the work a starved wave still holds when the others
+    // run out is half as long.  A whole unit that starts on the segment's
+    // last piece stores only the rows up to the segment's end (send).  (With
+    // 8-row groups the 2-column form costs more than the shorter tail saves.)
+    constexpr bool kMixed = !ACC && !SCALED && !SMALL && T == 4;
+    if constexpr (kMixed) {
+      constexpr int kSmallW = kWaves / 4;      // the youngest wave of each SIMD
+      constexpr int kBigW = kWaves - kSmallW;
+      constexpr int kPiece = kUnit / 2;        // half a unit: 2 columns
+      const bool small = wave >= kBigW;        // uniform per wave
+      const int take = small ? 1 : 2;          // pieces per take
+      const int64_t p0 = 2 * seg, pend = 2 * seg_end, pg0 = 2 * g_unit0;
+      const int64_t send = min(gend, gstart + (pend - pg0) * kPiece);
+      // the first piece of every wave is fixed; its loads overlap the staging
+      int64_t p = p0 + (small ? 2 * kBigW + (wave - kBigW) : 2 * wave);
+      uint32_t xw[T][4];
+      auto load_x = [&](int64_t piece) {
+        const int64_t b = gstart + (piece - pg0) * kPiece;
+        if (small) {
+          load_unit_x<SD, 2>(x, b, send, reinterpret_cast<uint32_t(&)[2][4]>(xw));
         } else {
-          const int64_t bpc = code_bits / 8;
-          const int64_t bend = min(ubase + kUnit, gend) * bpc;
-          for (int64_t b = ubase * bpc + lane; b < bend; b += 64) out[b] = 0xFFu;
+          load_unit_x<SD, T>(x, b, send, xw);
         }
+      };
+      if (!bad && p < pend) load_x(p);
+      if (!first_seg) __syncthreads();  // every wave is done with the previous segment
+      first_seg = false;
+      if (threadIdx.x == 0) *counter = 2 * kBigW + kSmallW;
+      bool exact_tile = false, fold = false;
+      if (!bad) {
+        // its barrier also publishes the counter
+        exact_tile = stage_codebook<SD, kTerms<SD, SCALED>, BF16, ROWS32, BLOCK, kFold<SD, SCALED>,
+                                    kARows, SMALL>(codebook + slot * cb_stride, n_c, n_cpad, s,
+                                                   hash_slots, nullptr, 0, units_per_wg < kWaves,
+                                                   fold);
       } else {
-        if constexpr (SCALED) {
-          // sub-slot of the unit's first row: (group start + unit offset) mod
-          // n_sub; the offset can pass 2^32 rows in one group
-          const int64_t rel = (u - g_unit0) * kUnit;
-          int sub0;
-          if constexpr (POW2) {  // the host launches this form only for a power of two
-            sub0 = (seg_sub0 + static_cast<int>(rel & sm.mask)) & sm.mask;
-          } else {
-            const uint32_t off = (rel >> 32) == 0
-                                     ? static_cast<uint32_t>(rel) % static_cast<uint32_t>(sm.n_sub)
-                                     : static_cast<uint32_t>(rel % sm.n_sub);
-            sub0 = mod_small(seg_sub0 + static_cast<int>(off), sm.n_sub, sm.inv_n_sub);
-          }
-          encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, POW2, SMALL>(
-              xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, sub0, code_bits, out, us);
-        } else {
-          encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, false, SMALL>(
-              xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, 0, code_bits, out, us);
-        }
+        __syncthreads();
       }
-      // the next unit is taken (a returning LDS atomic, which would wait
-      // behind the member-sum atomics) and its loads issued before this
-      // unit's rows join the sums
-      int next = 0;
-      if (lane == 0) next = atomicAdd(counter, 1);
-      u = seg + __builtin_amdgcn_readfirstlane(next);
+      while (p < pend) {  // uniform per wave
+        const int64_t ubase = gstart + (p - pg0) * kPiece;
+        if (bad) {  // a bad slot: all-one codes
+          const int64_t bpc = code_bits / 8;
+          const int64_t bend = min(ubase + kPiece * take, send) * bpc;
+          for (int64_t b = ubase * bpc + lane; b < bend; b += 64) out[b] = 0xFFu;
+        } else if (small) {
+          UnitSums<SD, 2> none;
+          encode_unit<SD, 2, BF16, ROWS32, false, false, false, SMALL>(
+              reinterpret_cast<const uint32_t(&)[2][4]>(xw), ubase, send, n_c, n_cpad, s,
+              exact_tile, fold, sm, 0, code_bits, out, none);
+        } else {
+          encode_unit<SD, T, BF16, ROWS32, false, false, false, SMALL>(
+              xw, ubase, send, n_c, n_cpad, s, exact_tile, fold, sm, 0, code_bits, out, us);
+        }
+        int next = 0;
+        if (lane == 0) next = atomicAdd(counter, take);
+        p = p0 + __builtin_amdgcn_readfirstlane(next);
+        if (!bad && p < pend) load_x(p);
+      }
+    } else {
+      // the first unit of every wave is fixed; its loads overlap the staging
+      int64_t u = seg + wave;
+      uint32_t xw[T][4];
       if (!bad && u < seg_end) load_unit_x<SD, T>(x, gstart + (u - g_unit0) * kUnit, gend, xw);
-      if constexpr (ACC) {
-        if (!bad) add_unit_sums<SD, T>(us, ubase, gend, lsum, lcnt);
+      if (!first_seg) __syncthreads();  // every wave is done with the previous segment
+      first_seg = false;
+      if (threadIdx.x == 0) *counter = kWaves;
+      bool exact_tile = false, fold = false;
+      if (!bad) {
+        // its barrier also publishes the counter
+        exact_tile = stage_codebook<SD, kTerms<SD, SCALED>, BF16, ROWS32, BLOCK, kFold<SD, SCALED>,
+                                    kARows, SMALL>(
+            codebook + slot * cb_stride, n_c, n_cpad, s, hash_slots,
+            (SCALED && scale) ? scale + slot * scale_stride : nullptr, scale_len,
+            units_per_wg < kWaves, fold);
+      } else {
+        __syncthreads();
+      }
+      while (u < seg_end) {  // uniform per wave
+        const int64_t ubase = gstart + (u - g_unit0) * kUnit;
+        if (bad) {
+          // a bad slot: all-one codes
+          if constexpr (SCALED) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+              store_codes32(0xFFFFFFFFu, ubase + t * 32, gend, code_bits, h == 0, out);
+          } else {
+            const int64_t bpc = code_bits / 8;
+            const int64_t bend = min(ubase + kUnit, gend) * bpc;
+            for (int64_t b = ubase * bpc + lane; b < bend; b += 64) out[b] = 0xFFu;
+          }
+        } else {
+          if constexpr (SCALED) {
+            // sub-slot of the unit's first row: (group start + unit offset) mod
+            // n_sub; the offset can pass 2^32 rows in one group
+            const int64_t rel = (u - g_unit0) * kUnit;
+            int sub0;
+            if constexpr (POW2) {  // the host launches this form only for a power of two
+              sub0 = (seg_sub0 + static_cast<int>(rel & sm.mask)) & sm.mask;
+            } else {
+              const uint32_t off = (rel >> 32) == 0
+                                       ? static_cast<uint32_t>(rel) % static_cast<uint32_t>(sm.n_sub)
+                                       : static_cast<uint32_t>(rel % sm.n_sub);
+              sub0 = mod_small(seg_sub0 + static_cast<int>(off), sm.n_sub, sm.inv_n_sub);
+            }
+            encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, POW2, SMALL>(
+                xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, sub0, code_bits, out, us);
+          } else {
+            encode_unit<SD, T, BF16, ROWS32, SCALED, ACC, false, SMALL>(
+                xw, ubase, gend, n_c, n_cpad, s, exact_tile, fold, sm, 0, code_bits, out, us);
+          }
+        }
+        // the next unit is taken (a returning LDS atomic, which would wait
+        // behind the member-sum atomics) and its loads issued before this
+        // unit's rows join the sums
+        int next = 0;
+        if (lane == 0) next = atomicAdd(counter, 1);
+        u = seg + __builtin_amdgcn_readfirstlane(next);
+        if (!bad && u < seg_end) load_unit_x<SD, T>(x, gstart + (u - g_unit0) * kUnit, gend, xw);
+        if constexpr (ACC) {
+          if (!bad) add_unit_sums<SD, T>(us, ubase, gend, lsum, lcnt);
+        }
       }
     }
     if constexpr (ACC) {

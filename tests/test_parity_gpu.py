@@ -92,13 +92,20 @@ def test_small_cases_match_oracle(case):
 # whichever wave is free, and the codebook slot is restaged per segment.
 # Group lengths that are not a multiple of the unit (32 T rows) leave partly
 # filled units at every group end; a map sends several groups to one slot,
-# some to bad slots.
+# some to bad slots.  Above 256 centroids the work goes out in half units
+# (2-column pieces for the youngest wave of each SIMD, whole units for the
+# others, from one piece counter that starts past the 28 pieces handed out
+# at the start): cases 54 and 55 give each workgroup 38 and 44 pieces, so
+# pieces also come from the counter, and a whole unit can start on a
+# segment's last piece and must stop at the segment's end.
 MULTI = [
     # (seed, n, sd, n_c, dtype, extra)
     (50, 200_000, 4, 256, W.F16, dict(n_codebooks=70, group_len=3000)),
     (51, 150_000, 8, 256, W.BF16, dict(n_codebooks=9, group_len=700, use_map=True)),
     (52, 120_000, 4, 100, W.F16, dict(n_codebooks=5, group_len=129, use_map=True, stride_pad=3)),
     (53, 100_000, 8, 2000, W.F16, dict(n_codebooks=3, group_len=9000, use_map=True)),
+    (54, 600_000, 4, 300, W.F16, dict(n_codebooks=6, group_len=3000, use_map=True)),
+    (55, 700_000, 8, 1100, W.BF16, dict(n_codebooks=4, group_len=4000, use_map=True, dup_frac=0.02)),
 ]
 
 

@@ -306,6 +306,14 @@ __device__ __forceinline__ f32x16 mfma(const uint4 &a, const uint4 &b, const f32
   }
 }
 
+// An empty use of a value: the loads that produce it are issued before this
+// point (the compiler may otherwise sink them past a branch to their use).
+__device__ __forceinline__ void hold(float v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void hold(const uint2 &v) { asm volatile("" ::"v"(v.x), "v"(v.y)); }
+__device__ __forceinline__ void hold(const uint4 &v) {
+  asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+
 // Minimum of the 16 values (finite or +inf).  The first step is a med3 with
 // -FLT_MAX, which equals min for such values and needs no NaN quieting.
 __device__ __forceinline__ float min16(const f32x16 &v) {
@@ -1101,11 +1109,127 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       }
     }
   };
-  if (!exact_tile) {
-    if (kFold<SD, SCALED> && fold) {
-      stage1(std::true_type{});
+  // The same block step as a function of the block index, for the forms
+  // that run faster this way: sub_dim 8 with 4-column units and 8-row groups
+  // (with the blocks unrolled: 7% on the Llama shape, 3% on the full cache)
+  // and the K-means forms (2.5%).  The other forms keep the loop above: the
+  // compiler schedules them better in that shape (the Falcon shape runs 3%
+  // slower through this one).
+  auto stage1_blocks = [&](auto folded) {
+    constexpr bool F = decltype(folded)::value;
+    constexpr int kGpb = SMALL ? 4 : 2;  // groups per block
+    OpT aop = a_operand(0);
+    float an0 = F ? 0.0f : s.gan[h];
+    float an1 = (F || !SMALL) ? 0.0f : s.gan[2 + h];
+    // sub_dim 8 with 8-row groups and all kSmallMaxCentroids / 32 blocks:
+    // the blocks are unrolled, so that the operand reads take constant LDS
+    // offsets and the group indices are constants
+    constexpr bool kUnrolled = SMALL && SD == 8 && T == 4;
+    auto block = [&](int blk) {
+      const OpT a_cur = aop;
+      const float an0_cur = an0, an1_cur = an1;
+      const f32x16 cop = F ? zero16 : c_operand(blk);
+      if constexpr (F) {
+        aop = a_operand(min(blk + 1, nblk - 1));
+      } else if (blk + 1 < nblk) {
+        aop = a_operand(blk + 1);
+        an0 = s.gan[kGpb * (blk + 1) + h];
+        if constexpr (SMALL) an1 = s.gan[kGpb * (blk + 1) + 2 + h];
+      }
+      // 16-row groups: group 2 blk + h, its index kept in g1
+      auto track = [&](int t, float mb) {
+        m2[t] = __builtin_amdgcn_fmed3f(m1[t], m2[t], mb);
+        g1[t] = (mb < m1[t]) ? 2 * blk + h : g1[t];
+        m1[t] = __builtin_amdgcn_fmed3f(m1[t], mb, kNegMax);
+      };
+      // the bounds of this lane's groups from a product: lo (and hi, SMALL)
+      auto reduce = [&](int t, const f32x16 &a, float &lo, float &hi) {
+        if constexpr (SMALL) {
+          lo = min8<0>(a);
+          hi = min8<8>(a);
+          if constexpr (!F) {
+            lo = __builtin_fmaf(-an0_cur, bn[t], lo);
+            hi = __builtin_fmaf(-an1_cur, bn[t], hi);
+          }
+        } else {
+          lo = F ? min16(a) : __builtin_fmaf(-an0_cur, bn[t], min16(a));
+        }
+      };
+      // (the index of the upper group is made a scalar of its own: folded into
+      // the other's, it costs a second VALU instruction per key)
+      const uint32_t k_lo = 2u * blk;
+      const uint32_t k_hi = __builtin_amdgcn_readfirstlane(k_lo + 1u);
+      auto track_all = [&](int t, float lo, float hi) {
+        if constexpr (SMALL) {
+          // 8-row groups: group 2 k + h with k = 2 blk + q, and k written
+          // into the 4 low bits of the bound (see Consts), so keys of
+          // different groups differ and min and med3 carry the index along
+          // with the bound.  Both keys of the block at once: with m1 <= m2
+          // and distinct keys a, b the new smallest is min3(m1, a, b) and the
+          // new second smallest min(m2, med3(m1, a, b)): 3 instructions for 2
+          // keys.  min3 and min are written out because keys with index bits
+          // are not canonical floats to the compiler, which would quiet them
+          // first (the keys are finite, so quieting changes nothing).
+          const float ka = __uint_as_float((__float_as_uint(lo) & ~kIdxMask) | k_lo);
+          const float kb = __uint_as_float((__float_as_uint(hi) & ~kIdxMask) | k_hi);
+          const float mid = __builtin_amdgcn_fmed3f(m1[t], ka, kb);
+          float n1, n2;
+          asm("v_min3_f32 %0, %1, %2, %3" : "=v"(n1) : "v"(m1[t]), "v"(ka), "v"(kb));
+          asm("v_min_f32 %0, %1, %2" : "=v"(n2) : "v"(m2[t]), "v"(mid));
+          m1[t] = n1;
+          m2[t] = n2;
+        } else {
+          track(t, lo);
+        }
+      };
+      if constexpr (F) {
+        // the error term is in the product: the group minimum is the bound
+        f32x16 acc[2];
+        acc[0] = mfma<BF16>(a_cur, bop[0], cop);
+        if constexpr (T > 1) acc[1] = mfma<BF16>(a_cur, bop[1], cop);
+        unroll<T>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          float lo, hi;
+          reduce(t, acc[t & 1], lo, hi);
+          if constexpr (t + 2 < T) acc[t & 1] = mfma<BF16>(a_cur, bop[t + 2], cop);
+          track_all(t, lo, hi);
+        });
+      } else {
+        unroll<T>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          float lo, hi;
+          reduce(t, mfma<BF16>(a_cur, bop[t], cop), lo, hi);
+          track_all(t, lo, hi);
+        });
+      }
+      if constexpr (kUnrolled) {  // the next block's operands are read in this one
+        hold(aop);
+        if constexpr (!F) {
+          hold(an0);
+          hold(an1);
+        }
+      }
+    };
+    if (kUnrolled && nblk == kSmallMaxCentroids / 32) {  // uniform
+      unroll<kSmallMaxCentroids / 32>([&](auto bc) { block(decltype(bc)::value); });
     } else {
-      stage1(std::false_type{});
+      for (int blk = 0; blk < nblk; ++blk) block(blk);
+    }
+  };
+  if (!exact_tile) {
+    constexpr bool kBlockFn = (SMALL && SD == 8 && T == 4) || ACC;
+    if (kFold<SD, SCALED> && fold) {
+      if constexpr (kBlockFn) {
+        stage1_blocks(std::true_type{});
+      } else {
+        stage1(std::true_type{});
+      }
+    } else {
+      if constexpr (kBlockFn) {
+        stage1_blocks(std::false_type{});
+      } else {
+        stage1(std::false_type{});
+      }
     }
   }
 

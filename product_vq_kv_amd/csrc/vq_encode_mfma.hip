@@ -310,9 +310,6 @@ __device__ __forceinline__ f32x16 mfma(const uint4 &a, const uint4 &b, const f32
 // point (the compiler may otherwise sink them past a branch to their use).
 __device__ __forceinline__ void hold(float v) { asm volatile("" ::"v"(v)); }
 __device__ __forceinline__ void hold(const uint2 &v) { asm volatile("" ::"v"(v.x), "v"(v.y)); }
-__device__ __forceinline__ void hold(const uint4 &v) {
-  asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
-}
 
 // Minimum of the 16 values (finite or +inf).  The first step is a med3 with
 // -FLT_MAX, which equals min for such values and needs no NaN quieting.
@@ -964,6 +961,8 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
 
   // A operand of block blk: -c for this lane's row; the plain form holds
   // the lane's half of the K slots, the smoothed form -c in both halves
+  // (plain: from this lane's first entry, 64 entries per block)
+  const uint2 *lane_rows = reinterpret_cast<const uint2 *>(s.rows) + 2 * col + h;
   auto a_operand = [&](int blk) -> OpT {
     if constexpr (SCALED && SD == 8) {
       return s.rows[blk * 32 + col];
@@ -975,7 +974,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
       const uint2 q = reinterpret_cast<const uint2 *>(s.rows)[blk * 64 + 2 * col + h];
       return (h == 0) ? make_uint4(q.x, q.y, q.x, q.y) : make_uint4(q.x, q.y, 0u, 0u);
     } else {
-      return reinterpret_cast<const uint2 *>(s.rows)[blk * 64 + 2 * col + h];
+      return lane_rows[blk * 64];
     }
   };
   auto c_operand = [&](int blk) {
@@ -1263,13 +1262,15 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     const PairVals pa = pair_vals(__float_as_uint(m1[t]));
     const PairVals pb = pair_vals(__float_as_uint(m2[t]));
     const float a0 = __uint_as_float(pa.first), a1 = __uint_as_float(pa.second);
-    int cg1;
+    int cg1 = 0;
+    [[maybe_unused]] int kk = 0, q1 = 0;  // 8-row groups: cg1 = 2 kk + q1
     if constexpr (SMALL) {
       // lane h's group is 2 k + h; equal keys hold equal k, and then lane
       // 0's group is the lower one
       const bool take1 = a1 < a0;
       const uint32_t key = take1 ? pa.second : pa.first;
-      cg1 = 2 * static_cast<int>(key & kIdxMask) + (take1 ? 1 : 0);
+      kk = static_cast<int>(key & kIdxMask);
+      q1 = take1 ? 1 : 0;
     } else {
       const PairVals pg = pair_vals(static_cast<uint32_t>(g1[t]));
       const bool take1 =
@@ -1289,9 +1290,8 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     if constexpr (SMALL) {
       // c0 = 16 k + 8 h + 4 (cg1 mod 2) with k = cg1 / 2, so c0 / 16 = k and
       // its fp32 row set starts at (SD + 1) c0 + 4 k
-      const int kk = cg1 >> 1;
-      const int c0 = 16 * kk + 8 * h + 4 * (cg1 & 1);
-      const int off = (SD + 1) * c0 + 4 * kk;
+      const int c0 = 16 * kk + 8 * h + 4 * q1;
+      const int off = (16 * (SD + 1) + 4) * kk + (SD + 1) * (8 * h + 4 * q1);
       if (padded) {
         exact_rows4<SD, BF16, ROWS32, true>(s, xv, c0, off, n_c, best, bk);
       } else {

@@ -537,6 +537,17 @@ def ab_compare(args, dev, stream) -> dict:
                 wl.codebook_stride, wl.n_codebooks, wl.group_len, None, out.data_ptr(),
                 stream.cuda_stream)
         cases.append((wl.name, [lambda m=m: m.encode_raw(*call) for m in mods]))
+    elif row == "fused":
+        wl = W.falcon_smoothed()
+        x = torch.from_numpy(wl.x.view(np.int16)).view(torch.float16).to(dev)
+        cb = torch.from_numpy(wl.codebook.view(np.int16)).view(torch.float16).to(dev)
+        sc = torch.from_numpy(wl.channel_scale[0]).to(dev)
+        out = torch.empty(mods[0].packed_bytes(wl.n, 8), dtype=torch.uint8, device=dev)
+        keep.append((x, cb, sc, out))
+        call = (x.data_ptr(), cb.data_ptr(), wl.n, wl.sub_dim, wl.n_centroids, wl.dtype,
+                wl.codebook_stride, wl.n_codebooks, wl.group_len, None, sc.data_ptr(), wl.head_dim,
+                0, 8, out.data_ptr(), stream.cuda_stream)
+        cases.append((wl.name + ", 8-bit codes", [lambda m=m: m.encode_packed_raw(*call) for m in mods]))
     elif row in ("kmeans", "kmeans_bf16"):
         wl = W.config(3 if row == "kmeans" else 5)
         tdt = torch.float16 if wl.dtype == W.F16 else torch.bfloat16
@@ -555,7 +566,7 @@ def ab_compare(args, dev, stream) -> dict:
             fns.append(lambda m=m, c=c: m.kmeans_raw(*c))
         cases.append((wl.name + f", Lloyd x{KMEANS_ITERATIONS}", fns))
     else:
-        raise SystemExit(f"--ab-row {row!r}: one of attention, config1..config5, kmeans, kmeans_bf16")
+        raise SystemExit(f"--ab-row {row!r}: one of attention, config1..config5, fused, kmeans, kmeans_bf16")
     res = {}
     for label, fns in cases:
         t = [[], []]
@@ -596,7 +607,7 @@ def main() -> int:
                          "directory: __init__.py and the libvq.so built beside it) on --ab-row")
     ap.add_argument("--ab-row", default="config3",
                     help="attention (at --attention-batches, default 32), config1..config5, "
-                         "kmeans or kmeans_bf16")
+                         "fused, kmeans or kmeans_bf16")
     ap.add_argument("--ab-rounds", type=int, default=10)
     ap.add_argument("--ab-steps", type=int, default=300)
     args = ap.parse_args()

@@ -310,6 +310,9 @@ __device__ __forceinline__ f32x16 mfma(const uint4 &a, const uint4 &b, const f32
 // point (the compiler may otherwise sink them past a branch to their use).
 __device__ __forceinline__ void hold(float v) { asm volatile("" ::"v"(v)); }
 __device__ __forceinline__ void hold(const uint2 &v) { asm volatile("" ::"v"(v.x), "v"(v.y)); }
+__device__ __forceinline__ void hold(const uint4 &v) {
+  asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
 
 // Minimum of the 16 values (finite or +inf).  The first step is a med3 with
 // -FLT_MAX, which equals min for such values and needs no NaN quieting.
@@ -1109,21 +1112,22 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     }
   };
   // The same block step as a function of the block index, for the forms
-  // that run faster this way: sub_dim 8 with 4-column units and 8-row groups
-  // (with the blocks unrolled: 7% on the Llama shape, 3% on the full cache)
-  // and the K-means forms (2.5%).  The other forms keep the loop above: the
-  // compiler schedules them better in that shape (the Falcon shape runs 3%
-  // slower through this one).
+  // that run faster this way: with the blocks unrolled, sub_dim 8 with
+  // 4-column units and 8-row groups (4-7% on the Llama shape, 3% on the full
+  // cache) and smoothed keys with 8-row groups (1%); and the K-means forms
+  // (2.5%).  The other forms keep the loop above: the compiler schedules them
+  // better in that shape (the Falcon shape runs 3% slower through this one).
   auto stage1_blocks = [&](auto folded) {
     constexpr bool F = decltype(folded)::value;
     constexpr int kGpb = SMALL ? 4 : 2;  // groups per block
     OpT aop = a_operand(0);
     float an0 = F ? 0.0f : s.gan[h];
     float an1 = (F || !SMALL) ? 0.0f : s.gan[2 + h];
-    // sub_dim 8 with 8-row groups and all kSmallMaxCentroids / 32 blocks:
-    // the blocks are unrolled, so that the operand reads take constant LDS
-    // offsets and the group indices are constants
-    constexpr bool kUnrolled = SMALL && SD == 8 && T == 4;
+    // 8-row groups (sub_dim 8 with 4-column units, or smoothed keys) with all
+    // kSmallMaxCentroids / 32 blocks: the blocks are unrolled, so that the
+    // operand reads take constant LDS offsets and the group indices are
+    // constants
+    constexpr bool kUnrolled = SMALL && ((SD == 8 && T == 4) || SCALED);
     auto block = [&](int blk) {
       const OpT a_cur = aop;
       const float an0_cur = an0, an1_cur = an1;
@@ -1216,7 +1220,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     }
   };
   if (!exact_tile) {
-    constexpr bool kBlockFn = (SMALL && SD == 8 && T == 4) || ACC;
+    constexpr bool kBlockFn = (SMALL && SD == 8 && T == 4) || ACC || (SCALED && SMALL);
     if (kFold<SD, SCALED> && fold) {
       if constexpr (kBlockFn) {
         stage1_blocks(std::true_type{});

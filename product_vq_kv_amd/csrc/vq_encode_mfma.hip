@@ -1114,8 +1114,8 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
   // The same block step as a function of the block index, for the forms
   // that run faster this way: with the blocks unrolled, sub_dim 8 with
   // 4-column units and 8-row groups (4-7% on the Llama shape, 3% on the full
-  // cache) and smoothed keys with 8-row groups (1%); and the K-means forms
-  // (2.5%).  The other forms keep the loop above: the compiler schedules them
+  // cache) and smoothed sub_dim 4 keys with a power-of-two key length and
+  // 8-row groups (1%); and the K-means forms (2.5%).  The other forms keep the loop above: the compiler schedules them
   // better in that shape (the Falcon shape runs 3% slower through this one).
   auto stage1_blocks = [&](auto folded) {
     constexpr bool F = decltype(folded)::value;
@@ -1123,11 +1123,12 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     OpT aop = a_operand(0);
     float an0 = F ? 0.0f : s.gan[h];
     float an1 = (F || !SMALL) ? 0.0f : s.gan[2 + h];
-    // 8-row groups (sub_dim 8 with 4-column units, or smoothed keys) with all
+    // 8-row groups (sub_dim 8 with 4-column units, or smoothed sub_dim 4 keys
+    // with a power-of-two key length) with all
     // kSmallMaxCentroids / 32 blocks: the blocks are unrolled, so that the
     // operand reads take constant LDS offsets and the group indices are
     // constants
-    constexpr bool kUnrolled = SMALL && ((SD == 8 && T == 4) || SCALED);
+    constexpr bool kUnrolled = SMALL && ((SD == 8 && T == 4) || (SCALED && SD == 4 && POW2));
     auto block = [&](int blk) {
       const OpT a_cur = aop;
       const float an0_cur = an0, an1_cur = an1;
@@ -1220,7 +1221,7 @@ __device__ void encode_unit(const uint32_t (&xin)[T][4], int64_t ubase, int64_t 
     }
   };
   if (!exact_tile) {
-    constexpr bool kBlockFn = (SMALL && SD == 8 && T == 4) || ACC || (SCALED && SMALL);
+    constexpr bool kBlockFn = (SMALL && SD == 8 && T == 4) || ACC || (SCALED && SMALL && SD == 4 && POW2);
     if (kFold<SD, SCALED> && fold) {
       if constexpr (kBlockFn) {
         stage1_blocks(std::true_type{});
